@@ -1,0 +1,170 @@
+"""Seeded synthetic inputs for the NVFP4 W4A4 linear layer.
+
+Shared by the tests, the benchmark and the smoke check: the oracle and the HIP path are fed the same
+bits from here.  This module holds no arithmetic of the method (no quantisation, no product); it
+only draws random tensors with the shapes, value distributions and outlier structure of the five
+workloads below, and rounds them once to bf16 with PyTorch's CPU round-to-nearest-even cast where
+the workload is bf16.
+
+Random streams: ``numpy.random.Generator(PCG64(1000 * workload + tensor_id))`` with tensor ids
+1 = activations, 2 = weights, 3 = outlier-channel indices, 4 = second activation factor / t draws.
+
+Statistics imitated (ai.info summary of arXiv 2609.04098, "Main Findings"): residual-stream inputs
+carry extreme outliers on a few hot channels (hot channels about 100x the median channel), and a
+sizeable share of 16-element blocks is dominated by a single value.  The workload shapes follow the
+hybrid model's projections named on the same page (fused GDN in_proj, MLP gate+up and down
+projections, decode GEMV).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+WEIGHT_STD = np.float32(0.02)
+
+
+@dataclass(frozen=True)
+class Workload:
+    """Shape and recipe of one synthetic workload."""
+
+    wid: int
+    name: str
+    M: int
+    K: int
+    N: int
+    seg_sizes: tuple  # output-column segments, one per calibrated module
+    act_dtype: str  # "f32" or "bf16" (what the quantiser reads)
+    w_dtype: str
+    outlier_frac: float
+    outlier_gain: float
+    outlier_kind: str  # "scale" (N(0,1) * gain) or "t3" (gain * Student-t, 3 dof) or "none"
+    seg_std_mult: tuple = field(default=())  # per-segment weight std multipliers
+    silu_mul: bool = False  # activations = SiLU(g) * u
+
+    @property
+    def seg_offsets(self):
+        off = [0]
+        for s in self.seg_sizes:
+            off.append(off[-1] + s)
+        return off
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+WORKLOADS = {
+    # Single quantise + W4A4 GEMM, fp32 inputs, 0.5% of K-channels x100.
+    1: Workload(1, "single_64x512x256", 64, 512, 256, (256,), "f32", "f32", 0.005, 100.0, "scale"),
+    # Fused GDN input projection q,k,v,decay-gate,write-gate; a/b pair with a 2.75x scale ratio.
+    2: Workload(2, "gdn_in_proj_4096x5120x8288", 4096, 5120, 8288, (2048, 2048, 4096, 48, 48),
+                "bf16", "bf16", 0.01, 50.0, "scale", seg_std_mult=(1.0, 1.0, 1.0, 2.75, 1.0)),
+    # Fused MLP gate+up, heavy-tailed outlier channels.
+    3: Workload(3, "mlp_gate_up_8192x5120x34816", 8192, 5120, 34816, (17408, 17408),
+                "bf16", "bf16", 0.01, 50.0, "t3"),
+    # Decode-shaped skinny GEMM (M is 1, 4 or 16).
+    4: Workload(4, "decode_Mx5120x5120", 16, 5120, 5120, (5120,), "bf16", "bf16", 0.01, 50.0,
+                "scale"),
+    # Long-prefill MLP down projection on SiLU(g)*u activations.
+    5: Workload(5, "mlp_down_32768x17408x5120", 32768, 17408, 5120, (5120,), "bf16", "bf16",
+                0.0, 1.0, "none", silu_mul=True),
+}
+
+
+def _rng(wid: int, tensor_id: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(1000 * wid + tensor_id))
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (PyTorch CPU cast, nearest-even) and widen back exactly."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def outlier_channels(w: Workload) -> np.ndarray:
+    n = int(round(w.outlier_frac * w.K))
+    if n == 0 or w.outlier_kind == "none":
+        return np.zeros(0, dtype=np.int64)
+    return np.sort(_rng(w.wid, 3).choice(w.K, size=n, replace=False))
+
+
+def activations(w: Workload, M: int | None = None, row0: int = 0) -> np.ndarray:
+    """Activation rows ``[row0, row0 + M)`` of workload ``w`` as float32 holding values of the
+    workload's dtype.  Rows are drawn in fixed 256-row chunks so any row range reproduces the same
+    values as the full tensor."""
+    M = w.M if M is None else M
+    if M == 0:
+        return np.zeros((0, w.K), dtype=np.float32)
+    chunk = 256
+    c0, c1 = row0 // chunk, (row0 + M + chunk - 1) // chunk
+    parts = [_activation_chunk(w, c, chunk) for c in range(c0, c1)]
+    full = np.concatenate(parts, axis=0)
+    off = row0 - c0 * chunk
+    return np.ascontiguousarray(full[off:off + M])
+
+
+def _activation_chunk(w: Workload, c: int, chunk: int) -> np.ndarray:
+    # One independent substream per 256-row chunk (jumped PCG64), so chunks are reproducible alone.
+    bitgen = np.random.PCG64(1000 * w.wid + 1).jumped(c)
+    rng = np.random.Generator(bitgen)
+    rows = chunk
+    if w.silu_mul:
+        g = rng.standard_normal((rows, w.K), dtype=np.float32)
+        u = rng.standard_normal((rows, w.K), dtype=np.float32)
+        x = (g / (np.float32(1.0) + np.exp(-g))) * u
+    else:
+        x = rng.standard_normal((rows, w.K), dtype=np.float32)
+        ch = outlier_channels(w)
+        if len(ch):
+            if w.outlier_kind == "scale":
+                x[:, ch] *= np.float32(w.outlier_gain)
+            elif w.outlier_kind == "t3":
+                trng = np.random.Generator(np.random.PCG64(1000 * w.wid + 4).jumped(c))
+                x[:, ch] = np.float32(w.outlier_gain) * trng.standard_t(3, (rows, len(ch))).astype(
+                    np.float32)
+    x = x.astype(np.float32)
+    return round_bf16(x) if w.act_dtype == "bf16" else x
+
+
+def weights(w: Workload, rows: slice | None = None) -> np.ndarray:
+    """Weight matrix ``[N, K]`` (nn.Linear layout) as float32 holding values of the weight dtype.
+    ``rows`` selects a row range without drawing the whole matrix (256-row substreams)."""
+    rows = slice(0, w.N) if rows is None else rows
+    r0, r1 = rows.start or 0, w.N if rows.stop is None else rows.stop
+    chunk = 256
+    c0, c1 = r0 // chunk, (r1 + chunk - 1) // chunk
+    parts = []
+    mult = _row_std_mult(w)
+    for c in range(c0, c1):
+        rng = np.random.Generator(np.random.PCG64(1000 * w.wid + 2).jumped(c))
+        lo, hi = c * chunk, min((c + 1) * chunk, w.N)
+        x = rng.standard_normal((chunk, w.K), dtype=np.float32)[: hi - lo]
+        x *= (WEIGHT_STD * mult[lo:hi])[:, None]
+        parts.append(x)
+    full = np.concatenate(parts, axis=0) if parts else np.zeros((0, w.K), np.float32)
+    out = np.ascontiguousarray(full[r0 - c0 * chunk: r1 - c0 * chunk])
+    return round_bf16(out) if w.w_dtype == "bf16" else out
+
+
+def _row_std_mult(w: Workload) -> np.ndarray:
+    mult = np.ones(w.N, dtype=np.float32)
+    if w.seg_std_mult:
+        off = w.seg_offsets
+        for j, m in enumerate(w.seg_std_mult):
+            mult[off[j]:off[j + 1]] = np.float32(m)
+    return mult
+
+
+def random_matrix(seed: int, rows: int, cols: int, std: float = 1.0, outlier_cols: int = 0,
+                  outlier_gain: float = 50.0, dtype: str = "f32") -> np.ndarray:
+    """Small seeded N(0, std^2) matrix with optional hot columns, for ragged/edge-case tests."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((rows, cols), dtype=np.float32) * np.float32(std)
+    if outlier_cols and cols:
+        ch = rng.choice(cols, size=min(outlier_cols, cols), replace=False)
+        x[:, ch] *= np.float32(outlier_gain)
+    return round_bf16(x) if dtype == "bf16" else x
