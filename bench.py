@@ -1,0 +1,230 @@
+"""Benchmark of the NVFP4 W4A4 linear-layer hot path on one MI355X.
+
+One step = the whole hot path over one batch of the fused MLP gate+up workload (M = 8192 tokens,
+K = 5120, N = 2 x 17408, two calibrated modules): encode the bf16 activations to NVFP4 with the
+static (calibrated) global scale, then the fused W4A4 product with the per-module epilogue, FP32
+output.  Weights are encoded once before timing (offline step).  Inputs are seeded synthetic
+tensors resident in HBM before the timed region starts.
+
+Printed: one JSON line with the prefill throughput (TFLOP/s = 2MNK / step time), the roofline of
+the dominant kernel (the product; its average duration from HIP events recorded on the stream it
+is launched on), the decode-shaped GEMV throughput (GB/s of algorithmic bytes), and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_F16_PEAK_TFLOPS = 2516.6  # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense f16/bf16
+MFMA_FP4_PEAK_TFLOPS = 10066.0  # dense MXFP4, context only
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill(args, torch, nv, W):
+    import numpy as np
+
+    w = W.WORKLOADS[3]
+    dev = "cuda:0"
+    log(f"[bench] generating {w.name}")
+    a = W.activations(w)
+    g_a = np.float32(2688.0 / np.abs(a).max())  # calibration stand-in: static scale from amax
+    ad = torch.from_numpy(a).to(torch.bfloat16).to(dev)
+    del a
+    segs = w.seg_offsets
+    wc = torch.empty((w.N, w.K // 2), dtype=torch.uint8, device=dev)
+    ws = torch.empty((w.N, w.K // 16), dtype=torch.uint8, device=dev)
+    gw = torch.empty(len(segs) - 1, dtype=torch.float32, device=dev)
+    for j in range(len(segs) - 1):
+        wj = W.weights(w, slice(segs[j], segs[j + 1]))
+        wd = torch.from_numpy(wj).to(torch.bfloat16).to(dev)
+        _, _, g = nv.nvfp4_quantize(wd, None, wc[segs[j]:segs[j + 1]], ws[segs[j]:segs[j + 1]])
+        gw[j:j + 1].copy_(g)
+        del wd, wj
+    ga = torch.tensor([g_a], dtype=torch.float32, device=dev)
+    ac = torch.empty((w.M, w.K // 2), dtype=torch.uint8, device=dev)
+    as_ = torch.empty((w.M, w.K // 16), dtype=torch.uint8, device=dev)
+    C = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        nv.nvfp4_quantize(ad, ga, ac, as_)
+        nv.fused_nvfp4_gemm(ac, as_, ga, wc, ws, gw, segs, out=C)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+
+    # per-kernel durations: events on the launch stream around each kernel
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
+    for i in range(args.steps):
+        evs[3 * i].record()
+        nv.nvfp4_quantize(ad, ga, ac, as_)
+        evs[3 * i + 1].record()
+        nv.fused_nvfp4_gemm(ac, as_, ga, wc, ws, gw, segs, out=C)
+        evs[3 * i + 2].record()
+    torch.cuda.synchronize()
+    q_ms = sum(evs[3 * i].elapsed_time(evs[3 * i + 1]) for i in range(args.steps)) / args.steps
+    g_ms = sum(evs[3 * i + 1].elapsed_time(evs[3 * i + 2]) for i in range(args.steps)) / args.steps
+    flops = w.flops
+    q_bytes = w.M * w.K * (2 + 9 / 16)
+    return dict(w=w, ms_step=ms_step, gemm_ms=g_ms, quant_ms=q_ms, flops=flops, q_bytes=q_bytes)
+
+
+def decode(args, torch, nv, W):
+    """Decode-shaped products M in {1, 4, 16}, K = N = 5120, NVFP4 weights resident in HBM and
+    rotated over 24 byte-identical copies (354 MB, beyond the 256 MB last-level cache); the
+    activations are encoded per call."""
+    import numpy as np
+
+    w = W.WORKLOADS[4]
+    dev = "cuda:0"
+    wt = W.weights(w)
+    wd = torch.from_numpy(wt).to(torch.bfloat16).to(dev)
+    wc0, ws0, gw = nv.nvfp4_quantize(wd)
+    del wd
+    R = 24
+    copies = [(wc0.clone(), ws0.clone()) for _ in range(R)]
+    res = {}
+    for M in (1, 4, 16):
+        a = W.activations(w, M)
+        ga = torch.tensor([np.float32(2688.0 / np.abs(a).max())], dtype=torch.float32, device=dev)
+        ad = torch.from_numpy(a).to(torch.bfloat16).to(dev)
+        ac = torch.empty((M, w.K // 2), dtype=torch.uint8, device=dev)
+        as_ = torch.empty((M, w.K // 16), dtype=torch.uint8, device=dev)
+        C = torch.empty((M, w.N), dtype=torch.float32, device=dev)
+        for i in range(2 * R):
+            nv.nvfp4_quantize(ad, ga, ac, as_)
+            wc, ws = copies[i % R]
+            nv.nvfp4_gemm(ac, as_, ga, wc, ws, gw, out=C)
+        torch.cuda.synchronize()
+        n = 10 * R
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(3 * n)]
+        for i in range(n):
+            wc, ws = copies[i % R]
+            evs[3 * i].record()
+            nv.nvfp4_quantize(ad, ga, ac, as_)
+            evs[3 * i + 1].record()
+            nv.nvfp4_gemm(ac, as_, ga, wc, ws, gw, out=C)
+            evs[3 * i + 2].record()
+        torch.cuda.synchronize()
+        g_ms = sorted(evs[3 * i + 1].elapsed_time(evs[3 * i + 2]) for i in range(n))[n // 2]
+        call_ms = sorted(evs[3 * i].elapsed_time(evs[3 * i + 2]) for i in range(n))[n // 2]
+        nbytes = w.N * w.K * 9 // 16 + M * w.K * 2 + M * w.N * 4
+        res[f"M{M}"] = {"gemm_us": round(g_ms * 1e3, 3), "call_us": round(call_ms * 1e3, 3),
+                        "GB/s": round(nbytes / (g_ms * 1e-3) / 1e9, 1),
+                        "frac_hbm": round(nbytes / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "bytes": nbytes}
+    return res
+
+
+def cpu_baseline(rows: int = 48):
+    """The oracle as it stands, on a bounded sample of the same workload: encode `rows` activation
+    rows and form their exact product with all 34816 output columns (the weights are encoded
+    beforehand, untimed, as on the GPU).  NumPy's int64 matmul runs on one thread."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    w = W.WORKLOADS[3]
+    a = W.activations(w, rows)
+    segs = w.seg_offsets
+    wt = W.weights(w)
+    wc, ws, gw = oracle.quantize_segments(wt, segs)
+    del wt
+    g_a = np.float32(2688.0 / np.abs(a).max())
+    t0 = time.perf_counter()
+    ac, as_, _ = oracle.quantize(a, g_a)
+    oracle.gemm_exact(ac, as_, g_a, wc, ws, gw, segs)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} of {w.M} activation rows x all {w.N} columns, K={w.K} "
+                      f"(encode + exact int64 product), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the hot path here is the single-GPU W4A4 linear "
+              "layer, and multi-GPU runs are not part of this build (use --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_block_scaled_nvfp4_amd as nv
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    nv.load_library()
+
+    p = prefill(args, torch, nv, W)
+    dec = None if args.no_decode else decode(args, torch, nv, W)
+    cpu = None if args.no_cpu_baseline else cpu_baseline()
+
+    w = p["w"]
+    value = p["flops"] / (p["ms_step"] * 1e-3) / 1e12
+    achieved = p["flops"] / (p["gemm_ms"] * 1e-3) / 1e12
+    line = {
+        "metric": "NVFP4 W4A4 GEMM TFLOP/s (prefill M=8192) + decode GB/s, % of MI355X roofline",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(p["ms_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 operands decoded exactly to f16, f16 MFMA, f32 accumulate",
+        "data": "synthetic (seeded; bf16 N(0,1) activations with 1% Student-t(3)x50 channels, "
+                "N(0,0.02) weights)",
+        "config": {"workload": w.name, "M": w.M, "K": w.K, "N": w.N,
+                   "segments": list(w.seg_sizes), "act_scale": "static", "output": "f32"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "fused_nvfp4_gemm (tiled)", "kernel_ms": round(p["gemm_ms"], 4),
+                     "frac_of_mxfp4_peak": round(achieved / MFMA_FP4_PEAK_TFLOPS, 4)},
+        "quantize": {"ms": round(p["quant_ms"], 4),
+                     "GB/s": round(p["q_bytes"] / (p["quant_ms"] * 1e-3) / 1e9, 1),
+                     "frac_hbm": round(p["q_bytes"] / (p["quant_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "decode": dec,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

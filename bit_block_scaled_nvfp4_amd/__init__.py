@@ -1,0 +1,183 @@
+"""Python binding of libnvfp4 (NVFP4 W4A4 linear layer on MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels of libnvfp4.so,
+reached through the C ABI declared in ``include/nvfp4.h``.  PyTorch provides device memory and the
+current HIP stream.  If the library has not been built, importing works but every call raises; the
+library is never replaced by a CPU or PyTorch fallback.
+
+Entry points (same names as the C ABI):
+
+* ``nvfp4_quantize(x, global_scale=None)`` -> ``(codes, scales, global_scale)``
+* ``nvfp4_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, out_dtype)`` -> ``C``
+* ``fused_nvfp4_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_gscale, seg_offsets,
+  out_dtype)`` -> ``C``
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libnvfp4.so")
+
+NVFP4_OK, NVFP4_EINVAL, NVFP4_ESHAPE, NVFP4_EALIGN, NVFP4_EDEVICE = range(5)
+NVFP4_F32, NVFP4_BF16, NVFP4_F16 = 0, 1, 2
+NVFP4_MAX_SEGMENTS = 16
+
+#: every symbol include/nvfp4.h declares
+EXPORTED_SYMBOLS = ("nvfp4_quantize", "nvfp4_gemm", "fused_nvfp4_gemm", "nvfp4_status_string",
+                    "nvfp4_version")
+
+_lib = None
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libnvfp4.so (once) and declare the C signatures.  Raises if it is missing."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"libnvfp4.so not found at {p}: build it with `python -m bit_block_scaled_nvfp4_amd.build`"
+            " (there is no fallback implementation)")
+    lib = ctypes.CDLL(p)
+    c_i64, c_int, c_vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    lib.nvfp4_quantize.argtypes = [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_int, c_vp, c_vp, c_vp]
+    lib.nvfp4_quantize.restype = c_int
+    lib.nvfp4_gemm.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_int,
+                               c_i64, c_vp]
+    lib.nvfp4_gemm.restype = c_int
+    lib.fused_nvfp4_gemm.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.POINTER(c_i64),
+                                     c_int, c_i64, c_i64, c_i64, c_vp, c_int, c_i64, c_vp]
+    lib.fused_nvfp4_gemm.restype = c_int
+    lib.nvfp4_status_string.argtypes = [c_int]
+    lib.nvfp4_status_string.restype = ctypes.c_char_p
+    lib.nvfp4_version.argtypes = []
+    lib.nvfp4_version.restype = c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().nvfp4_status_string(status).decode()
+
+
+def _check(status: int):
+    if status != NVFP4_OK:
+        msg = status_string(status)
+        if status == NVFP4_EDEVICE:
+            raise Nvfp4Error(status, msg)
+        raise Nvfp4Error(status, msg)
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t == torch.float32:
+        return NVFP4_F32
+    if t == torch.bfloat16:
+        return NVFP4_BF16
+    if t == torch.float16:
+        return NVFP4_F16
+    raise ValueError(f"unsupported dtype {t}")
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+
+
+def nvfp4_quantize(x, global_scale=None, codes=None, scales=None):
+    """Encode ``x[rows, cols]`` (f32/bf16/f16, row-contiguous) as NVFP4 on the GPU.
+
+    ``global_scale``: a 1-element float32 device tensor holding a static scale, or None for the
+    dynamic scale, which is then returned in a new 1-element tensor.  Returns
+    ``(codes uint8[rows, cols/2], scales uint8[rows, cols/16], global_scale)``."""
+    torch = _torch()
+    lib = load_library()
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with contiguous rows")
+    _require_cuda(x)
+    rows, cols = x.shape
+    dynamic = global_scale is None
+    if dynamic:
+        global_scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    _require_cuda(global_scale)
+    if codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=x.device)
+    _check(lib.nvfp4_quantize(_ptr(x), _dtype_code(x.dtype), rows, cols, x.stride(0),
+                              _ptr(global_scale), int(dynamic), _ptr(codes), _ptr(scales),
+                              _stream(x.device)))
+    return codes, scales, global_scale
+
+
+def _out(M, N, out_dtype, device):
+    torch = _torch()
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    return torch.empty((M, N), dtype=out_dtype, device=device)
+
+
+def nvfp4_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, out_dtype=None, out=None):
+    """``C = A @ W^T / (gA * gW)`` for NVFP4 ``A[M, K]`` and ``W[N, K]``."""
+    torch = _torch()
+    lib = load_library()
+    _require_cuda(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale)
+    M, K = a_codes.shape[0], a_codes.shape[1] * 2
+    N = w_codes.shape[0]
+    if w_codes.shape[1] * 2 != K:
+        raise ValueError("A and W disagree on K")
+    if out is None:
+        out = _out(M, N, out_dtype or torch.float32, a_codes.device)
+    _check(lib.nvfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(a_gscale), _ptr(w_codes),
+                          _ptr(w_scales), _ptr(w_gscale), M, N, K, _ptr(out),
+                          _dtype_code(out.dtype), out.stride(0), _stream(a_codes.device)))
+    return out
+
+
+def fused_nvfp4_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_gscale, seg_offsets,
+                     out_dtype=None, out=None):
+    """Product with a fused weight of ``len(seg_offsets) - 1`` calibrated modules; columns
+    ``[seg_offsets[j], seg_offsets[j+1])`` are divided by ``gA * seg_gscale[j]``."""
+    torch = _torch()
+    lib = load_library()
+    _require_cuda(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_gscale)
+    M, K = a_codes.shape[0], a_codes.shape[1] * 2
+    N = w_codes.shape[0]
+    if w_codes.shape[1] * 2 != K:
+        raise ValueError("A and W disagree on K")
+    offs = [int(o) for o in seg_offsets]
+    nseg = len(offs) - 1
+    arr = (ctypes.c_int64 * len(offs))(*offs)
+    if out is None:
+        out = _out(M, N, out_dtype or torch.float32, a_codes.device)
+    _check(lib.fused_nvfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(a_gscale), _ptr(w_codes),
+                                _ptr(w_scales), _ptr(seg_gscale), arr, nseg, M, N, K, _ptr(out),
+                                _dtype_code(out.dtype), out.stride(0), _stream(a_codes.device)))
+    return out

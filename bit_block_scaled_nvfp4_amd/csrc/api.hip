@@ -1,0 +1,149 @@
+// Host layer of libnvfp4: argument validation (before any HIP call), kernel selection, launch.
+// The entry points and their contracts are declared in include/nvfp4.h.
+#include <stdint.h>
+
+#include "nvfp4_internal.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int64_t dtype_bytes(nvfp4_dtype d) { return d == NVFP4_F32 ? 4 : 2; }
+
+bool valid_in_dtype(int d) { return d == NVFP4_F32 || d == NVFP4_BF16 || d == NVFP4_F16; }
+
+bool valid_out_dtype(int d) { return d == NVFP4_F32 || d == NVFP4_BF16; }
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+nvfp4_status device_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_EDEVICE; }
+
+// Validation shared by nvfp4_gemm and fused_nvfp4_gemm.
+nvfp4_status check_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                        const uint8_t* w_codes, const uint8_t* w_scales, const float* seg_gscale,
+                        const int64_t* seg_offsets, int nseg, int64_t M, int64_t N, int64_t K,
+                        const void* c, int c_dtype, int64_t ldc) {
+  if (!a_codes || !a_scales || !a_gscale || !w_codes || !w_scales || !seg_gscale || !seg_offsets ||
+      !c)
+    return NVFP4_EINVAL;
+  if (!valid_out_dtype(c_dtype)) return NVFP4_EINVAL;
+  if (nseg < 1 || nseg > NVFP4_MAX_SEGMENTS) return NVFP4_EINVAL;
+  if (M < 0 || N < 0 || K <= 0 || K % 16 != 0) return NVFP4_ESHAPE;
+  if (M > kMaxDim || N > kMaxDim || K >= (int64_t(1) << 24)) return NVFP4_ESHAPE;
+  if (ldc < N || ldc < 1) return NVFP4_ESHAPE;
+  if (M * ldc > (int64_t(1) << 40)) return NVFP4_ESHAPE;
+  if (seg_offsets[0] != 0 || seg_offsets[nseg] != N) return NVFP4_ESHAPE;
+  for (int j = 0; j < nseg; ++j) {
+    const bool empty_problem = (N == 0 && nseg == 1);
+    if (!(seg_offsets[j + 1] > seg_offsets[j]) && !empty_problem) return NVFP4_ESHAPE;
+  }
+  if (!aligned(a_codes, 16) || !aligned(a_scales, 16) || !aligned(w_codes, 16) ||
+      !aligned(w_scales, 16) || !aligned(c, 16) || !aligned(a_gscale, 4) ||
+      !aligned(seg_gscale, 4))
+    return NVFP4_EALIGN;
+  return NVFP4_OK;
+}
+
+nvfp4_status run_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                      const uint8_t* w_codes, const uint8_t* w_scales, const float* seg_gscale,
+                      const int64_t* seg_offsets, int nseg, int64_t M, int64_t N, int64_t K,
+                      void* c, nvfp4_dtype c_dtype, int64_t ldc, void* stream) {
+  nvfp4::GemmArgs a{};
+  a.a_codes = a_codes;
+  a.a_scales = a_scales;
+  a.a_g = a_gscale;
+  a.w_codes = w_codes;
+  a.w_scales = w_scales;
+  a.seg_g = seg_gscale;
+  a.M = (int32_t)M;
+  a.N = (int32_t)N;
+  a.K = (int32_t)K;
+  a.c = c;
+  a.c_bf16 = c_dtype == NVFP4_BF16 ? 1 : 0;
+  a.ldc = ldc;
+  a.seg.nseg = nseg;
+  for (int j = 0; j <= nseg; ++j) a.seg.off[j] = (int32_t)seg_offsets[j];
+  for (int j = nseg + 1; j <= NVFP4_MAX_SEGMENTS; ++j) a.seg.off[j] = (int32_t)N;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  switch (nvfp4::choose_gemm_path(M, K)) {
+    case nvfp4::GemmPath::General:
+      e = nvfp4::launch_gemm_general(a, s);
+      break;
+    case nvfp4::GemmPath::Tiled:
+      e = nvfp4::launch_gemm_tiled(a, s);
+      break;
+    case nvfp4::GemmPath::Skinny:
+      e = nvfp4::launch_gemm_skinny(a, s);
+      break;
+  }
+  return device_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols,
+                            int64_t ldx, float* global_scale, int dynamic, uint8_t* codes,
+                            uint8_t* scales, void* stream) {
+  if (!x || !global_scale || !codes || !scales) return NVFP4_EINVAL;
+  if (!valid_in_dtype(x_dtype)) return NVFP4_EINVAL;
+  if (dynamic != 0 && dynamic != 1) return NVFP4_EINVAL;
+  if (rows < 0 || cols < 0 || cols % 16 != 0) return NVFP4_ESHAPE;
+  if (ldx < cols || ldx < 1) return NVFP4_ESHAPE;
+  if (rows * (cols / 16) >= (int64_t(1) << 31)) return NVFP4_ESHAPE;
+  if (rows > 0 && (rows - 1) * ldx + cols > (int64_t(1) << 40)) return NVFP4_ESHAPE;
+  if (!aligned(x, 16) || (ldx * dtype_bytes(x_dtype)) % 16 != 0) return NVFP4_EALIGN;
+  if (!aligned(codes, 8) || !aligned(global_scale, 4)) return NVFP4_EALIGN;
+  if ((rows == 0 || cols == 0) && !dynamic) return NVFP4_OK;
+  hipError_t e = nvfp4::launch_quantize(x, x_dtype, rows, cols, ldx, global_scale, dynamic, codes,
+                                        scales, reinterpret_cast<hipStream_t>(stream));
+  return device_status(e);
+}
+
+nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                        const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale,
+                        int64_t M, int64_t N, int64_t K, void* c, nvfp4_dtype c_dtype, int64_t ldc,
+                        void* stream) {
+  const int64_t off[2] = {0, N};
+  nvfp4_status st = check_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, off, 1, M,
+                               N, K, c, c_dtype, ldc);
+  if (st != NVFP4_OK) return st;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  return run_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, off, 1, M, N, K, c,
+                  c_dtype, ldc, stream);
+}
+
+nvfp4_status fused_nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
+                              const float* a_gscale, const uint8_t* w_codes,
+                              const uint8_t* w_scales, const float* seg_gscale,
+                              const int64_t* seg_offsets, int nseg, int64_t M, int64_t N,
+                              int64_t K, void* c, nvfp4_dtype c_dtype, int64_t ldc, void* stream) {
+  nvfp4_status st = check_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_gscale,
+                               seg_offsets, nseg, M, N, K, c, c_dtype, ldc);
+  if (st != NVFP4_OK) return st;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  return run_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_gscale, seg_offsets, nseg, M,
+                  N, K, c, c_dtype, ldc, stream);
+}
+
+const char* nvfp4_status_string(nvfp4_status s) {
+  switch (s) {
+    case NVFP4_OK:
+      return "NVFP4_OK: success";
+    case NVFP4_EINVAL:
+      return "NVFP4_EINVAL: null pointer, unknown dtype, bad flag or segment count";
+    case NVFP4_ESHAPE:
+      return "NVFP4_ESHAPE: bad size, leading dimension, K not a multiple of 16, or segment offsets";
+    case NVFP4_EALIGN:
+      return "NVFP4_EALIGN: pointer or row pitch not aligned as required";
+    case NVFP4_EDEVICE:
+      return "NVFP4_EDEVICE: the HIP runtime reported an error";
+  }
+  return "NVFP4: unknown status";
+}
+
+int nvfp4_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// Internal declarations shared by the host layer and the kernels of libnvfp4 (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nvfp4.h"
+
+namespace nvfp4 {
+
+// Per-launch segment table, passed by value in the kernel arguments.  Column n belongs to the
+// segment j with off[j] <= n < off[j+1]; its epilogue factor is 1 / (gA * seg_g[j]).
+struct SegTable {
+  int32_t nseg;
+  int32_t off[NVFP4_MAX_SEGMENTS + 1];
+};
+
+struct GemmArgs {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const float* a_g;
+  const uint8_t* w_codes;
+  const uint8_t* w_scales;
+  const float* seg_g;
+  int32_t M, N, K;
+  void* c;
+  int32_t c_bf16;  // 0: f32 output, 1: bf16 output
+  int64_t ldc;
+  SegTable seg;
+};
+
+// Kernel launchers (defined next to their kernels).  They return the launch status.
+hipError_t launch_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
+                           float* g, int dynamic, uint8_t* codes, uint8_t* scales,
+                           hipStream_t stream);
+hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_gemm_general(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);
+
+// Which kernel family serves a problem.  The choice depends on M and K only, never on N, so a
+// fused product and its per-segment products run the same kernel with the same accumulation order.
+enum class GemmPath { General, Tiled, Skinny };
+GemmPath choose_gemm_path(int64_t M, int64_t K);
+
+}  // namespace nvfp4

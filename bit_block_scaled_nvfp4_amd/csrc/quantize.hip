@@ -1,0 +1,224 @@
+// NVFP4 encoder for gfx950: one FP32 global scale per tensor, one E4M3 scale per 16 consecutive
+// elements of a row, E2M1 element codes packed two per byte.
+//
+// Source: "Why Gated DeltaNet Survives 4-Bit Quantization" (arXiv 2609.04098), ai.info summary,
+// "Methodology in Plain English" (E2M1 values with an E4M3 scale per 16-element block; the block's
+// largest value fixes the scale) and "Main Findings" (one FP32 global scale per module).  The
+// rounding rules the pages leave open are the ones stated in include/nvfp4.h; every operation
+// below is one IEEE binary32 operation in that order (this file is built with -ffp-contract=off
+// and correctly rounded division), so the codes are bit-exact with the CPU reference encoder.
+//
+// Work split: one thread encodes one 16-element block (32 bytes of bf16/f16 or 64 bytes of f32 in,
+// 8 code bytes and 1 scale byte out).  Consecutive threads take consecutive blocks of a row, so
+// loads and stores of a wavefront are contiguous.  The kernel is bound by HBM bandwidth.
+#include "nvfp4_internal.h"
+
+namespace nvfp4 {
+namespace {
+
+constexpr int kThreads = 256;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---- element loading: 16 consecutive elements widened exactly to f32 --------------------------
+
+template <nvfp4_dtype DT>
+__device__ __forceinline__ void load_block(const void* base, float (&v)[16]);
+
+template <>
+__device__ __forceinline__ void load_block<NVFP4_F32>(const void* base, float (&v)[16]) {
+  const f32x4* p = reinterpret_cast<const f32x4*>(base);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f32x4 q = __builtin_nontemporal_load(p + i);
+    v[4 * i + 0] = q.x;
+    v[4 * i + 1] = q.y;
+    v[4 * i + 2] = q.z;
+    v[4 * i + 3] = q.w;
+  }
+}
+
+template <>
+__device__ __forceinline__ void load_block<NVFP4_BF16>(const void* base, float (&v)[16]) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(base);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    u32x4 q = __builtin_nontemporal_load(p + i);
+    uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * i + 2 * j + 0] = __uint_as_float(w[j] << 16);
+      v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  }
+}
+
+template <>
+__device__ __forceinline__ void load_block<NVFP4_F16>(const void* base, float (&v)[16]) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(base);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    u32x4 q = __builtin_nontemporal_load(p + i);
+    uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      _Float16 lo = __builtin_bit_cast(_Float16, (uint16_t)(w[j] & 0xFFFFu));
+      _Float16 hi = __builtin_bit_cast(_Float16, (uint16_t)(w[j] >> 16));
+      v[8 * i + 2 * j + 0] = (float)lo;
+      v[8 * i + 2 * j + 1] = (float)hi;
+    }
+  }
+}
+
+template <nvfp4_dtype DT>
+constexpr int elem_bytes() {
+  return DT == NVFP4_F32 ? 4 : 2;
+}
+
+// ---- the two codecs ------------------------------------------------------------------------
+
+// Non-negative binary32 -> OCP E4M3 code: nearest, ties to the even code, >= 448 saturates to
+// 0x7E, subnormal codes kept.  Below 2^-6 the E4M3 grid is the multiples of 2^-9, so the code is
+// round-to-nearest-even of s * 512 (exact product).  In the normal range the code is the binary32
+// pattern rounded to 3 mantissa bits (nearest-even on the 20 dropped bits, carries into the
+// exponent are the correct binade change) and rebiased: code = (bits >> 20) - ((127 - 7) << 3).
+__device__ __forceinline__ uint32_t e4m3_encode(float s) {
+  if (!(s < 448.0f)) return 0x7Eu;
+  if (s < 0.015625f) return (uint32_t)__builtin_rintf(s * 512.0f);
+  uint32_t u = __float_as_uint(s);
+  u = u + 0x7FFFFu + ((u >> 20) & 1u);
+  return (u >> 20) - 960u;
+}
+
+// Exact binary32 value of an E4M3 code 0x00..0x7E.
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  return c < 8u ? (float)c * 0.001953125f : __uint_as_float((c + 960u) << 20);
+}
+
+// Non-negative binary32 (or +inf) -> E2M1 magnitude index: nearest, ties to the even index,
+// saturating at 6.  Below 1 the grid is {0, 0.5, 1}: round-to-nearest-even of 2y.  From 1 up the
+// grid keeps one mantissa bit: round the pattern to 1 mantissa bit (nearest-even on 22 dropped
+// bits) and read exponent and that bit as the index, (bits >> 22) - 252, clamped at 7.
+__device__ __forceinline__ uint32_t e2m1_index(float y) {
+  if (y < 1.0f) return (uint32_t)__builtin_rintf(y * 2.0f);
+  uint32_t u = __float_as_uint(y);
+  u = (u + 0x1FFFFFu + ((u >> 22) & 1u)) >> 22;
+  uint32_t i = u - 252u;
+  return i > 7u ? 7u : i;
+}
+
+__device__ __forceinline__ float read_global_scale(const float* g, int dynamic) {
+  float v = __builtin_nontemporal_load(g);
+  if (!dynamic) return v;
+  // dynamic: *g holds amax(|x|) at this point (written by amax_kernel)
+  return v == 0.0f ? 1.0f : 2688.0f / v;
+}
+
+template <nvfp4_dtype DT>
+__global__ void __launch_bounds__(kThreads)
+quantize_kernel(const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t nb, uint32_t total,
+                const float* __restrict__ gptr, int dynamic, uint8_t* __restrict__ codes,
+                uint8_t* __restrict__ scales) {
+  const uint32_t b = blockIdx.x * kThreads + threadIdx.x;
+  if (b >= total) return;
+  const float g = read_global_scale(gptr, dynamic);
+  const float gs6 = g / 6.0f;
+  const uint32_t row = b / nb;
+  const uint32_t j = b - row * nb;
+
+  float v[16];
+  load_block<DT>(x + (int64_t)row * ldx_bytes + (int64_t)j * 16 * elem_bytes<DT>(), v);
+
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const uint32_t sc = e4m3_encode(amax * gs6);
+  const float sd = e4m3_value(sc);
+  // sd == 0: r = 0 makes every magnitude 0 (finite inputs)
+  const float r = sd > 0.0f ? g / sd : 0.0f;
+
+  uint32_t word[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t code = e2m1_index(fabsf(v[i]) * r) | ((__float_as_uint(v[i]) >> 31) << 3);
+    word[i >> 3] |= code << (4 * (i & 7));
+  }
+  uint2 out;
+  out.x = word[0];
+  out.y = word[1];
+  *reinterpret_cast<uint2*>(codes + (int64_t)b * 8) = out;
+  scales[b] = (uint8_t)sc;
+}
+
+// Tensor-wide max |x| (exact, order-free) into *out as a binary32 bit pattern: for non-negative
+// floats the unsigned integer order of the bit patterns is the numeric order, so atomicMax on the
+// pattern is the float max.  *out must hold +0.0 before the launch.
+template <nvfp4_dtype DT>
+__global__ void __launch_bounds__(kThreads)
+amax_kernel(const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t nb, uint32_t total,
+            float* out) {
+  float m = 0.0f;
+  for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < total; b += gridDim.x * kThreads) {
+    const uint32_t row = b / nb;
+    const uint32_t j = b - row * nb;
+    float v[16];
+    load_block<DT>(x + (int64_t)row * ldx_bytes + (int64_t)j * 16 * elem_bytes<DT>(), v);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0 && m > 0.0f)
+    atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(m));
+}
+
+__global__ void fill_zero_kernel(float* p) { *p = 0.0f; }
+
+__global__ void finalize_dynamic_scale_kernel(float* p) {
+  const float amax = *p;
+  *p = amax == 0.0f ? 1.0f : 2688.0f / amax;
+}
+
+template <nvfp4_dtype DT>
+hipError_t launch_typed(const void* x, int64_t rows, int64_t cols, int64_t ldx, float* g,
+                        int dynamic, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  const uint32_t nb = (uint32_t)(cols / 16);
+  const uint32_t total = (uint32_t)(rows * (cols / 16));
+  const int64_t ldx_bytes = ldx * elem_bytes<DT>();
+  const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
+  if (dynamic) {
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(1), dim3(1), 0, stream, g);
+    if (total > 0) {
+      uint32_t grid = (total + kThreads - 1) / kThreads;
+      grid = grid > 4096u ? 4096u : grid;
+      hipLaunchKernelGGL(amax_kernel<DT>, dim3(grid), dim3(kThreads), 0, stream, xb, ldx_bytes, nb,
+                         total, g);
+    }
+  }
+  if (total > 0) {
+    const uint32_t grid = (total + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(quantize_kernel<DT>, dim3(grid), dim3(kThreads), 0, stream, xb, ldx_bytes,
+                       nb, total, g, dynamic, codes, scales);
+  }
+  if (dynamic) hipLaunchKernelGGL(finalize_dynamic_scale_kernel, dim3(1), dim3(1), 0, stream, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
+                           float* g, int dynamic, uint8_t* codes, uint8_t* scales,
+                           hipStream_t stream) {
+  switch (dt) {
+    case NVFP4_F32:
+      return launch_typed<NVFP4_F32>(x, rows, cols, ldx, g, dynamic, codes, scales, stream);
+    case NVFP4_BF16:
+      return launch_typed<NVFP4_BF16>(x, rows, cols, ldx, g, dynamic, codes, scales, stream);
+    case NVFP4_F16:
+      return launch_typed<NVFP4_F16>(x, rows, cols, ldx, g, dynamic, codes, scales, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,150 @@
+/*
+ * nvfp4.h -- C ABI of the NVFP4 W4A4 linear-layer library for AMD Instinct MI355X (gfx950).
+ *
+ * The library implements the three steps of an NVFP4 W4A4 linear layer as described in
+ * "Why Gated DeltaNet Survives 4-Bit Quantization: NVFP4 W4A4 for the Recurrent Half of a Hybrid
+ * 27B LLM" (arXiv 2609.04098), ai.info AI-summary page:
+ *
+ *   1. encoding a tensor to NVFP4 -- 4-bit E2M1 values with one FP8 E4M3 scale per 16-element
+ *      block, the block's largest value fixing that scale ("Methodology in Plain English"), under
+ *      one FP32 global scale per tensor or calibrated module ("Main Findings");
+ *   2. the W4A4 product of two NVFP4 operands with FP32 accumulation;
+ *   3. fused modules: several calibrated modules concatenated along the output dimension and served
+ *      as one product, each output segment divided by its own module's global scale.  Applying the
+ *      largest of the modules' global scales to every segment instead is the serving defect that
+ *      "Main Findings" reports (paired scales 1.82x and 2.75x apart); passing a table filled with
+ *      that maximum reproduces it.
+ *
+ * Number format (the pages name the formats; the encoding rules the pages leave open are fixed
+ * here and implemented identically by the CPU oracle used in the tests):
+ *   - E2M1 magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}; code = sign << 3 | magnitude index.
+ *   - E4M3 is OCP e4m3fn (bias 7, max 448, no infinities); 0x7F is never produced.
+ *   - g: FP32 global scale, encode direction (value ~= V * sd / g).  Dynamic g = 2688 / amax(x)
+ *     (2688 = 6 * 448), or 1 when the tensor is all zeros.
+ *   - per block of 16 consecutive elements of a row: s = fl(amax_block * fl(g / 6)), rounded to
+ *     E4M3 (nearest, ties to even code, >= 448 saturates to 0x7E, subnormals kept); sd = its
+ *     value; each element y = fl(|x| * fl(g / sd)) rounded to E2M1 (nearest, ties to even code,
+ *     saturating at 6); sd == 0 gives magnitude 0; the sign bit is always copied (so -0.0 -> 0x8).
+ *   - layout: codes [rows, cols/2] bytes, element 2j in the low nibble of byte j; scales
+ *     [rows, cols/16] E4M3 bytes, row-major, no swizzle.  Blocks run along the row (for the
+ *     product: along the contraction dimension K of both operands).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers, except the segment-offset array of
+ *     fused_nvfp4_gemm, which is a HOST array.  The caller owns every buffer; the library
+ *     allocates nothing, keeps no mutable global state, is thread-safe, and enqueues its work
+ *     asynchronously on `stream` (a hipStream_t; NULL = the null stream).  Nothing synchronises
+ *     with the host.
+ *   - Every argument check happens on the host before any HIP call: a non-OK status other than
+ *     NVFP4_EDEVICE means nothing was enqueued.  NVFP4_EDEVICE reports a HIP launch error.
+ *   - Sizes are element counts; leading dimensions (ld*) are in elements of that tensor.
+ *   - Empty problems (rows, M or N equal to 0) are valid and enqueue nothing.
+ *   - NaN and infinite inputs are unsupported: their codes are unspecified (no error is raised).
+ *   - Results are deterministic: identical inputs give identical bits on every call.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nvfp4_status {
+  NVFP4_OK = 0,
+  NVFP4_EINVAL = 1,  /* NULL pointer, unknown dtype, nseg out of range, bad flag value         */
+  NVFP4_ESHAPE = 2,  /* negative size, cols/K not a multiple of 16, ld < row length, segment
+                        offsets not rising strictly from 0 to N, problem too large             */
+  NVFP4_EALIGN = 3,  /* a pointer or a row pitch is not aligned as the entry point requires  */
+  NVFP4_EDEVICE = 4  /* the HIP runtime reported an error when the work was enqueued         */
+} nvfp4_status;
+
+typedef enum nvfp4_dtype {
+  NVFP4_F32 = 0,
+  NVFP4_BF16 = 1,
+  NVFP4_F16 = 2
+} nvfp4_dtype;
+
+/* Largest number of segments (calibrated modules) in one fused product. */
+#define NVFP4_MAX_SEGMENTS 16
+
+/*
+ * nvfp4_quantize -- encode x[rows, cols] (row pitch ldx elements) to NVFP4.
+ *
+ * Source: ai.info summary, "Methodology in Plain English" (E2M1 values, E4M3 scale per 16-element
+ * block, the block's largest value fixes the scale) and "Main Findings" (one FP32 global scale per
+ * module); activations are encoded on every call, weights once offline with the same routine.
+ *
+ *   x            device, dtype x_dtype (F32, BF16 or F16); 16-byte aligned; ldx * sizeof(elem) a
+ *                multiple of 16 bytes; ldx >= cols.
+ *   rows, cols   rows >= 0; cols >= 0 and a multiple of 16.
+ *   global_scale device, one float.  dynamic == 0: read (static, e.g. calibrated, scale; must be
+ *                positive and finite -- not checked, it lives on the device).  dynamic == 1: the
+ *                dynamic scale 2688/amax(x) is computed and WRITTEN here (stream-ordered).
+ *   codes        device, rows * cols/2 bytes, row pitch cols/2; 8-byte aligned.
+ *   scales       device, rows * cols/16 bytes, row pitch cols/16.
+ *   stream       hipStream_t.
+ * Codes and scales are bit-exact with the rules in the file header.
+ */
+nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols,
+                            int64_t ldx, float* global_scale, int dynamic, uint8_t* codes,
+                            uint8_t* scales, void* stream);
+
+/*
+ * nvfp4_gemm -- C[m, n] = sum_k a[m,k] * w[n,k] / (gA * gW) for NVFP4 operands; equivalent to
+ * fused_nvfp4_gemm with one segment.
+ *
+ * Source: ai.info summary, "Main Findings" and "Methodology in Plain English" (W4A4: weights and
+ * activations both NVFP4); the sum is accumulated in FP32 from exactly decoded products.
+ *
+ *   a_codes, a_scales   device, activations [M, K] encoded by nvfp4_quantize (pitches K/2, K/16).
+ *   a_gscale            device, one float: gA.
+ *   w_codes, w_scales   device, weights [N, K] (nn.Linear layout) encoded along K.
+ *   w_gscale            device, one float: gW.
+ *   M, N, K             M, N >= 0; K > 0 and a multiple of 16; K < 2^24.
+ *   c                   device, [M, N] with row pitch ldc >= N, dtype c_dtype (F32 or BF16); the
+ *                       product is rounded once from FP32 to BF16 when c_dtype is BF16.
+ *   Alignment: every code/scale pointer 16-byte aligned and c 16-byte aligned.  K a multiple of 64
+ *   selects the tiled kernels; other multiples of 16 take a slower general kernel.
+ * Accuracy: |C - exact| <= 1e-4 * sum_k |a*w| / (gA*gW) per element (FP32 accumulation order is
+ * unspecified), deterministic across calls.
+ */
+nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                        const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale,
+                        int64_t M, int64_t N, int64_t K, void* c, nvfp4_dtype c_dtype, int64_t ldc,
+                        void* stream);
+
+/*
+ * fused_nvfp4_gemm -- product with a fused weight made of nseg calibrated modules concatenated
+ * along N: columns [seg_offsets[j], seg_offsets[j+1]) come from module j, whose weights were
+ * encoded with global scale seg_gscale[j]; those columns are divided by gA * seg_gscale[j].
+ *
+ * Source: ai.info summary, "Main Findings" (one FP32 global scale per module from calibration;
+ * in_proj_qkv + z and in_proj_b + a served fused) and "Methodology in Plain English" (the repair of
+ * the fused global scales).  Filling seg_gscale with max_j gW[j] reproduces the defect.
+ *
+ *   seg_gscale   device, nseg floats.
+ *   seg_offsets  HOST, nseg + 1 int64: 0 = o_0 < o_1 < ... < o_nseg = N.  Read during the call
+ *                only; may be freed on return.
+ *   nseg         1 .. NVFP4_MAX_SEGMENTS.
+ *   other arguments as nvfp4_gemm.  With N == 0 the offsets must be {0, 0} and nseg == 1.
+ * The result equals, bit for bit, the concatenation of one nvfp4_gemm per segment.
+ */
+nvfp4_status fused_nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
+                              const float* a_gscale, const uint8_t* w_codes,
+                              const uint8_t* w_scales, const float* seg_gscale,
+                              const int64_t* seg_offsets, int nseg, int64_t M, int64_t N,
+                              int64_t K, void* c, nvfp4_dtype c_dtype, int64_t ldc, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* nvfp4_status_string(nvfp4_status s);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int nvfp4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

@@ -1,0 +1,129 @@
+"""The C-ABI library (CPU side): it loads, exports every function include/nvfp4.h declares, and
+rejects every malformed call with the documented status before touching the device.
+
+These tests pass fake but aligned device addresses: every call here fails validation (or is an
+empty problem), so no HIP call is made and no GPU is needed.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import bit_block_scaled_nvfp4_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(nv.LIB_PATH),
+                                reason="libnvfp4.so not built (run __graft_entry__.build())")
+
+P = 0x10000  # a fake, 256-byte aligned device address (never dereferenced here)
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S[^\n(]*?\b(nvfp4_\w+|fused_nvfp4_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = _declared_functions()
+    for n in ("nvfp4_quantize", "nvfp4_gemm", "fused_nvfp4_gemm", "nvfp4_status_string"):
+        assert n in names
+    assert sorted(nv.EXPORTED_SYMBOLS) == names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", nv.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in _declared_functions():
+        assert name in exported, name
+    lib = nv.load_library()
+    for name in _declared_functions():
+        assert hasattr(lib, name)
+
+
+def test_status_strings_and_version():
+    for s in range(5):
+        assert nv.status_string(s).startswith("NVFP4")
+    assert "unknown" in nv.status_string(99)
+    assert nv.load_library().nvfp4_version() >= 100
+
+
+def _q(**kw):
+    a = dict(x=P, dt=nv.NVFP4_BF16, rows=4, cols=32, ldx=32, g=P, dyn=0, codes=P, scales=P, s=None)
+    a.update(kw)
+    return nv.load_library().nvfp4_quantize(a["x"], a["dt"], a["rows"], a["cols"], a["ldx"], a["g"],
+                                            a["dyn"], a["codes"], a["scales"], a["s"])
+
+
+def test_quantize_validation():
+    assert _q(x=None) == nv.NVFP4_EINVAL
+    assert _q(g=None) == nv.NVFP4_EINVAL
+    assert _q(codes=None) == nv.NVFP4_EINVAL
+    assert _q(scales=None) == nv.NVFP4_EINVAL
+    assert _q(dt=7) == nv.NVFP4_EINVAL
+    assert _q(dyn=2) == nv.NVFP4_EINVAL
+    assert _q(cols=24, ldx=24) == nv.NVFP4_ESHAPE
+    assert _q(rows=-1) == nv.NVFP4_ESHAPE
+    assert _q(ldx=16) == nv.NVFP4_ESHAPE
+    assert _q(x=P + 8) == nv.NVFP4_EALIGN
+    assert _q(ldx=36) == nv.NVFP4_EALIGN  # 72-byte bf16 row pitch
+    assert _q(codes=P + 4) == nv.NVFP4_EALIGN
+    assert _q(rows=1 << 28, cols=1 << 8, ldx=1 << 8) == nv.NVFP4_ESHAPE  # 2^32 blocks
+    # empty static problems are valid and enqueue nothing
+    assert _q(rows=0) == nv.NVFP4_OK
+    assert _q(cols=0, ldx=16) == nv.NVFP4_OK
+
+
+def _g(fused=False, **kw):
+    a = dict(ac=P, as_=P, ga=P, wc=P, ws=P, gw=P, M=64, N=96, K=512, c=P, cdt=nv.NVFP4_F32, ldc=96,
+             offs=None, nseg=None, s=None)
+    a.update(kw)
+    lib = nv.load_library()
+    if not fused:
+        return lib.nvfp4_gemm(a["ac"], a["as_"], a["ga"], a["wc"], a["ws"], a["gw"], a["M"], a["N"],
+                              a["K"], a["c"], a["cdt"], a["ldc"], a["s"])
+    offs = a["offs"] if a["offs"] is not None else [0, a["N"]]
+    nseg = a["nseg"] if a["nseg"] is not None else len(offs) - 1
+    arr = (ctypes.c_int64 * max(len(offs), 1))(*offs)
+    return lib.fused_nvfp4_gemm(a["ac"], a["as_"], a["ga"], a["wc"], a["ws"], a["gw"], arr, nseg,
+                                a["M"], a["N"], a["K"], a["c"], a["cdt"], a["ldc"], a["s"])
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_gemm_validation(fused):
+    E = nv
+    for k in ("ac", "as_", "ga", "wc", "ws", "gw", "c"):
+        assert _g(fused, **{k: None}) == E.NVFP4_EINVAL, k
+    assert _g(fused, cdt=E.NVFP4_F16) == E.NVFP4_EINVAL
+    assert _g(fused, K=40) == E.NVFP4_ESHAPE
+    assert _g(fused, K=0) == E.NVFP4_ESHAPE
+    assert _g(fused, M=-1) == E.NVFP4_ESHAPE
+    assert _g(fused, ldc=95) == E.NVFP4_ESHAPE
+    assert _g(fused, K=1 << 24) == E.NVFP4_ESHAPE
+    assert _g(fused, ac=P + 8) == E.NVFP4_EALIGN
+    assert _g(fused, ws=P + 4) == E.NVFP4_EALIGN
+    assert _g(fused, c=P + 4) == E.NVFP4_EALIGN
+    assert _g(fused, M=0) == E.NVFP4_OK  # empty: nothing enqueued
+
+
+def test_fused_segment_validation():
+    E = nv
+    assert _g(True, offs=[0, 32, 96], nseg=0) == E.NVFP4_EINVAL
+    assert _g(True, offs=list(range(0, 96, 5)) + [96], nseg=20) == E.NVFP4_EINVAL  # > 16 segments
+    assert _g(True, offs=[1, 32, 96]) == E.NVFP4_ESHAPE  # must start at 0
+    assert _g(True, offs=[0, 32, 95]) == E.NVFP4_ESHAPE  # must end at N
+    assert _g(True, offs=[0, 32, 32, 96]) == E.NVFP4_ESHAPE  # strictly rising
+    assert _g(True, offs=[0, 64, 32, 96]) == E.NVFP4_ESHAPE
+    assert _g(True, offs=[0, 0], N=0, ldc=1) == E.NVFP4_OK  # empty problem
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    with pytest.raises(ValueError):
+        nv.nvfp4_quantize(torch.zeros(4, 32))

@@ -1,0 +1,197 @@
+"""GPU parity of nvfp4_gemm and fused_nvfp4_gemm against the oracle's exact product.
+
+Tolerance (stated for FP32 accumulation of exactly decoded products):
+  |C_gpu - C_ref| <= 1e-4 * sum_k |a*w| / (gA gW[seg])  per element, and
+  ||C_gpu - C_ref||_F <= 1e-5 ||C_ref||_F.
+Operands are always encoded by the oracle on the host (never taken from the GPU encoder), uploaded,
+and multiplied on the GPU.  Full-size workloads are checked on sampled rows and columns."""
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import WORKLOADS, activations, random_matrix, weights
+
+from .gpu_util import DEV, check_gemm, log, scalar
+
+pytestmark = pytest.mark.gpu
+
+
+def _up(arr):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(DEV)
+
+
+def _gpu_product(ac, as_, ga, wc, ws, seg_g, segs, out_dtype="f32"):
+    import torch
+
+    import bit_block_scaled_nvfp4_amd as nv
+
+    odt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    C = nv.fused_nvfp4_gemm(_up(ac), _up(as_), scalar(ga), _up(wc), _up(ws),
+                            _up(np.asarray(seg_g, np.float32)), segs, out_dtype=odt)
+    torch.cuda.synchronize()
+    return C.float().cpu().numpy()
+
+
+def _encode(a, w, segs, seg_g=None, ga=None):
+    ac, as_, ga = oracle.quantize(a, ga)
+    wc, ws, gw = oracle.quantize_segments(w, segs, seg_g)
+    return ac, as_, ga, wc, ws, gw
+
+
+def _check(ac, as_, ga, wc, ws, gw, segs, what):
+    C = _gpu_product(ac, as_, ga, wc, ws, gw, segs)
+    R = oracle.gemm_exact(ac, as_, ga, wc, ws, gw, segs)
+    B = oracle.gemm_abs_bound(ac, as_, ga, wc, ws, gw, segs)
+    worst = check_gemm(C, R, B, what)
+    log(f"{what}: worst err / sum|ab| = {worst:.2e}")
+    return C, R
+
+
+def test_workload1_full():
+    w = WORKLOADS[1]
+    a, wt = activations(w), weights(w)
+    enc = _encode(a, wt, w.seg_offsets)
+    _check(*enc, w.seg_offsets, "workload 1")
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1, 1, 16), (1, 37, 64), (5, 70, 48), (33, 65, 80), (31, 129, 128), (64, 64, 64),
+    (129, 130, 192), (200, 300, 1024), (257, 255, 320), (96, 160, 5120),
+])
+def test_ragged_shapes(M, N, K):
+    a = random_matrix(M * 7 + K, M, K, outlier_cols=max(1, K // 100))
+    wt = random_matrix(N * 5 + K, N, K, std=0.02)
+    enc = _encode(a, wt, [0, N])
+    _check(*enc, [0, N], f"M={M} N={N} K={K}")
+
+
+def test_bf16_output():
+    a = random_matrix(3, 100, 256, outlier_cols=3)
+    wt = random_matrix(4, 72, 256, std=0.02)
+    ac, as_, ga, wc, ws, gw = _encode(a, wt, [0, 72])
+    C = _gpu_product(ac, as_, ga, wc, ws, gw, [0, 72], out_dtype="bf16")
+    R = oracle.gemm_exact(ac, as_, ga, wc, ws, gw, [0, 72])
+    # bf16 output: one extra rounding of the FP32 result (relative 2^-9)
+    assert np.all(np.abs(C - R) <= 2.0 ** -8 * np.abs(R) + 1e-4 * oracle.gemm_abs_bound(
+        ac, as_, ga, wc, ws, gw, [0, 72]))
+
+
+def test_fused_equals_per_segment_calls_bitwise():
+    M, K = 96, 512
+    sizes = [64, 64, 128, 48, 48, 7]
+    segs = list(np.cumsum([0] + sizes))
+    N = segs[-1]
+    a = random_matrix(10, M, K, outlier_cols=5)
+    wt = random_matrix(11, N, K, std=0.02)
+    ac, as_, ga, wc, ws, gw = _encode(a, wt, segs)
+    fused = _gpu_product(ac, as_, ga, wc, ws, gw, segs)
+    parts = [_gpu_product(ac, as_, ga, wc[segs[j]:segs[j + 1]], ws[segs[j]:segs[j + 1]], [gw[j]],
+                          [0, sizes[j]]) for j in range(len(sizes))]
+    assert np.array_equal(fused, np.concatenate(parts, axis=1))
+    R = oracle.gemm_exact(ac, as_, ga, wc, ws, gw, segs)
+    check_gemm(fused, R, oracle.gemm_abs_bound(ac, as_, ga, wc, ws, gw, segs), "fused")
+
+
+def test_defective_fused_scale_reproduced_on_gpu():
+    """The pages' defect (largest global scale for every segment) versus the per-segment repair,
+    at the paired ratios 1.82 (qkv/z) and 2.75 (b/a)."""
+    M, K, n = 64, 5120, 96
+    a = random_matrix(20, M, K, outlier_cols=51, outlier_gain=50.0)
+    for ratio in (1.82, 2.75):
+        wt = random_matrix(21, 2 * n, K, std=0.02)
+        g0 = np.float32(20000.0)
+        g1 = np.float32(g0 * np.float32(ratio))
+        segs = [0, n, 2 * n]
+        ac, as_, ga, wc, ws, gw = _encode(a, wt, segs, [g0, g1])
+        good = _gpu_product(ac, as_, ga, wc, ws, gw, segs)
+        bad = _gpu_product(ac, as_, ga, wc, ws, oracle.fused_scale_defect(gw), segs)
+        R = oracle.gemm_exact(ac, as_, ga, wc, ws, gw, segs)
+        check_gemm(good, R, oracle.gemm_abs_bound(ac, as_, ga, wc, ws, gw, segs), "repaired")
+        assert np.array_equal(bad[:, n:], good[:, n:])
+        rel = np.linalg.norm(bad[:, :n] - R[:, :n]) / np.linalg.norm(R[:, :n])
+        assert abs(rel - (1 - 1 / ratio)) < 1e-5, rel
+        log(f"ratio {ratio}: defective segment relative error {rel:.4f}")
+
+
+def test_determinism():
+    a = random_matrix(30, 256, 1024, outlier_cols=5)
+    wt = random_matrix(31, 384, 1024, std=0.02)
+    enc = _encode(a, wt, [0, 384])
+    c1 = _gpu_product(*enc, [0, 384])
+    c2 = _gpu_product(*enc, [0, 384])
+    assert np.array_equal(c1, c2)
+
+
+def _sampled_full_size(wid, M=None):
+    """Full-size product on the GPU (inputs encoded on the GPU from the same seeded tensors, then
+    checked bit for bit against the oracle's encoding on the sampled rows), sampled outputs
+    compared with the oracle's exact product."""
+    import torch
+
+    import bit_block_scaled_nvfp4_amd as nv
+
+    from .gpu_util import to_device
+
+    w = WORKLOADS[wid]
+    M = w.M if M is None else M
+    log(f"workload {wid}: generating A {M}x{w.K}, W {w.N}x{w.K}")
+    a = activations(w, M)
+    wt = weights(w)
+    ga = oracle.dynamic_global_scale(a)
+    segs = w.seg_offsets
+    gw = np.array([oracle.dynamic_global_scale(wt[segs[j]:segs[j + 1]])
+                   for j in range(len(segs) - 1)], np.float32)
+    ad = to_device(a, w.act_dtype)
+    wd = to_device(wt, w.w_dtype)
+    log(f"workload {wid}: encode on GPU")
+    ac_d, as_d, _ = nv.nvfp4_quantize(ad, scalar(ga))
+    wc_d = torch.empty((w.N, w.K // 2), dtype=torch.uint8, device=DEV)
+    ws_d = torch.empty((w.N, w.K // 16), dtype=torch.uint8, device=DEV)
+    for j in range(len(segs) - 1):
+        nv.nvfp4_quantize(wd[segs[j]:segs[j + 1]], scalar(gw[j]), wc_d[segs[j]:segs[j + 1]],
+                          ws_d[segs[j]:segs[j + 1]])
+    del ad, wd
+    log(f"workload {wid}: product on GPU")
+    C = nv.fused_nvfp4_gemm(ac_d, as_d, scalar(ga), wc_d, ws_d, _up(gw), segs)
+    torch.cuda.synchronize()
+
+    rng = np.random.Generator(np.random.PCG64(100 + wid))
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 30, replace=False)]))
+    cols = [0, w.N - 1]
+    for j in range(len(segs) - 1):
+        cols += [segs[j], segs[j + 1] - 1]
+        cols += list(rng.choice(np.arange(segs[j], segs[j + 1]), min(40, segs[j + 1] - segs[j]),
+                                replace=False))
+    cols = np.unique(np.array(cols))
+    log(f"workload {wid}: oracle on {len(rows)} rows x {len(cols)} cols")
+    ac, as_, _ = oracle.quantize(a[rows], ga)
+    assert np.array_equal(ac, ac_d[rows].cpu().numpy()) and np.array_equal(as_, as_d[rows].cpu().numpy())
+    seg_of = np.searchsorted(segs, cols, side="right") - 1
+    wc = np.zeros((len(cols), w.K // 2), np.uint8)
+    ws = np.zeros((len(cols), w.K // 16), np.uint8)
+    for i, (cidx, j) in enumerate(zip(cols, seg_of)):
+        c1, s1, _ = oracle.quantize(wt[cidx:cidx + 1], gw[j])
+        wc[i], ws[i] = c1[0], s1[0]
+    assert np.array_equal(wc, wc_d[cols].cpu().numpy()) and np.array_equal(ws, ws_d[cols].cpu().numpy())
+    # per-column global scales: treat each sampled column as its own one-column segment
+    one = list(range(len(cols) + 1))
+    R = oracle.gemm_exact(ac, as_, ga, wc, ws, gw[seg_of], one)
+    B = oracle.gemm_abs_bound(ac, as_, ga, wc, ws, gw[seg_of], one)
+    got = C[torch.from_numpy(rows).to(DEV)][:, torch.from_numpy(cols).to(DEV)].cpu().numpy()
+    worst = check_gemm(got, R, B, f"workload {wid}")
+    log(f"workload {wid}: worst err / sum|ab| = {worst:.2e}")
+    del C, ac_d, as_d, wc_d, ws_d
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("wid", [2, 3, 5])
+def test_full_size_sampled(wid):
+    _sampled_full_size(wid)
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_decode_shapes(M):
+    _sampled_full_size(4, M)
