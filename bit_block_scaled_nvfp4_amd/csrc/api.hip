@@ -30,6 +30,8 @@ nvfp4_status check_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const f
   if (nseg < 1 || nseg > NVFP4_MAX_SEGMENTS) return NVFP4_EINVAL;
   if (M < 0 || N < 0 || K <= 0 || K % 16 != 0) return NVFP4_ESHAPE;
   if (M > kMaxDim || N > kMaxDim || K >= (int64_t(1) << 24)) return NVFP4_ESHAPE;
+  // each operand's codes must stay below 2 GiB (32-bit row offsets inside the kernels)
+  if (M * (K / 2) >= (int64_t(1) << 31) || N * (K / 2) >= (int64_t(1) << 31)) return NVFP4_ESHAPE;
   if (ldc < N || ldc < 1) return NVFP4_ESHAPE;
   if (M * ldc > (int64_t(1) << 40)) return NVFP4_ESHAPE;
   if (seg_offsets[0] != 0 || seg_offsets[nseg] != N) return NVFP4_ESHAPE;

@@ -74,83 +74,217 @@ struct TileCfg {
   static constexpr int kThreads = WAVES_M * WAVES_N * 64;
   static constexpr int BM = WAVES_M * FM * 32;
   static constexpr int BN = WAVES_N * FN * 32;
-  // one stage: codes of BM + BN rows (32 bytes each per K chunk) and their 4 scale bytes
+  // one LDS stage: the codes of BM + BN rows (32 bytes each per K chunk of 64), then their 4 scale
+  // bytes per row
   static constexpr int kCodesA = BM * 32;
   static constexpr int kCodesB = BN * 32;
   static constexpr int kScalesA = BM * 4;
   static constexpr int kScalesB = BN * 4;
   static constexpr int kStage = kCodesA + kCodesB + kScalesA + kScalesB;
-  static constexpr int kPiecesA = BM * 2 / kThreads;  // 16-byte pieces per thread
+  static constexpr int kPiecesA = BM * 2 / kThreads;  // 16-byte copies per thread per chunk
   static constexpr int kPiecesB = BN * 2 / kThreads;
-  static constexpr int kScaleWords = (BM + BN) / kThreads;  // 4-byte scale words per thread
+  static constexpr int kWordsA = BM / kThreads;  // 4-byte scale copies per thread per chunk
+  static constexpr int kWordsB = BN / kThreads;
   static_assert(BM * 2 % kThreads == 0 && BN * 2 % kThreads == 0, "piece split");
-  static_assert((BM + BN) % kThreads == 0, "scale split");
+  static_assert(BM % kThreads == 0 && BN % kThreads == 0, "scale split");
+  static_assert(FM == 4 && FN == 4, "one 16-byte scale read per operand assumes 4 fragments");
+  static_assert(2 * kStage <= 64 * 1024, "static LDS");
 };
 
+// Per-thread byte offsets of the global rows this thread copies (rows beyond the matrix are
+// clamped to the last row: they are loaded but never stored).
 template <class Cfg>
-struct Prefetch {
-  uint4 a[Cfg::kPiecesA];
-  uint4 b[Cfg::kPiecesB];
-  uint32_t s[Cfg::kScaleWords];
+struct RowOffsets {
+  uint32_t a[Cfg::kPiecesA];
+  uint32_t b[Cfg::kPiecesB];
+  uint32_t sa[Cfg::kWordsA];
+  uint32_t sb[Cfg::kWordsB];
 };
 
-// Global -> registers for K chunk `kc` of the tile.  Piece p of an operand holds row
-// (p / 64) * 32 + (p % 32), bytes [16 * ((p % 64) / 32), +16) of the chunk, and is stored at LDS
-// offset 16 p: each 32-row group becomes 1 KiB laid out [half][row][16 B], which is exactly the
-// order in which the 64 lanes of a fragment read it (lane l at 16 l), so fragment reads are
-// contiguous and free of bank conflicts.
-template <class Cfg>
-__device__ __forceinline__ void load_chunk(const GemmArgs& p, int m0, int n0, int kc,
-                                           Prefetch<Cfg>& f) {
-  const int64_t kb = p.K / 2, ks = p.K / 16;
+// LDS layout of one stage and the copy that fills it.  Copies are direct global->LDS: copy index
+// d = i * threads + tid lands at LDS slot d (16 bytes for codes, 4 bytes for scales), because the
+// 64 lanes of a wavefront write consecutive slots.  The layout is chosen by which global row each
+// copy index fetches:
+//  * codes: slot d holds row (d / 64) * 32 + (d % 32), bytes [16 * ((d % 64) / 32), +16) of the
+//    chunk.  Each 32-row group is 1 KiB laid out [half][row][16 B] -- exactly the order in which
+//    the 64 lanes of a fragment read it (lane l at 16 l): reads are contiguous, conflict-free.
+//  * scales: slot d holds the 4 scale bytes of row (d / (32F)) * 32F + (d % F) * 32 + (d / F) % 32
+//    (F fragments per wavefront): the F scale words one lane needs sit in one 16-byte slot group.
+template <int F>
+__device__ __forceinline__ int scale_slot_row(int d) {
+  return (d / (32 * F)) * (32 * F) + (d % F) * 32 + (d / F) % 32;
+}
+
+template <class Cfg, int FM, int FN>
+__device__ __forceinline__ void row_offsets(const GemmArgs& p, int m0, int n0, RowOffsets<Cfg>& o) {
+  const uint32_t kb = (uint32_t)p.K / 2, ks = (uint32_t)p.K / 16;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < Cfg::kPiecesA; ++i) {
-    const int pc = tid + i * Cfg::kThreads;
-    const int row = (pc >> 6) * 32 + (pc & 31);
-    const int gm = min(m0 + row, p.M - 1);
-    f.a[i] = *reinterpret_cast<const uint4*>(p.a_codes + gm * kb + kc * 32 + ((pc >> 5) & 1) * 16);
+    const int d = tid + i * Cfg::kThreads;
+    const int row = (d >> 6) * 32 + (d & 31);
+    o.a[i] = (uint32_t)min(m0 + row, p.M - 1) * kb + ((d >> 5) & 1) * 16;
   }
 #pragma unroll
   for (int i = 0; i < Cfg::kPiecesB; ++i) {
-    const int pc = tid + i * Cfg::kThreads;
-    const int row = (pc >> 6) * 32 + (pc & 31);
-    const int gn = min(n0 + row, p.N - 1);
-    f.b[i] = *reinterpret_cast<const uint4*>(p.w_codes + gn * kb + kc * 32 + ((pc >> 5) & 1) * 16);
+    const int d = tid + i * Cfg::kThreads;
+    const int row = (d >> 6) * 32 + (d & 31);
+    o.b[i] = (uint32_t)min(n0 + row, p.N - 1) * kb + ((d >> 5) & 1) * 16;
   }
 #pragma unroll
-  for (int i = 0; i < Cfg::kScaleWords; ++i) {
-    const int w = tid + i * Cfg::kThreads;
-    if (w < Cfg::BM) {
-      const int gm = min(m0 + w, p.M - 1);
-      f.s[i] = *reinterpret_cast<const uint32_t*>(p.a_scales + gm * ks + kc * 4);
-    } else {
-      const int gn = min(n0 + (w - Cfg::BM), p.N - 1);
-      f.s[i] = *reinterpret_cast<const uint32_t*>(p.w_scales + gn * ks + kc * 4);
-    }
-  }
+  for (int i = 0; i < Cfg::kWordsA; ++i)
+    o.sa[i] = (uint32_t)min(m0 + scale_slot_row<FM>(tid + i * Cfg::kThreads), p.M - 1) * ks;
+#pragma unroll
+  for (int i = 0; i < Cfg::kWordsB; ++i)
+    o.sb[i] = (uint32_t)min(n0 + scale_slot_row<FN>(tid + i * Cfg::kThreads), p.N - 1) * ks;
 }
 
+// Issue the direct global->LDS copies of K chunk `kc` into `stage`.
 template <class Cfg>
-__device__ __forceinline__ void store_chunk(uint8_t* stage, const Prefetch<Cfg>& f) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void issue_chunk(const GemmArgs& p, const RowOffsets<Cfg>& o, int kc,
+                                            uint8_t* stage) {
+  const int wave_slot = (threadIdx.x >> 6) * 64;
 #pragma unroll
   for (int i = 0; i < Cfg::kPiecesA; ++i)
-    *reinterpret_cast<uint4*>(stage + (tid + i * Cfg::kThreads) * 16) = f.a[i];
+    __builtin_amdgcn_global_load_lds(p.a_codes + o.a[i] + kc * 32,
+                                     stage + (i * Cfg::kThreads + wave_slot) * 16, 16, 0, 0);
 #pragma unroll
   for (int i = 0; i < Cfg::kPiecesB; ++i)
-    *reinterpret_cast<uint4*>(stage + Cfg::kCodesA + (tid + i * Cfg::kThreads) * 16) = f.b[i];
+    __builtin_amdgcn_global_load_lds(p.w_codes + o.b[i] + kc * 32,
+                                     stage + Cfg::kCodesA + (i * Cfg::kThreads + wave_slot) * 16,
+                                     16, 0, 0);
 #pragma unroll
-  for (int i = 0; i < Cfg::kScaleWords; ++i)
-    *reinterpret_cast<uint32_t*>(stage + Cfg::kCodesA + Cfg::kCodesB +
-                                 (tid + i * Cfg::kThreads) * 4) = f.s[i];
+  for (int i = 0; i < Cfg::kWordsA; ++i)
+    __builtin_amdgcn_global_load_lds(p.a_scales + o.sa[i] + kc * 4,
+                                     stage + Cfg::kCodesA + Cfg::kCodesB +
+                                         (i * Cfg::kThreads + wave_slot) * 4,
+                                     4, 0, 0);
+#pragma unroll
+  for (int i = 0; i < Cfg::kWordsB; ++i)
+    __builtin_amdgcn_global_load_lds(p.w_scales + o.sb[i] + kc * 4,
+                                     stage + Cfg::kCodesA + Cfg::kCodesB + Cfg::kScalesA +
+                                         (i * Cfg::kThreads + wave_slot) * 4,
+                                     4, 0, 0);
 }
 
+// Tile order: hardware hands workgroup ids to the 8 XCDs round-robin, so id b runs on XCD b % 8.
+// Remap ids so each XCD walks a contiguous range of the logical order, and walk the logical order
+// in groups of kGroupM tile-rows (column-major inside a group): the tiles an XCD runs at the same
+// time then share a few A row-blocks and a few W row-blocks in that XCD's L2.
+constexpr int kGroupM = 8;
+
+__device__ __forceinline__ void tile_coords(uint32_t bid, uint32_t tiles_m, uint32_t tiles_n,
+                                            uint32_t& tm, uint32_t& tn) {
+  const uint32_t ntiles = tiles_m * tiles_n;
+  uint32_t t = bid;
+  if (ntiles % 8u == 0u) t = (bid % 8u) * (ntiles / 8u) + bid / 8u;
+  const uint32_t per_group = kGroupM * tiles_n;
+  const uint32_t group = t / per_group;
+  const uint32_t first_m = group * kGroupM;
+  const uint32_t gsize = min(tiles_m - first_m, (uint32_t)kGroupM);
+  const uint32_t in_group = t - group * per_group;
+  tm = first_m + in_group % gsize;
+  tn = in_group / gsize;
+}
+
+// One K chunk of a wavefront's fragments, read from LDS: FM + FN code words of 16 bytes (32
+// codes) and one 16-byte scale group per operand.
+template <int FM, int FN>
+struct Frags {
+  uint4 qa[FM];
+  uint4 qb[FN];
+  uint4 sa;
+  uint4 sb;
+};
+
+template <int FM, int FN>
+__device__ __forceinline__ void read_frags(const uint8_t* stage, int a_frag, int b_frag, int a_scl,
+                                           int b_scl, Frags<FM, FN>& f) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i) f.qa[i] = *reinterpret_cast<const uint4*>(stage + a_frag + i * 1024);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) f.qb[j] = *reinterpret_cast<const uint4*>(stage + b_frag + j * 1024);
+  f.sa = *reinterpret_cast<const uint4*>(stage + a_scl);
+  f.sb = *reinterpret_cast<const uint4*>(stage + b_scl);
+}
+
+template <int STEP>
+__device__ __forceinline__ uint32_t word(const uint4& q) {
+  return STEP == 0 ? q.x : STEP == 1 ? q.y : STEP == 2 ? q.z : q.w;
+}
+
+template <int STEP, int FM, int FN>
+__device__ __forceinline__ void decode_step(const Frags<FM, FN>& f, const half2_t (&sa)[FM],
+                                            const half2_t (&sb)[FN], half8_t (&av)[FM],
+                                            half8_t (&bv)[FN]) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i) av[i] = decode8(word<STEP>(f.qa[i]), STEP < 2 ? sa[i][0] : sa[i][1]);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) bv[j] = decode8(word<STEP>(f.qb[j]), STEP < 2 ? sb[j][0] : sb[j][1]);
+}
+
+template <int FM, int FN>
+__device__ __forceinline__ void mfma_step(const half8_t (&av)[FM], const half8_t (&bv)[FN],
+                                          floatx16 (&acc)[FM][FN]) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+}
+
+// Interleave the FM*FN MFMAs of one step with the VALU work of decoding the next step: one MFMA,
+// then a few VALU instructions, so the matrix core stays busy while the decode runs beside it.
+template <int FM, int FN>
+__device__ __forceinline__ void interleave_mfma_valu() {
+  constexpr int kValuPerMfma = (8 * (FM + FN)) / (FM * FN) + 1;
+#pragma unroll
+  for (int k = 0; k < FM * FN; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
+  }
+}
+
+// Decode one K chunk's fragments and issue its 4 x FM x FN MFMAs; the decode of K step s+1 is
+// software-pipelined under the MFMAs of step s.  Lane half h uses scale bytes 2h and 2h+1 of each
+// fragment's 4-byte scale word.
+template <int FM, int FN>
+__device__ __forceinline__ void compute_chunk(const Frags<FM, FN>& f, int h,
+                                              floatx16 (&acc)[FM][FN]) {
+  half2_t sa[FM], sb[FN];
+  const uint32_t sh = 16u * (uint32_t)h;
+  const uint32_t swa[4] = {f.sa.x, f.sa.y, f.sa.z, f.sa.w};
+  const uint32_t swb[4] = {f.sb.x, f.sb.y, f.sb.z, f.sb.w};
+#pragma unroll
+  for (int i = 0; i < FM; ++i) sa[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(swa[i] >> sh, 1.0f, false);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) sb[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(swb[j] >> sh, 1.0f, false);
+  half8_t a0[FM], b0[FN], a1[FM], b1[FN];
+  decode_step<0>(f, sa, sb, a0, b0);
+  mfma_step(a0, b0, acc);
+  decode_step<1>(f, sa, sb, a1, b1);
+  interleave_mfma_valu<FM, FN>();
+  mfma_step(a1, b1, acc);
+  decode_step<2>(f, sa, sb, a0, b0);
+  interleave_mfma_valu<FM, FN>();
+  mfma_step(a0, b0, acc);
+  decode_step<3>(f, sa, sb, a1, b1);
+  interleave_mfma_valu<FM, FN>();
+  mfma_step(a1, b1, acc);
+}
+
+// Main kernel.  Two LDS stages filled by direct global->LDS copies.  At K chunk kc every wavefront
+// waits for its own copies of chunk kc, meets the others at a barrier (after which chunk kc is
+// complete in LDS and every wavefront has finished with chunk kc-1), reads its fragments of chunk
+// kc into registers, then issues the copies of chunk kc+1 into the stage chunk kc-1 occupied and
+// computes chunk kc from registers while they fly.  The K loop is unrolled by 2 so each stage is
+// named statically.
 template <int WAVES_M, int WAVES_N, int FM, int FN>
-__global__ void __launch_bounds__(WAVES_M * WAVES_N * 64)
-gemm_tiled_kernel(GemmArgs p, uint32_t tiles_n) {
+__global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1)
+gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
   using Cfg = TileCfg<WAVES_M, WAVES_N, FM, FN>;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ __attribute__((aligned(16))) uint8_t s0[Cfg::kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s1[Cfg::kStage];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -158,10 +292,14 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_n) {
   const int wn = wave % WAVES_N;
   const int h = lane >> 5;
   const int r = lane & 31;
-  const uint32_t tile = blockIdx.x;
-  const int m0 = (int)(tile / tiles_n) * Cfg::BM;
-  const int n0 = (int)(tile % tiles_n) * Cfg::BN;
+  uint32_t tmi, tni;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tmi, tni);
+  const int m0 = (int)tmi * Cfg::BM;
+  const int n0 = (int)tni * Cfg::BN;
   const int nchunks = p.K / 64;
+
+  RowOffsets<Cfg> ro;
+  row_offsets<Cfg, FM, FN>(p, m0, n0, ro);
 
   floatx16 acc[FM][FN];
 #pragma unroll
@@ -169,56 +307,46 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_n) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = floatx16{};
 
-  Prefetch<Cfg> f;
-  load_chunk<Cfg>(p, m0, n0, 0, f);
-  store_chunk<Cfg>(lds, f);
-  __syncthreads();
+  // LDS read offsets of this lane's fragments and scale groups (within a stage)
+  const int a_frag = (wm * FM) * 1024 + lane * 16;
+  const int b_frag = Cfg::kCodesA + (wn * FN) * 1024 + lane * 16;
+  const int a_scl = Cfg::kCodesA + Cfg::kCodesB + (wm * 32 + r) * FM * 4;
+  const int b_scl = Cfg::kCodesA + Cfg::kCodesB + Cfg::kScalesA + (wn * 32 + r) * FN * 4;
 
-  for (int kc = 0; kc < nchunks; ++kc) {
-    uint8_t* stage = lds + (kc & 1) * Cfg::kStage;
-    if (kc + 1 < nchunks) load_chunk<Cfg>(p, m0, n0, kc + 1, f);
+  issue_chunk<Cfg>(p, ro, 0, s0);
+  Frags<FM, FN> f;
+  int kc = 0;
+  for (; kc + 1 < nchunks; kc += 2) {
+    // the scheduling fences keep all of the previous chunk's MFMAs ahead of the wait
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): this wavefront's copies of chunk kc
+    __builtin_amdgcn_s_barrier();
+    read_frags(s0, a_frag, b_frag, a_scl, b_scl, f);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_chunk<Cfg>(p, ro, kc + 1, s1);
+    compute_chunk(f, h, acc);
 
-    uint4 qa[FM], qb[FN];
-    uint32_t sa[FM], sb[FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int g = wm * FM + i;
-      qa[i] = *reinterpret_cast<const uint4*>(stage + g * 1024 + lane * 16);
-      sa[i] = *reinterpret_cast<const uint16_t*>(stage + Cfg::kCodesA + Cfg::kCodesB +
-                                                 (g * 32 + r) * 4 + h * 2);
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int g = wn * FN + j;
-      qb[j] = *reinterpret_cast<const uint4*>(stage + Cfg::kCodesA + g * 1024 + lane * 16);
-      sb[j] = *reinterpret_cast<const uint16_t*>(stage + Cfg::kCodesA + Cfg::kCodesB +
-                                                 Cfg::kScalesA + (g * 32 + r) * 4 + h * 2);
-    }
-#pragma unroll
-    for (int step = 0; step < 4; ++step) {
-      half8_t av[FM], bv[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const uint32_t q = step == 0 ? qa[i].x : step == 1 ? qa[i].y : step == 2 ? qa[i].z : qa[i].w;
-        av[i] = decode8(q, e4m3_to_half(step < 2 ? (sa[i] & 0xFFu) : (sa[i] >> 8)));
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const uint32_t q = step == 0 ? qb[j].x : step == 1 ? qb[j].y : step == 2 ? qb[j].z : qb[j].w;
-        bv[j] = decode8(q, e4m3_to_half(step < 2 ? (sb[j] & 0xFFu) : (sb[j] >> 8)));
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
-    }
-
-    if (kc + 1 < nchunks) store_chunk<Cfg>(lds + ((kc + 1) & 1) * Cfg::kStage, f);
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x3F70);
+    __builtin_amdgcn_s_barrier();
+    read_frags(s1, a_frag, b_frag, a_scl, b_scl, f);
+    __builtin_amdgcn_sched_barrier(0);
+    // past the last chunk the copy is clamped to it (redundant, never read): no branch in the loop
+    issue_chunk<Cfg>(p, ro, min(kc + 2, nchunks - 1), s0);
+    compute_chunk(f, h, acc);
   }
+  if (kc < nchunks) {  // odd number of chunks: the last one is in s0
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x3F70);
+    __builtin_amdgcn_s_barrier();
+    read_frags(s0, a_frag, b_frag, a_scl, b_scl, f);
+    compute_chunk(f, h, acc);
+  }
+  // no copy may still be writing LDS when the workgroup ends
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0x3F70);
 
-  // epilogue: lane holds column n = tile col + r of each FN fragment, rows 8*(i/4) + 4h + i%4
+  // epilogue: lane holds column n = tile col + r of each FN fragment, rows 8*(e/4) + 4h + e%4
   const float ga = *p.a_g;
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
@@ -237,14 +365,18 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_n) {
   }
 }
 
+#ifndef NVFP4_TILED_CFG
+#define NVFP4_TILED_CFG 2, 2, 4, 4
+#endif
+
 template <int WAVES_M, int WAVES_N, int FM, int FN>
 hipError_t launch_tiled_cfg(const GemmArgs& a, hipStream_t stream) {
   using Cfg = TileCfg<WAVES_M, WAVES_N, FM, FN>;
   const uint32_t tiles_m = (a.M + Cfg::BM - 1) / Cfg::BM;
   const uint32_t tiles_n = (a.N + Cfg::BN - 1) / Cfg::BN;
   auto kern = gemm_tiled_kernel<WAVES_M, WAVES_N, FM, FN>;
-  hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(Cfg::kThreads), 2 * Cfg::kStage, stream,
-                     a, tiles_n);
+  hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(Cfg::kThreads), 0, stream, a, tiles_m,
+                     tiles_n);
   return hipGetLastError();
 }
 
@@ -259,7 +391,7 @@ hipError_t launch_gemm_general(const GemmArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
-  return launch_tiled_cfg<2, 2, 2, 2>(a, stream);
+  return launch_tiled_cfg<NVFP4_TILED_CFG>(a, stream);
 }
 
 hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
@@ -267,9 +399,10 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
 }
 
 GemmPath choose_gemm_path(int64_t M, int64_t K) {
-  if (K % 64 != 0) return GemmPath::General;
+  // the tiled kernel needs whole K chunks of 64 (the host layer keeps every operand below 2 GiB,
+  // so 32-bit row offsets suffice)
   (void)M;
-  return GemmPath::Tiled;
+  return K % 64 == 0 ? GemmPath::Tiled : GemmPath::General;
 }
 
 }  // namespace nvfp4

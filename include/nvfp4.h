@@ -102,7 +102,8 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, in
  *   a_gscale            device, one float: gA.
  *   w_codes, w_scales   device, weights [N, K] (nn.Linear layout) encoded along K.
  *   w_gscale            device, one float: gW.
- *   M, N, K             M, N >= 0; K > 0 and a multiple of 16; K < 2^24.
+ *   M, N, K             M, N >= 0; K > 0 and a multiple of 16; K < 2^24; each operand's codes
+ *                       below 2 GiB (M*K/2 and N*K/2 < 2^31).
  *   c                   device, [M, N] with row pitch ldc >= N, dtype c_dtype (F32 or BF16); the
  *                       product is rounded once from FP32 to BF16 when c_dtype is BF16.
  *   Alignment: every code/scale pointer 16-byte aligned and c 16-byte aligned.  K a multiple of 64

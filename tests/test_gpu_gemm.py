@@ -159,7 +159,7 @@ def _sampled_full_size(wid, M=None):
     torch.cuda.synchronize()
 
     rng = np.random.Generator(np.random.PCG64(100 + wid))
-    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 30, replace=False)]))
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(30, M), replace=False)]))
     cols = [0, w.N - 1]
     for j in range(len(segs) - 1):
         cols += [segs[j], segs[j + 1] - 1]
