@@ -245,40 +245,71 @@ __device__ __forceinline__ void interleave_mfma_valu() {
   }
 }
 
-// Decode one K chunk's fragments and issue its 4 x FM x FN MFMAs; the decode of K step s+1 is
-// software-pipelined under the MFMAs of step s.  Lane half h uses scale bytes 2h and 2h+1 of each
-// fragment's 4-byte scale word.
 template <int FM, int FN>
-__device__ __forceinline__ void compute_chunk(const Frags<FM, FN>& f, int h,
-                                              floatx16 (&acc)[FM][FN]) {
-  half2_t sa[FM], sb[FN];
-  const uint32_t sh = 16u * (uint32_t)h;
+__device__ __forceinline__ void decode_scales(const Frags<FM, FN>& f, uint32_t sh,
+                                              half2_t (&sa)[FM], half2_t (&sb)[FN]) {
   const uint32_t swa[4] = {f.sa.x, f.sa.y, f.sa.z, f.sa.w};
   const uint32_t swb[4] = {f.sb.x, f.sb.y, f.sb.z, f.sb.w};
 #pragma unroll
-  for (int i = 0; i < FM; ++i) sa[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(swa[i] >> sh, 1.0f, false);
+  for (int i = 0; i < FM; ++i)
+    sa[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(swa[i] >> sh, 1.0f, false);
 #pragma unroll
-  for (int j = 0; j < FN; ++j) sb[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(swb[j] >> sh, 1.0f, false);
-  half8_t a0[FM], b0[FN], a1[FM], b1[FN];
-  decode_step<0>(f, sa, sb, a0, b0);
-  mfma_step(a0, b0, acc);
-  decode_step<1>(f, sa, sb, a1, b1);
-  interleave_mfma_valu<FM, FN>();
-  mfma_step(a1, b1, acc);
-  decode_step<2>(f, sa, sb, a0, b0);
-  interleave_mfma_valu<FM, FN>();
-  mfma_step(a0, b0, acc);
-  decode_step<3>(f, sa, sb, a1, b1);
-  interleave_mfma_valu<FM, FN>();
-  mfma_step(a1, b1, acc);
+  for (int j = 0; j < FN; ++j)
+    sb[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(swb[j] >> sh, 1.0f, false);
 }
 
-// Main kernel.  Two LDS stages filled by direct global->LDS copies.  At K chunk kc every wavefront
-// waits for its own copies of chunk kc, meets the others at a barrier (after which chunk kc is
-// complete in LDS and every wavefront has finished with chunk kc-1), reads its fragments of chunk
-// kc into registers, then issues the copies of chunk kc+1 into the stage chunk kc-1 occupied and
-// computes chunk kc from registers while they fly.  The K loop is unrolled by 2 so each stage is
-// named statically.
+// Wait until this wavefront's copies of the chunk in `stage` have landed, meet the other
+// wavefronts (after which the chunk is complete in LDS and every wavefront has read its fragments
+// of the chunk before it), and read this lane's fragments.  The scheduling fences keep the work
+// issued before this point ahead of the wait.
+template <int FM, int FN>
+__device__ __forceinline__ void sync_and_read(const uint8_t* stage, int a_frag, int b_frag,
+                                              int a_scl, int b_scl, Frags<FM, FN>& f) {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  read_frags(stage, a_frag, b_frag, a_scl, b_scl, f);
+}
+
+// One K chunk, software-pipelined with the next: the MFMAs of steps 0-1 of chunk kc run under the
+// decode of steps 1-2; then the next chunk's fragments are read (sync_and_read) and its copy of
+// chunk kc+2 issued (`next`); the MFMAs of step 2 run under the decode of step 3 while those LDS
+// reads complete, and the MFMAs of step 3 run under the decode of the next chunk's step 0.  On
+// entry `cur` holds chunk kc's fragments and a0/b0 its decoded step 0; on exit `nxt` holds chunk
+// kc+1's fragments and a0/b0 its decoded step 0.
+template <int FM, int FN, class Next>
+__device__ __forceinline__ void pipelined_chunk(const Frags<FM, FN>& cur, Frags<FM, FN>& nxt,
+                                                half2_t (&sa)[FM], half2_t (&sb)[FN],
+                                                half8_t (&a0)[FM], half8_t (&b0)[FN],
+                                                half8_t (&a1)[FM], half8_t (&b1)[FN], uint32_t sh,
+                                                floatx16 (&acc)[FM][FN], Next&& next) {
+  mfma_step(a0, b0, acc);
+  decode_step<1>(cur, sa, sb, a1, b1);
+  interleave_mfma_valu<FM, FN>();
+  mfma_step(a1, b1, acc);
+  decode_step<2>(cur, sa, sb, a0, b0);
+  interleave_mfma_valu<FM, FN>();
+  next(nxt);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_step(a0, b0, acc);
+  decode_step<3>(cur, sa, sb, a1, b1);
+  interleave_mfma_valu<FM, FN>();
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_step(a1, b1, acc);
+  decode_scales(nxt, sh, sa, sb);
+  decode_step<0>(nxt, sa, sb, a0, b0);
+  interleave_mfma_valu<FM, FN>();
+}
+
+// Main kernel.  Two LDS stages filled by direct global->LDS copies, two register sets of
+// fragments.  In the middle of K chunk kc (after its second MFMA step) every wavefront waits for its
+// own copies of chunk kc+1, meets the others at a barrier (chunk kc+1 is then complete in LDS and
+// every wavefront has read chunk kc, whose stage is free), reads its fragments of chunk kc+1, and
+// issues the copies of chunk kc+2 into chunk kc's stage.  The remaining MFMA steps of chunk kc
+// then cover the LDS reads and the decode of chunk kc+1's first step, so the matrix core does not
+// idle across chunks.
+// The K loop is unrolled by 2 so each stage and register set is named statically; past the last
+// chunk, reads and copies are clamped to it (redundant, never used), keeping the loop branch-free.
 template <int WAVES_M, int WAVES_N, int FM, int FN>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1)
 gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
@@ -292,11 +323,13 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
   const int wn = wave % WAVES_N;
   const int h = lane >> 5;
   const int r = lane & 31;
+  const uint32_t sh = 16u * (uint32_t)h;  // lane half h uses scale bytes 2h, 2h+1
   uint32_t tmi, tni;
   tile_coords(blockIdx.x, tiles_m, tiles_n, tmi, tni);
   const int m0 = (int)tmi * Cfg::BM;
   const int n0 = (int)tni * Cfg::BN;
   const int nchunks = p.K / 64;
+  const int last = nchunks - 1;
 
   RowOffsets<Cfg> ro;
   row_offsets<Cfg, FM, FN>(p, m0, n0, ro);
@@ -313,35 +346,32 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
   const int a_scl = Cfg::kCodesA + Cfg::kCodesB + (wm * 32 + r) * FM * 4;
   const int b_scl = Cfg::kCodesA + Cfg::kCodesB + Cfg::kScalesA + (wn * 32 + r) * FN * 4;
 
+  Frags<FM, FN> f0, f1;
+  half2_t sa[FM], sb[FN];
+  half8_t a0[FM], b0[FN], a1[FM], b1[FN];
+
+  // prologue: chunk 0 into s0 and registers, chunk 1 in flight into s1
   issue_chunk<Cfg>(p, ro, 0, s0);
-  Frags<FM, FN> f;
+  sync_and_read(s0, a_frag, b_frag, a_scl, b_scl, f0);
+  issue_chunk<Cfg>(p, ro, min(1, last), s1);
+  decode_scales(f0, sh, sa, sb);
+  decode_step<0>(f0, sa, sb, a0, b0);
+
   int kc = 0;
   for (; kc + 1 < nchunks; kc += 2) {
-    // the scheduling fences keep all of the previous chunk's MFMAs ahead of the wait
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): this wavefront's copies of chunk kc
-    __builtin_amdgcn_s_barrier();
-    read_frags(s0, a_frag, b_frag, a_scl, b_scl, f);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_chunk<Cfg>(p, ro, kc + 1, s1);
-    compute_chunk(f, h, acc);
-
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0x3F70);
-    __builtin_amdgcn_s_barrier();
-    read_frags(s1, a_frag, b_frag, a_scl, b_scl, f);
-    __builtin_amdgcn_sched_barrier(0);
-    // past the last chunk the copy is clamped to it (redundant, never read): no branch in the loop
-    issue_chunk<Cfg>(p, ro, min(kc + 2, nchunks - 1), s0);
-    compute_chunk(f, h, acc);
+    // chunk kc (in f0; stage s0), chunk kc+1 in flight into s1
+    pipelined_chunk(f0, f1, sa, sb, a0, b0, a1, b1, sh, acc, [&](Frags<FM, FN>& n) {
+      sync_and_read(s1, a_frag, b_frag, a_scl, b_scl, n);
+      issue_chunk<Cfg>(p, ro, min(kc + 2, last), s0);
+    });
+    // chunk kc+1 (in f1; stage s1), chunk kc+2 in flight into s0
+    pipelined_chunk(f1, f0, sa, sb, a0, b0, a1, b1, sh, acc, [&](Frags<FM, FN>& n) {
+      sync_and_read(s0, a_frag, b_frag, a_scl, b_scl, n);
+      issue_chunk<Cfg>(p, ro, min(kc + 3, last), s1);
+    });
   }
-  if (kc < nchunks) {  // odd number of chunks: the last one is in s0
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0x3F70);
-    __builtin_amdgcn_s_barrier();
-    read_frags(s0, a_frag, b_frag, a_scl, b_scl, f);
-    compute_chunk(f, h, acc);
-  }
+  if (kc < nchunks)  // odd number of chunks: the last one is in f0
+    pipelined_chunk(f0, f1, sa, sb, a0, b0, a1, b1, sh, acc, [&](Frags<FM, FN>& n) {});
   // no copy may still be writing LDS when the workgroup ends
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(0x3F70);
