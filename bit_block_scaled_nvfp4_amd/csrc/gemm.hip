@@ -424,14 +424,11 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
   return launch_tiled_cfg<NVFP4_TILED_CFG>(a, stream);
 }
 
-hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
-  return launch_gemm_general(a, stream);
-}
-
 GemmPath choose_gemm_path(int64_t M, int64_t K) {
-  // the tiled kernel needs whole K chunks of 64 (the host layer keeps every operand below 2 GiB,
-  // so 32-bit row offsets suffice)
-  (void)M;
+  // decode shapes (at most 16 activation rows) stream the weights with the skinny kernel; the
+  // tiled kernel needs whole K chunks of 64 (the host layer keeps every operand below 2 GiB, so
+  // 32-bit row offsets suffice)
+  if (M <= 16 && K % 128 == 0) return GemmPath::Skinny;
   return K % 64 == 0 ? GemmPath::Tiled : GemmPath::General;
 }
 

@@ -60,6 +60,8 @@ def test_workload1_full():
 @pytest.mark.parametrize("M,N,K", [
     (1, 1, 16), (1, 37, 64), (5, 70, 48), (33, 65, 80), (31, 129, 128), (64, 64, 64),
     (129, 130, 192), (200, 300, 1024), (257, 255, 320), (96, 160, 5120),
+    # decode-shaped (M <= 16, K a multiple of 128): the skinny kernel, ragged N and short K runs
+    (1, 100, 128), (3, 77, 256), (16, 40, 1024), (7, 33, 384), (16, 16, 2048), (2, 300, 17408),
 ])
 def test_ragged_shapes(M, N, K):
     a = random_matrix(M * 7 + K, M, K, outlier_cols=max(1, K // 100))
