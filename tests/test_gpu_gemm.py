@@ -60,8 +60,10 @@ def test_workload1_full():
 @pytest.mark.parametrize("M,N,K", [
     (1, 1, 16), (1, 37, 64), (5, 70, 48), (33, 65, 80), (31, 129, 128), (64, 64, 64),
     (129, 130, 192), (200, 300, 1024), (257, 255, 320), (96, 160, 5120),
-    # decode-shaped (M <= 16, K a multiple of 128): the skinny kernel, ragged N and short K runs
-    (1, 100, 128), (3, 77, 256), (16, 40, 1024), (7, 33, 384), (16, 16, 2048), (2, 300, 17408),
+    # decode-shaped (M <= 16): the skinny kernel for K a multiple of 512 up to 16384 (ragged N,
+    # K runs shorter than the 8 wavefronts), the tiled kernel otherwise
+    (1, 100, 512), (3, 77, 1536), (16, 40, 1024), (7, 33, 512), (16, 16, 2048), (5, 3, 16384),
+    (2, 300, 17408), (1, 19, 384),
 ])
 def test_ragged_shapes(M, N, K):
     a = random_matrix(M * 7 + K, M, K, outlier_cols=max(1, K // 100))
