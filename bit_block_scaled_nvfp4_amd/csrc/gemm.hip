@@ -428,7 +428,7 @@ GemmPath choose_gemm_path(int64_t M, int64_t K) {
   // decode shapes (at most 16 activation rows) stream the weights with the skinny kernel; the
   // tiled kernel needs whole K chunks of 64 (the host layer keeps every operand below 2 GiB, so
   // 32-bit row offsets suffice)
-  if (M <= 16 && K % 512 == 0 && K <= kSkinnyMaxK) return GemmPath::Skinny;
+  if (M <= 16 && K % 1024 == 0 && K <= kSkinnyMaxK) return GemmPath::Skinny;
   return K % 64 == 0 ? GemmPath::Tiled : GemmPath::General;
 }
 

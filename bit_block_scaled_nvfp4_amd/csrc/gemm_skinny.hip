@@ -31,102 +31,161 @@ namespace {
 
 constexpr int kSkinnyWaves = 8;
 constexpr int kSkinnyThreads = kSkinnyWaves * 64;
-constexpr int kSkinnyMaxChunks = (int)(kSkinnyMaxK / 128 / kSkinnyWaves);  // per wavefront
+constexpr int kPhaseK = 1024;                    // K elements per phase (8 chunks of 128)
+constexpr int kPhasePieces = kPhaseK / 32;       // 16-byte code pieces per row per phase (32)
+constexpr int kPhaseCodes = 16 * kPhasePieces;   // code slots per phase (512 = one per thread)
+constexpr int kPhaseScaleBytes = kPhaseK / 16;   // scale bytes per row per phase (64)
+constexpr int kPhaseBytes = kPhaseCodes * 16;   // 8 KiB of codes per phase
+constexpr int kVmemPerPhase = 2;  // per wavefront: weight-code copy, activation-code load
 
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ uint32_t load_u16_global(const uint8_t* p) {
-  return *reinterpret_cast<const uint16_t*>(p);
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
 }
 
+// Issue phase P's copy (weight codes of the 16 rows into `buf`) and this lane's activation-code
+// load for its chunk of the phase.  Every wavefront issues exactly kVmemPerPhase vector memory
+// instructions per phase, so the wait for phase P is a compile-time vmcnt.
+template <int P>
+__device__ __forceinline__ void issue_phase(const GemmArgs& p, int n0, int wave, int lane, int r,
+                                            int g, uint8_t* buf, uint4& aw) {
+  const int kb = p.K / 2;
+  // codes: slot t = wave * 64 + lane holds row t / 32, phase piece (t % 32) ^ row within 16s
+  {
+    const int t = wave * 64 + lane;
+    const int row = t / kPhasePieces;
+    const int jl = t - row * kPhasePieces;
+    const int j = (jl & ~15) | ((jl ^ row) & 15);
+    const int grow = min(n0 + row, p.N - 1);
+    __builtin_amdgcn_global_load_lds(p.w_codes + (int64_t)grow * kb + P * (kPhaseK / 2) + j * 16,
+                                     buf + wave * 64 * 16, 16, 0, 0);
+  }
+  // this lane's activation fragment for chunk `wave` of the phase; rows >= M load the last row
+  // (unconditionally, so no register merge forces an early wait) and are zeroed at use
+  {
+    const int c = P * (kPhaseK / 128) + wave;
+    const int arow = min(r, p.M - 1);
+    aw = *reinterpret_cast<const uint4*>(p.a_codes + (int64_t)arow * kb + c * 64 + g * 16);
+  }
+  // keep the phases' memory instructions in phase order (the waits count on it)
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Contract this wavefront's chunk of phase data in `buf` (chunk `wave` of the phase).
+__device__ __forceinline__ void compute_phase(const uint8_t* buf, const uint8_t* wsc,
+                                              const uint8_t* asc, int ks, int c, int wave, int r,
+                                              int g, bool arow_valid, const uint4& aw_in,
+                                              floatx4_t& acc) {
+  const uint32_t keep = arow_valid ? 0xFFFFFFFFu : 0u;  // padded rows contribute zeros
+  const uint4 aw = {aw_in.x & keep, aw_in.y & keep, aw_in.z & keep, aw_in.w & keep};
+  const uint32_t as2 = *reinterpret_cast<const uint16_t*>(asc + r * ks + c * 8 + g * 2) & keep;
+  const int j = wave * 4 + g;
+  const uint4 ww = *reinterpret_cast<const uint4*>(
+      buf + (r * kPhasePieces + ((j & ~15) | ((j ^ r) & 15))) * 16);
+  const uint32_t ws2 = *reinterpret_cast<const uint16_t*>(wsc + r * ks + c * 8 + g * 2);
+  const half2_t sw = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ws2, 1.0f, false);
+  const half2_t sa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(as2, 1.0f, false);
+  const uint32_t wq[4] = {ww.x, ww.y, ww.z, ww.w};
+  const uint32_t aq[4] = {aw.x, aw.y, aw.z, aw.w};
+#pragma unroll
+  for (int s2 = 0; s2 < 4; ++s2) {
+    const half8_t bv = decode8(wq[s2], s2 < 2 ? sw[0] : sw[1]);
+    const half8_t av = decode8(aq[s2], s2 < 2 ? sa[0] : sa[1]);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc, 0, 0, 0);
+  }
+}
+
+// K = NPH * 1024.  Every phase has its own statically named LDS buffer, and all copies are issued
+// before any phase is computed: the compiler sees which buffer each read depends on, so phase P is
+// computed as soon as its own copies (and activation loads) have landed while later phases are
+// still streaming in.
+template <int NPH>
 __global__ void __launch_bounds__(kSkinnyThreads)
 gemm_skinny_kernel(GemmArgs p) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ floatx4_t partial[kSkinnyWaves][64];
+  // block scales of the 16 weight rows and of up to 16 activation rows, [16][K/16] each (sized
+  // for the largest K: a template-dependent size here is miscompiled by the host pass)
+  __shared__ __attribute__((aligned(16))) uint8_t wsc[16 * (kSkinnyMaxK / 16)];
+  __shared__ __attribute__((aligned(16))) uint8_t asc[16 * (kSkinnyMaxK / 16)];
+  __shared__ __attribute__((aligned(16))) uint8_t b0[kPhaseBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t b1[NPH > 1 ? kPhaseBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t b2[NPH > 2 ? kPhaseBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t b3[NPH > 3 ? kPhaseBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t b4[NPH > 4 ? kPhaseBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t b5[NPH > 5 ? kPhaseBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t b6[NPH > 6 ? kPhaseBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t b7[NPH > 7 ? kPhaseBytes : 16];
+  uint8_t* const bufs[8] = {b0, b1, b2, b3, b4, b5, b6, b7};
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane & 15;  // weight row (output column) and activation row of this lane
   const int g = lane >> 4;  // k group
   const int n0 = blockIdx.x * 16;
-  const int kb = p.K / 2, ks = p.K / 16;
-  const int P = p.K / 32;                  // 16-byte code pieces per row
-  const int code_slots = 16 * P;
-  const int scale_slots = 16 * (ks / 16);  // 16-byte scale pieces of the 16 rows
-  uint8_t* const lds_codes = lds;
-  uint8_t* const lds_scales = lds + code_slots * 16;
+  const bool arow_valid = r < p.M;
 
-  // 1. coalesced copy of the 16 weight rows into LDS (rows past N are clamped to the last row)
-  for (int s0 = wave * 64; s0 < code_slots; s0 += kSkinnyThreads) {
-    const int s = s0 + lane;
-    if (s < code_slots) {
-      const int row = s / P;
-      const int jl = s - row * P;
-      const int j = (jl & ~15) | ((jl ^ row) & 15);
-      const int grow = min(n0 + row, p.N - 1);
-      __builtin_amdgcn_global_load_lds(p.w_codes + (int64_t)grow * kb + j * 16,
-                                       lds_codes + s0 * 16, 16, 0, 0);
-    }
-  }
-  for (int s0 = wave * 64; s0 < scale_slots; s0 += kSkinnyThreads) {
-    const int s = s0 + lane;
-    if (s < scale_slots) {
-      const int per_row = ks / 16;
+  // all block scales of the 16 weight rows and of the M activation rows, copied once (coalesced:
+  // 16-byte pieces of consecutive rows); older than every phase's instructions, so each phase's
+  // wait covers them
+  {
+    const int ks = p.K / 16, per_row = ks / 16;
+    const int s = threadIdx.x;
+    if (s < 16 * per_row) {
       const int row = s / per_row;
       const int grow = min(n0 + row, p.N - 1);
       __builtin_amdgcn_global_load_lds(p.w_scales + (int64_t)grow * ks + (s - row * per_row) * 16,
-                                       lds_scales + s0 * 16, 16, 0, 0);
+                                       wsc + (s & ~63) * 16, 16, 0, 0);
+    }
+    if (s < p.M * per_row) {
+      const int row = s / per_row;
+      __builtin_amdgcn_global_load_lds(p.a_scales + (int64_t)row * ks + (s - row * per_row) * 16,
+                                       asc + (s & ~63) * 16, 16, 0, 0);
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
 
-  // 2. this wavefront's share of K; its activation fragments (rows >= M are zero) are loaded now,
-  //    so their latency overlaps the weight copies
-  const int nchunks = p.K / 128;
-  const int per_wave = (nchunks + kSkinnyWaves - 1) / kSkinnyWaves;
-  const int c_begin = min(wave * per_wave, nchunks);
-  const int count = min(c_begin + per_wave, nchunks) - c_begin;
-  const bool arow_valid = r < p.M;
-  const uint8_t* ac = p.a_codes + (int64_t)min(r, p.M - 1) * kb + g * 16 + c_begin * 64;
-  const uint8_t* asc = p.a_scales + (int64_t)min(r, p.M - 1) * ks + g * 2 + c_begin * 8;
-  uint4 aw[kSkinnyMaxChunks];
-  uint32_t as2[kSkinnyMaxChunks];
+  uint4 aw[8];  // entries >= NPH are never touched
 #pragma unroll
-  for (int i = 0; i < kSkinnyMaxChunks; ++i) {
-    aw[i] = uint4{0u, 0u, 0u, 0u};
-    as2[i] = 0u;
-    if (i < count && arow_valid) {
-      aw[i] = *reinterpret_cast<const uint4*>(ac + i * 64);
-      as2[i] = load_u16_global(asc + i * 8);
+  for (int q = 0; q < NPH; ++q) {
+    const int ph = q;
+    switch (ph) {  // compile-time after unrolling
+      case 0: issue_phase<0>(p, n0, wave, lane, r, g, bufs[0], aw[0]); break;
+      case 1: issue_phase<1>(p, n0, wave, lane, r, g, bufs[1], aw[1]); break;
+      case 2: issue_phase<2>(p, n0, wave, lane, r, g, bufs[2], aw[2]); break;
+      case 3: issue_phase<3>(p, n0, wave, lane, r, g, bufs[3], aw[3]); break;
+      case 4: issue_phase<4>(p, n0, wave, lane, r, g, bufs[4], aw[4]); break;
+      case 5: issue_phase<5>(p, n0, wave, lane, r, g, bufs[5], aw[5]); break;
+      case 6: issue_phase<6>(p, n0, wave, lane, r, g, bufs[6], aw[6]); break;
+      default: issue_phase<7>(p, n0, wave, lane, r, g, bufs[7], aw[7]); break;
     }
   }
-
-  __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): this wavefront's copies and loads have landed
-  __syncthreads();                      // ... and every other wavefront's copies
 
   floatx4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int i = 0; i < kSkinnyMaxChunks; ++i) {
-    if (i < count) {
-      const int c = c_begin + i;
-      const int j = c * 4 + g;
-      const uint4 ww = *reinterpret_cast<const uint4*>(
-          lds_codes + (r * P + ((j & ~15) | ((j ^ r) & 15))) * 16);
-      const uint32_t ws2 =
-          *reinterpret_cast<const uint16_t*>(lds_scales + r * ks + c * 8 + g * 2);
-      const half2_t sw = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ws2, 1.0f, false);
-      const half2_t sa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(as2[i], 1.0f, false);
-      const uint32_t wq[4] = {ww.x, ww.y, ww.z, ww.w};
-      const uint32_t aq[4] = {aw[i].x, aw[i].y, aw[i].z, aw[i].w};
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
-        const half8_t bv = decode8(wq[s2], s2 < 2 ? sw[0] : sw[1]);
-        const half8_t av = decode8(aq[s2], s2 < 2 ? sa[0] : sa[1]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc, 0, 0, 0);
-      }
+  for (int q = 0; q < NPH; ++q) {
+    const int ph = q;
+    // phase ph has landed once only the later phases' instructions are outstanding
+    __builtin_amdgcn_sched_barrier(0);
+    switch (NPH - 1 - q) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<1 * kVmemPerPhase>(); break;
+      case 2: wait_vmcnt<2 * kVmemPerPhase>(); break;
+      case 3: wait_vmcnt<3 * kVmemPerPhase>(); break;
+      case 4: wait_vmcnt<4 * kVmemPerPhase>(); break;
+      case 5: wait_vmcnt<5 * kVmemPerPhase>(); break;
+      case 6: wait_vmcnt<6 * kVmemPerPhase>(); break;
+      default: wait_vmcnt<7 * kVmemPerPhase>(); break;
     }
+    __builtin_amdgcn_s_barrier();  // every wavefront's copies of phase ph have landed
+    __builtin_amdgcn_sched_barrier(0);
+    compute_phase(bufs[ph], wsc, asc, p.K / 16, ph * (kPhaseK / 128) + wave, wave, r, g,
+                  arow_valid, aw[ph], acc);
   }
 
-  // 3. deterministic reduction of the 8 partial tiles: wave 0 adds waves 1..7 in order
+  // deterministic reduction of the 8 partial tiles: wave 0 adds waves 1..7 in order
   partial[wave][lane] = acc;
   __syncthreads();
   if (wave != 0) return;
@@ -146,20 +205,20 @@ gemm_skinny_kernel(GemmArgs p) {
 
 }  // namespace
 
-size_t skinny_lds_bytes(int64_t K) { return (size_t)(16 * (K / 2) + 16 * (K / 16)); }
-
 hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
   const uint32_t blocks = (a.N + 15) / 16;
-  const size_t lds = skinny_lds_bytes(a.K);
-  static bool attr_set = false;  // idempotent; a race between threads is benign
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_skinny_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)skinny_lds_bytes(kSkinnyMaxK));
-    if (e != hipSuccess) return e;
-    attr_set = true;
+  const dim3 grid(blocks), block(kSkinnyThreads);
+  switch (a.K / kPhaseK) {
+    case 1: hipLaunchKernelGGL(gemm_skinny_kernel<1>, grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(gemm_skinny_kernel<2>, grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL(gemm_skinny_kernel<3>, grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(gemm_skinny_kernel<4>, grid, block, 0, stream, a); break;
+    case 5: hipLaunchKernelGGL(gemm_skinny_kernel<5>, grid, block, 0, stream, a); break;
+    case 6: hipLaunchKernelGGL(gemm_skinny_kernel<6>, grid, block, 0, stream, a); break;
+    case 7: hipLaunchKernelGGL(gemm_skinny_kernel<7>, grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL(gemm_skinny_kernel<8>, grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL(gemm_skinny_kernel, dim3(blocks), dim3(kSkinnyThreads), lds, stream, a);
   return hipGetLastError();
 }
 

@@ -38,7 +38,7 @@ hipError_t launch_gemm_general(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);
 
 // The skinny (decode-shape) kernel keeps a workgroup's 16 weight rows over all of K in LDS
-// (9/16 byte per element): K up to this bound, a multiple of 512.
+// (9/16 byte per element), in phases of 1024: K up to this bound, a multiple of 1024.
 constexpr int64_t kSkinnyMaxK = 8192;
 
 // Which kernel family serves a problem.  The choice depends on M and K only, never on N, so a
