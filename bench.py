@@ -76,17 +76,23 @@ def prefill(args, torch, nv, W):
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
 
-    # per-kernel durations: events on the launch stream around each kernel
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
+    # per-kernel durations, events on the launch stream: the product around each launch (it runs
+    # for milliseconds); the encode around `steps` launches back to back (it runs for tens of
+    # microseconds, so single-launch events would mostly time the launch)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
     for i in range(args.steps):
-        evs[3 * i].record()
         nv.nvfp4_quantize(ad, ga, ac, as_)
-        evs[3 * i + 1].record()
+        evs[2 * i].record()
         nv.fused_nvfp4_gemm(ac, as_, ga, wc, ws, gw, segs, out=C)
-        evs[3 * i + 2].record()
+        evs[2 * i + 1].record()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        nv.nvfp4_quantize(ad, ga, ac, as_)
+    e1.record()
     torch.cuda.synchronize()
-    q_ms = sum(evs[3 * i].elapsed_time(evs[3 * i + 1]) for i in range(args.steps)) / args.steps
-    g_ms = sum(evs[3 * i + 1].elapsed_time(evs[3 * i + 2]) for i in range(args.steps)) / args.steps
+    g_ms = sum(evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(args.steps)) / args.steps
+    q_ms = e0.elapsed_time(e1) / args.steps
     flops = w.flops
     q_bytes = w.M * w.K * (2 + 9 / 16)
     return dict(w=w, ms_step=ms_step, gemm_ms=g_ms, quant_ms=q_ms, flops=flops, q_bytes=q_bytes)
@@ -95,7 +101,12 @@ def prefill(args, torch, nv, W):
 def decode(args, torch, nv, W):
     """Decode-shaped products M in {1, 4, 16}, K = N = 5120, NVFP4 weights resident in HBM and
     rotated over 24 byte-identical copies (354 MB, beyond the 256 MB last-level cache); the
-    activations are encoded per call."""
+    activations are encoded per call.
+
+    Two timings per M: ``call_us``, the median over single calls (encode + product) between HIP
+    events, launch latency included; ``kernel_us``, the product kernels alone, 24 of them (one per
+    weight copy) replayed back to back from a HIP graph, total / 24.  The algorithmic bytes of the
+    product are the NVFP4 weights (codes + scales), the encoded activations and the f32 output."""
     import numpy as np
 
     w = W.WORKLOADS[4]
@@ -120,23 +131,75 @@ def decode(args, torch, nv, W):
             nv.nvfp4_gemm(ac, as_, ga, wc, ws, gw, out=C)
         torch.cuda.synchronize()
         n = 10 * R
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(3 * n)]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
         for i in range(n):
             wc, ws = copies[i % R]
-            evs[3 * i].record()
+            evs[2 * i].record()
             nv.nvfp4_quantize(ad, ga, ac, as_)
-            evs[3 * i + 1].record()
             nv.nvfp4_gemm(ac, as_, ga, wc, ws, gw, out=C)
-            evs[3 * i + 2].record()
+            evs[2 * i + 1].record()
         torch.cuda.synchronize()
-        g_ms = sorted(evs[3 * i + 1].elapsed_time(evs[3 * i + 2]) for i in range(n))[n // 2]
-        call_ms = sorted(evs[3 * i].elapsed_time(evs[3 * i + 2]) for i in range(n))[n // 2]
-        nbytes = w.N * w.K * 9 // 16 + M * w.K * 2 + M * w.N * 4
-        res[f"M{M}"] = {"gemm_us": round(g_ms * 1e3, 3), "call_us": round(call_ms * 1e3, 3),
-                        "GB/s": round(nbytes / (g_ms * 1e-3) / 1e9, 1),
-                        "frac_hbm": round(nbytes / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        call_ms = sorted(evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(n))[n // 2]
+
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for wc, ws in copies:
+                nv.nvfp4_gemm(ac, as_, ga, wc, ws, gw, out=C)
+        graph.replay()
+        torch.cuda.synchronize()
+        reps = 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        k_ms = e0.elapsed_time(e1) / (reps * R)
+        del graph
+        nbytes = w.N * w.K * 9 // 16 + M * w.K * 9 // 16 + M * w.N * 4
+        gbs = nbytes / (k_ms * 1e-3) / 1e9
+        res[f"M{M}"] = {"kernel_us": round(k_ms * 1e3, 3), "call_us": round(call_ms * 1e3, 3),
+                        "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
                         "bytes": nbytes}
     return res
+
+
+def copy_calibration(args, torch):
+    """A plain device-to-device copy of 1 GiB, the reference for scaling HBM byte counters:
+    it reads and writes exactly 2^30 bytes per launch."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(max(args.steps, 1)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copied {n} bytes x {max(args.steps, 1)}")
+
+
+def traffic_from_profile(kernel_files, summary):
+    """HBM bytes per launch recorded in a committed counter summary, or None when the summary is
+    missing or the kernel's sources have changed since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in kernel_files:
+        with open(os.path.join(ROOT, "bit_block_scaled_nvfp4_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith((" ", "#", "|")):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != h.hexdigest():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(rows: int = 48):
@@ -165,6 +228,12 @@ def cpu_baseline(rows: int = 48):
                       f"(encode + exact int64 product), {dt:.1f} s"}
 
 
+# Sources of the tiled product kernel: its committed HBM counter summary is valid while they are
+# unchanged.
+TILED_SOURCES = ("gemm.hip", "gemm_common.h", "nvfp4_internal.h", "api.hip")
+TILED_TRAFFIC = "gemm_tiled_mlp_gate_up_8192x5120x34816_traffic.txt"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +241,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--only", choices=("all", "prefill", "decode", "copy"), default="all",
+                    help="run one part (for profiler runs); 'copy' is the counter calibration copy")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the hot path here is the single-GPU W4A4 linear "
@@ -189,13 +260,22 @@ def main():
         sys.exit(1)
     nv.load_library()
 
+    if args.only == "copy":
+        copy_calibration(args, torch)
+        return
+    if args.only == "decode":
+        print(json.dumps({"decode": decode(args, torch, nv, W)}), flush=True)
+        return
+
     p = prefill(args, torch, nv, W)
-    dec = None if args.no_decode else decode(args, torch, nv, W)
-    cpu = None if args.no_cpu_baseline else cpu_baseline()
+    run_rest = args.only == "all"
+    dec = decode(args, torch, nv, W) if run_rest and not args.no_decode else None
+    cpu = cpu_baseline() if run_rest and not args.no_cpu_baseline else None
 
     w = p["w"]
     value = p["flops"] / (p["ms_step"] * 1e-3) / 1e12
     achieved = p["flops"] / (p["gemm_ms"] * 1e-3) / 1e12
+    q_gbs = p["q_bytes"] / (p["quant_ms"] * 1e-3) / 1e9
     line = {
         "metric": "NVFP4 W4A4 GEMM TFLOP/s (prefill M=8192) + decode GB/s, % of MI355X roofline",
         "value": round(value, 2),
@@ -207,19 +287,20 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4 operands decoded exactly to f16, f16 MFMA, f32 accumulate",
+        "dtype": "nvfp4 (e2m1 + e4m3/16) operands decoded exactly to f16, f16 MFMA, f32 accumulate",
         "data": "synthetic (seeded; bf16 N(0,1) activations with 1% Student-t(3)x50 channels, "
                 "N(0,0.02) weights)",
         "config": {"workload": w.name, "M": w.M, "K": w.K, "N": w.N,
                    "segments": list(w.seg_sizes), "act_scale": "static", "output": "f32"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "fused_nvfp4_gemm (tiled)", "kernel_ms": round(p["gemm_ms"], 4),
+                     "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": traffic_from_profile(TILED_SOURCES, TILED_TRAFFIC),
+                     "kernel": "gemm_tiled_kernel (fused_nvfp4_gemm)",
+                     "kernel_ms": round(p["gemm_ms"], 4),
                      "frac_of_mxfp4_peak": round(achieved / MFMA_FP4_PEAK_TFLOPS, 4)},
-        "quantize": {"ms": round(p["quant_ms"], 4),
-                     "GB/s": round(p["q_bytes"] / (p["quant_ms"] * 1e-3) / 1e9, 1),
-                     "frac_hbm": round(p["q_bytes"] / (p["quant_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "quantize": {"bound": "hbm", "ms": round(p["quant_ms"], 4), "GB/s": round(q_gbs, 1),
+                     "frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4), "bytes": int(p["q_bytes"])},
         "decode": dec,
         "cpu_baseline": cpu,
     }
