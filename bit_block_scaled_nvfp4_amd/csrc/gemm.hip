@@ -20,6 +20,8 @@
 // elements [32h, 32h + 32) of its row and uses 32-bit word j of them in MFMA step j (j = 0..3).
 // A and W use the same map, so after 4 steps every k of the chunk has been contracted once.  Word
 // j covers elements 32h + 8j .. +7, which lie in 16-block 2h + j/2 of the chunk.
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace nvfp4 {
@@ -88,7 +90,6 @@ struct TileCfg {
   static_assert(BM * 2 % kThreads == 0 && BN * 2 % kThreads == 0, "piece split");
   static_assert(BM % kThreads == 0 && BN % kThreads == 0, "scale split");
   static_assert(FM == 4 && FN == 4, "one 16-byte scale read per operand assumes 4 fragments");
-  static_assert(2 * kStage <= 64 * 1024, "static LDS");
 };
 
 // Per-thread byte offsets of the global rows this thread copies (rows beyond the matrix are
@@ -116,9 +117,9 @@ __device__ __forceinline__ int scale_slot_row(int d) {
 }
 
 template <class Cfg, int FM, int FN>
-__device__ __forceinline__ void row_offsets(const GemmArgs& p, int m0, int n0, RowOffsets<Cfg>& o) {
+__device__ __forceinline__ void row_offsets(const GemmArgs& p, int m0, int n0, int tid,
+                                            RowOffsets<Cfg>& o) {
   const uint32_t kb = (uint32_t)p.K / 2, ks = (uint32_t)p.K / 16;
-  const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < Cfg::kPiecesA; ++i) {
     const int d = tid + i * Cfg::kThreads;
@@ -223,6 +224,9 @@ __device__ __forceinline__ void decode_step(const Frags<FM, FN>& f, const half2_
   for (int j = 0; j < FN; ++j) bv[j] = decode8(word<STEP>(f.qb[j]), STEP < 2 ? sb[j][0] : sb[j][1]);
 }
 
+// The weight fragment is the MFMA's first operand, so acc[i][j] holds the transposed 32x32 block:
+// lane (r, h) owns row m = r of A fragment i and columns n = 8 q + 4 h + (0..3) of W fragment j
+// in registers 4 q .. 4 q + 3 -- four consecutive columns of one row of C, stored as one vector.
 template <int FM, int FN>
 __device__ __forceinline__ void mfma_step(const half8_t (&av)[FM], const half8_t (&bv)[FN],
                                           floatx16 (&acc)[FM][FN]) {
@@ -230,7 +234,7 @@ __device__ __forceinline__ void mfma_step(const half8_t (&av)[FM], const half8_t
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[j], av[i], acc[i][j], 0, 0, 0);
 }
 
 // Interleave the FM*FN MFMAs of one step with the VALU work of decoding the next step: one MFMA,
@@ -301,21 +305,104 @@ __device__ __forceinline__ void pipelined_chunk(const Frags<FM, FN>& cur, Frags<
   interleave_mfma_valu<FM, FN>();
 }
 
-// Main kernel.  Two LDS stages filled by direct global->LDS copies, two register sets of
-// fragments.  In the middle of K chunk kc (after its second MFMA step) every wavefront waits for its
-// own copies of chunk kc+1, meets the others at a barrier (chunk kc+1 is then complete in LDS and
-// every wavefront has read chunk kc, whose stage is free), reads its fragments of chunk kc+1, and
-// issues the copies of chunk kc+2 into chunk kc's stage.  The remaining MFMA steps of chunk kc
-// then cover the LDS reads and the decode of chunk kc+1's first step, so the matrix core does not
-// idle across chunks.
+// The thread index behind a compiler barrier: values derived from it inside a loop are not hoisted
+// out of the loop, so they do not occupy registers across the main loop.
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass parses device code but cannot take AMDGPU constraints
+  asm volatile("" : "+v"(t));
+#endif
+  return t;
+}
+
+// Epilogue of one tile: C = acc * alpha[column], through LDS one fragment row (32 rows of the
+// wavefront's sub-tile) at a time.  Each lane writes its four-column pieces into the wavefront's
+// own staging rows, then reads back four consecutive columns of one row, so that a wavefront store
+// covers two rows x 512 bytes -- whole cache lines, not 32 rows x 32 bytes.  The staging area
+// belongs to one wavefront and LDS instructions of a wavefront execute in order, so no barrier is
+// needed.  Rows and columns past the matrix are masked at the store; a lane stores its four
+// columns as one vector when they are all inside and rows of C start 16-byte aligned (`vec`).
+template <int FN>
+constexpr int kEpiStride = FN * 32 + 4;  // floats per staged row; the pad spreads rows over banks
+
+template <bool BF16, int FM, int FN>
+__device__ __forceinline__ void store_tile(const GemmArgs& p, const floatx16 (&acc)[FM][FN],
+                                           const float* alpha, float* epi, int m0, int n0, int wm,
+                                           int wn, int lane, bool vec) {
+  using OutT = typename std::conditional<BF16, uint16_t, float>::type;
+  OutT* const c = reinterpret_cast<OutT*>(p.c);
+  constexpr int S = kEpiStride<FN>;
+  const int r = lane & 31, h = lane >> 5;
+  const int cc = (lane & 31) * 4;  // read-back columns of this lane within the wavefront's 128
+  const int n = n0 + wn * FN * 32 + cc;
+  const floatx4 al = *reinterpret_cast<const floatx4*>(alpha + wn * FN * 32 + cc);
+  const bool full = vec && n + 3 < p.N;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<floatx4*>(epi + r * S + j * 32 + 8 * q + 4 * h) =
+            floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                    acc[i][j][4 * q + 3]};
+    const int mb = m0 + wm * FM * 32 + i * 32 + h;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const floatx4 x = *reinterpret_cast<const floatx4*>(epi + (2 * t + h) * S + cc);
+      const floatx4 v = {x[0] * al[0], x[1] * al[1], x[2] * al[2], x[3] * al[3]};
+      const int m = mb + 2 * t;
+      if (m >= p.M) continue;
+      OutT* const dst = c + (int64_t)m * p.ldc + n;
+      if (full) {
+        if constexpr (BF16) {
+          const uint32_t lo = f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+          const uint32_t hi = f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+          *reinterpret_cast<uint2*>(dst) = uint2{lo, hi};
+        } else {
+          *reinterpret_cast<floatx4*>(dst) = v;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (n + e < p.N) {
+            if constexpr (BF16)
+              dst[e] = f32_to_bf16_rne(v[e]);
+            else
+              dst[e] = v[e];
+          }
+        }
+      }
+    }
+    // one fragment row at a time: its accumulators are read into registers only here
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Main kernel, persistent: workgroup b runs tiles b, b + G, b + 2G, ... (G = grid size, at most
+// one workgroup per compute unit).  Two LDS stages filled by direct global->LDS copies, two
+// register sets of fragments.  In the middle of K chunk kc (after its second MFMA step) every
+// wavefront waits for its own copies of chunk kc+1, meets the others at a barrier (chunk kc+1 is
+// then complete in LDS and every wavefront has read chunk kc, whose stage is free), reads its
+// fragments of chunk kc+1, and issues the copies of chunk kc+2 into chunk kc's stage.  The
+// remaining MFMA steps of chunk kc then cover the LDS reads and the decode of chunk kc+1's first
+// step, so the matrix core does not idle across chunks.
 // The K loop is unrolled by 2 so each stage and register set is named statically; past the last
 // chunk, reads and copies are clamped to it (redundant, never used), keeping the loop branch-free.
+// Between tiles, the copies of the next tile's first two chunks are issued before the stores of
+// the finished tile, so the store traffic and the next tile's first loads are in flight together.
+// Each lane copies into LDS slots of its own wavefront only, and waits for its own copies before
+// issuing the next tile's, so stages never see two tiles' copies race.
 template <int WAVES_M, int WAVES_N, int FM, int FN>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1)
 gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
   using Cfg = TileCfg<WAVES_M, WAVES_N, FM, FN>;
   __shared__ __attribute__((aligned(16))) uint8_t s0[Cfg::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t s1[Cfg::kStage];
+  // per-column epilogue factors of the current tile, double-buffered by tile parity
+  __shared__ __attribute__((aligned(16))) float alpha_s[2][Cfg::BN];
+  // epilogue staging, one area of 32 rows per wavefront
+  __shared__ __attribute__((aligned(16))) float epi_s[WAVES_M * WAVES_N][32 * kEpiStride<FN>];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -324,21 +411,11 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
   const int h = lane >> 5;
   const int r = lane & 31;
   const uint32_t sh = 16u * (uint32_t)h;  // lane half h uses scale bytes 2h, 2h+1
-  uint32_t tmi, tni;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, tmi, tni);
-  const int m0 = (int)tmi * Cfg::BM;
-  const int n0 = (int)tni * Cfg::BN;
+  const uint32_t ntiles = tiles_m * tiles_n;
   const int nchunks = p.K / 64;
   const int last = nchunks - 1;
-
-  RowOffsets<Cfg> ro;
-  row_offsets<Cfg, FM, FN>(p, m0, n0, ro);
-
-  floatx16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = floatx16{};
+  const float ga = *p.a_g;
+  const bool vec = (p.ldc & 3) == 0;  // rows of C start 16-byte aligned (C itself is)
 
   // LDS read offsets of this lane's fragments and scale groups (within a stage)
   const int a_frag = (wm * FM) * 1024 + lane * 16;
@@ -346,52 +423,89 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
   const int a_scl = Cfg::kCodesA + Cfg::kCodesB + (wm * 32 + r) * FM * 4;
   const int b_scl = Cfg::kCodesA + Cfg::kCodesB + Cfg::kScalesA + (wn * 32 + r) * FN * 4;
 
-  Frags<FM, FN> f0, f1;
-  half2_t sa[FM], sb[FN];
-  half8_t a0[FM], b0[FN], a1[FM], b1[FN];
-
-  // prologue: chunk 0 into s0 and registers, chunk 1 in flight into s1
-  issue_chunk<Cfg>(p, ro, 0, s0);
-  sync_and_read(s0, a_frag, b_frag, a_scl, b_scl, f0);
-  issue_chunk<Cfg>(p, ro, min(1, last), s1);
-  decode_scales(f0, sh, sa, sb);
-  decode_step<0>(f0, sa, sb, a0, b0);
-
-  int kc = 0;
-  for (; kc + 1 < nchunks; kc += 2) {
-    // chunk kc (in f0; stage s0), chunk kc+1 in flight into s1
-    pipelined_chunk(f0, f1, sa, sb, a0, b0, a1, b1, sh, acc, [&](Frags<FM, FN>& n) {
-      sync_and_read(s1, a_frag, b_frag, a_scl, b_scl, n);
-      issue_chunk<Cfg>(p, ro, min(kc + 2, last), s0);
-    });
-    // chunk kc+1 (in f1; stage s1), chunk kc+2 in flight into s0
-    pipelined_chunk(f1, f0, sa, sb, a0, b0, a1, b1, sh, acc, [&](Frags<FM, FN>& n) {
-      sync_and_read(s0, a_frag, b_frag, a_scl, b_scl, n);
-      issue_chunk<Cfg>(p, ro, min(kc + 3, last), s1);
-    });
+  uint32_t v = blockIdx.x;
+  uint32_t tmi, tni;
+  tile_coords(v, tiles_m, tiles_n, tmi, tni);
+  int m0 = (int)tmi * Cfg::BM;
+  int n0 = (int)tni * Cfg::BN;
+  {
+    const int tid_t = threadIdx.x;
+    RowOffsets<Cfg> ro;
+    row_offsets<Cfg, FM, FN>(p, m0, n0, tid_t, ro);
+    issue_chunk<Cfg>(p, ro, 0, s0);
+    issue_chunk<Cfg>(p, ro, min(1, last), s1);
   }
-  if (kc < nchunks)  // odd number of chunks: the last one is in f0
-    pipelined_chunk(f0, f1, sa, sb, a0, b0, a1, b1, sh, acc, [&](Frags<FM, FN>& n) {});
-  // no copy may still be writing LDS when the workgroup ends
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(0x3F70);
 
-  // epilogue: lane holds column n = tile col + r of each FN fragment, rows 8*(e/4) + 4h + e%4
-  const float ga = *p.a_g;
+  for (int par = 0;; par ^= 1) {
+    // The copy offsets are recomputed here rather than carried over from the early issue of this
+    // tile's first chunks: carried over, they would stay live across the previous tile's stores
+    // (the empty asm keeps the two computations apart).
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" : "+s"(m0), "+s"(n0));
+#endif
+    const int tid_t = opaque_tid();
+    RowOffsets<Cfg> ro;
+    row_offsets<Cfg, FM, FN>(p, m0, n0, tid_t, ro);
+    for (int c = tid_t; c < Cfg::BN; c += Cfg::kThreads)
+      alpha_s[par][c] = column_alpha(p.seg, p.seg_g, ga, min(n0 + c, p.N - 1));
+
+    floatx16 acc[FM][FN];
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int n = n0 + wn * FN * 32 + j * 32 + r;
-    if (n >= p.N) continue;
-    const float alpha = column_alpha(p.seg, p.seg_g, ga, n);
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int mb = m0 + wm * FM * 32 + i * 32 + 4 * h;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = mb + 8 * (e / 4) + (e % 4);
-        if (m < p.M) store_c(p.c, p.c_bf16, p.ldc, m, n, acc[i][j][e] * alpha);
-      }
+      for (int j = 0; j < FN; ++j) acc[i][j] = floatx16{};
+
+    Frags<FM, FN> f0, f1;
+    half2_t sa[FM], sb[FN];
+    half8_t a0[FM], b0[FN], a1[FM], b1[FN];
+
+    // chunk 0 into registers (chunk 1 is already in flight into s1)
+    sync_and_read(s0, a_frag, b_frag, a_scl, b_scl, f0);
+    decode_scales(f0, sh, sa, sb);
+    decode_step<0>(f0, sa, sb, a0, b0);
+
+    int kc = 0;
+    for (; kc + 1 < nchunks; kc += 2) {
+      // chunk kc (in f0; stage s0), chunk kc+1 in flight into s1
+      pipelined_chunk(f0, f1, sa, sb, a0, b0, a1, b1, sh, acc, [&](Frags<FM, FN>& n) {
+        sync_and_read(s1, a_frag, b_frag, a_scl, b_scl, n);
+        issue_chunk<Cfg>(p, ro, min(kc + 2, last), s0);
+      });
+      // chunk kc+1 (in f1; stage s1), chunk kc+2 in flight into s0
+      pipelined_chunk(f1, f0, sa, sb, a0, b0, a1, b1, sh, acc, [&](Frags<FM, FN>& n) {
+        sync_and_read(s0, a_frag, b_frag, a_scl, b_scl, n);
+        issue_chunk<Cfg>(p, ro, min(kc + 3, last), s1);
+      });
     }
+    if (kc < nchunks)  // odd number of chunks: the last one is in f0
+      pipelined_chunk(f0, f1, sa, sb, a0, b0, a1, b1, sh, acc, [&](Frags<FM, FN>& n) {});
+    // this lane's redundant copies past the last chunk have landed before its stages are reused
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x3F70);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // lane values of the epilogue and of the next tile's copies, derived afresh (not hoisted)
+    const int tid_e = opaque_tid();
+    const int lane_e = tid_e & 63, wave_e = tid_e >> 6;
+    const int tm0 = m0, tn0 = n0;
+    v += gridDim.x;
+    const bool more = v < ntiles;
+    if (more) {
+      tile_coords(v, tiles_m, tiles_n, tmi, tni);
+      m0 = (int)tmi * Cfg::BM;
+      n0 = (int)tni * Cfg::BN;
+      RowOffsets<Cfg> ron;
+      row_offsets<Cfg, FM, FN>(p, m0, n0, tid_e, ron);
+      issue_chunk<Cfg>(p, ron, 0, s0);
+      issue_chunk<Cfg>(p, ron, min(1, last), s1);
+    }
+    if (p.c_bf16)
+      store_tile<true>(p, acc, alpha_s[par], epi_s[wave_e], tm0, tn0, wave_e / WAVES_N,
+                       wave_e % WAVES_N, lane_e, vec);
+    else
+      store_tile<false>(p, acc, alpha_s[par], epi_s[wave_e], tm0, tn0, wave_e / WAVES_N,
+                        wave_e % WAVES_N, lane_e, vec);
+    if (!more) break;
   }
 }
 
@@ -404,9 +518,16 @@ hipError_t launch_tiled_cfg(const GemmArgs& a, hipStream_t stream) {
   using Cfg = TileCfg<WAVES_M, WAVES_N, FM, FN>;
   const uint32_t tiles_m = (a.M + Cfg::BM - 1) / Cfg::BM;
   const uint32_t tiles_n = (a.N + Cfg::BN - 1) / Cfg::BN;
-  auto kern = gemm_tiled_kernel<WAVES_M, WAVES_N, FM, FN>;
-  hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(Cfg::kThreads), 0, stream, a, tiles_m,
-                     tiles_n);
+  // one workgroup per compute unit (the kernel's registers allow one per compute unit), each
+  // walking its share of the tiles
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const uint32_t ntiles = tiles_m * tiles_n;
+  const uint32_t grid = min(ntiles, (uint32_t)max(cus, 1));
+  hipLaunchKernelGGL((gemm_tiled_kernel<WAVES_M, WAVES_N, FM, FN>), dim3(grid),
+                     dim3(Cfg::kThreads), 0, stream, a, tiles_m, tiles_n);
   return hipGetLastError();
 }
 

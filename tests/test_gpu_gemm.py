@@ -60,8 +60,8 @@ def test_workload1_full():
 @pytest.mark.parametrize("M,N,K", [
     (1, 1, 16), (1, 37, 64), (5, 70, 48), (33, 65, 80), (31, 129, 128), (64, 64, 64),
     (129, 130, 192), (200, 300, 1024), (257, 255, 320), (96, 160, 5120),
-    # decode-shaped (M <= 16): the skinny kernel for K a multiple of 512 up to 16384 (ragged N,
-    # K runs shorter than the 8 wavefronts), the tiled kernel otherwise
+    # decode-shaped (M <= 16): the skinny kernel for K a multiple of 1024 up to 8192 (ragged N),
+    # the tiled or general kernel otherwise
     (1, 100, 512), (3, 77, 1536), (16, 40, 1024), (7, 33, 512), (16, 16, 2048), (5, 3, 16384),
     (2, 300, 17408), (1, 19, 384),
 ])
@@ -81,6 +81,37 @@ def test_bf16_output():
     # bf16 output: one extra rounding of the FP32 result (relative 2^-9)
     assert np.all(np.abs(C - R) <= 2.0 ** -8 * np.abs(R) + 1e-4 * oracle.gemm_abs_bound(
         ac, as_, ga, wc, ws, gw, [0, 72]))
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 260, 256), (3, 70, 1024), (40, 33, 80)])
+@pytest.mark.parametrize("pad", [3, 8])
+@pytest.mark.parametrize("odt", ["f32", "bf16"])
+def test_output_view_with_row_pitch(M, N, K, pad, odt):
+    """C written into a column window of a wider buffer: row pitch N + pad elements (not a multiple
+    of 4 for pad = 3, so rows are not 16-byte aligned), window starting 8 elements in.  Elements
+    outside the window keep their sentinel value."""
+    import torch
+
+    import bit_block_scaled_nvfp4_amd as nv
+
+    a = random_matrix(M + 3 * K, M, K, outlier_cols=2)
+    wt = random_matrix(N + 5 * K, N, K, std=0.02)
+    ac, as_, ga, wc, ws, gw = _encode(a, wt, [0, N])
+    dt = torch.float32 if odt == "f32" else torch.bfloat16
+    buf = torch.full((M, N + pad + 8), -7.0, dtype=dt, device=DEV)
+    out = buf[:, 8:8 + N]
+    nv.nvfp4_gemm(_up(ac), _up(as_), scalar(ga), _up(wc), _up(ws), _up(np.asarray([gw], np.float32)),
+                  out=out)
+    torch.cuda.synchronize()
+    hb = buf.float().cpu().numpy()
+    assert np.all(hb[:, :8] == -7.0) and np.all(hb[:, 8 + N:] == -7.0)
+    C = hb[:, 8:8 + N].astype(np.float64)
+    R = oracle.gemm_exact(ac, as_, ga, wc, ws, [gw], [0, N])
+    B = oracle.gemm_abs_bound(ac, as_, ga, wc, ws, [gw], [0, N])
+    if odt == "f32":
+        check_gemm(C, R, B, f"view M={M} N={N} K={K} pad={pad}")
+    else:  # one extra rounding of the FP32 result to bf16
+        assert np.all(np.abs(C - R) <= 2.0 ** -8 * np.abs(R) + 1e-4 * B)
 
 
 def test_fused_equals_per_segment_calls_bitwise():
