@@ -275,33 +275,78 @@ __device__ __forceinline__ void sync_and_read(const uint8_t* stage, int a_frag, 
   read_frags(stage, a_frag, b_frag, a_scl, b_scl, f);
 }
 
-// One K chunk, software-pipelined with the next: the MFMAs of steps 0-1 of chunk kc run under the
-// decode of steps 1-2; then the next chunk's fragments are read (sync_and_read) and its copy of
-// chunk kc+2 issued (`next`); the MFMAs of step 2 run under the decode of step 3 while those LDS
-// reads complete, and the MFMAs of step 3 run under the decode of the next chunk's step 0.  On
-// entry `cur` holds chunk kc's fragments and a0/b0 its decoded step 0; on exit `nxt` holds chunk
-// kc+1's fragments and a0/b0 its decoded step 0.
-template <int FM, int FN, class Next>
+// MFMAs k = FROM .. TO-1 of one step, k = i * FN + j.
+template <int FROM, int TO, int FM, int FN>
+__device__ __forceinline__ void mfma_range(const half8_t (&av)[FM], const half8_t (&bv)[FN],
+                                           floatx16 (&acc)[FM][FN]) {
+#pragma unroll
+  for (int k = FROM; k < TO; ++k)
+    acc[k / FN][k % FN] =
+        __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[k % FN], av[k / FN], acc[k / FN][k % FN], 0, 0, 0);
+}
+
+// MFMAs of step 2 issued before the mid-chunk barrier: they keep the matrix core busy while the
+// wavefronts meet.
+constexpr int kPreBarrierMfma = 4;
+
+// Schedule of the MFMAs after the mid-chunk barrier: the next chunk's LDS reads (two per MFMA) and
+// the copies of the chunk after it go out between MFMAs, with the decode VALU spread over all of
+// them, rather than as one block in front of the MFMAs.
+template <int FM, int FN, int NDS, int NVM>
+__device__ __forceinline__ void interleave_after_barrier() {
+  constexpr int kM = FM * FN - kPreBarrierMfma;
+  constexpr int kDsMfma = (NDS + 1) / 2;  // MFMAs carrying two LDS reads
+  constexpr int kValu = (8 * (FM + FN) + NVM + kM - 1) / kM + 1;
+#pragma unroll
+  for (int k = 0; k < kM; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if (k < kDsMfma) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+    else if (k - kDsMfma < NVM) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM
+    __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);  // VALU
+  }
+}
+
+// One K chunk, software-pipelined with the next.  The MFMAs of steps 0-1 of chunk kc run under
+// the decode of steps 1-2.  The first MFMAs of step 2 are issued; then every wavefront waits for
+// its own copies of chunk kc+1 and meets the others at a barrier (chunk kc+1 is complete in LDS,
+// and every wavefront has read chunk kc, whose stage is free).  The remaining MFMAs of step 2 run
+// under the LDS reads of chunk kc+1's fragments, the copies of chunk kc+2 (`issue`, into chunk
+// kc's stage) and the decode of step 3; the MFMAs of step 3 run under the decode of the next
+// chunk's step 0.  On entry `cur` holds chunk kc's fragments and a0/b0 its decoded step 0; on exit
+// (HAS_NEXT) `nxt` holds chunk kc+1's fragments and a0/b0 its decoded step 0.
+template <bool HAS_NEXT, int NVM, int FM, int FN, class Issue>
 __device__ __forceinline__ void pipelined_chunk(const Frags<FM, FN>& cur, Frags<FM, FN>& nxt,
-                                                half2_t (&sa)[FM], half2_t (&sb)[FN],
-                                                half8_t (&a0)[FM], half8_t (&b0)[FN],
-                                                half8_t (&a1)[FM], half8_t (&b1)[FN], uint32_t sh,
-                                                floatx16 (&acc)[FM][FN], Next&& next) {
+                                                const uint8_t* nstage, int a_frag, int b_frag,
+                                                int a_scl, int b_scl, half2_t (&sa)[FM],
+                                                half2_t (&sb)[FN], half8_t (&a0)[FM],
+                                                half8_t (&b0)[FN], half8_t (&a1)[FM],
+                                                half8_t (&b1)[FN], uint32_t sh,
+                                                floatx16 (&acc)[FM][FN], Issue&& issue) {
   mfma_step(a0, b0, acc);
   decode_step<1>(cur, sa, sb, a1, b1);
   interleave_mfma_valu<FM, FN>();
   mfma_step(a1, b1, acc);
   decode_step<2>(cur, sa, sb, a0, b0);
   interleave_mfma_valu<FM, FN>();
-  next(nxt);
   __builtin_amdgcn_sched_barrier(0);
-  mfma_step(a0, b0, acc);
+  mfma_range<0, kPreBarrierMfma>(a0, b0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (HAS_NEXT) {
+    __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): this lane's copies of chunk kc+1 landed
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(nstage, a_frag, b_frag, a_scl, b_scl, nxt);
+    issue();
+  }
+  mfma_range<kPreBarrierMfma, FM * FN>(a0, b0, acc);
   decode_step<3>(cur, sa, sb, a1, b1);
-  interleave_mfma_valu<FM, FN>();
+  interleave_after_barrier<FM, FN, HAS_NEXT ? FM + FN + 2 : 0, HAS_NEXT ? NVM : 0>();
   __builtin_amdgcn_sched_barrier(0);
   mfma_step(a1, b1, acc);
-  decode_scales(nxt, sh, sa, sb);
-  decode_step<0>(nxt, sa, sb, a0, b0);
+  if constexpr (HAS_NEXT) {
+    decode_scales(nxt, sh, sa, sb);
+    decode_step<0>(nxt, sa, sb, a0, b0);
+  }
   interleave_mfma_valu<FM, FN>();
 }
 
@@ -464,21 +509,21 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
     decode_scales(f0, sh, sa, sb);
     decode_step<0>(f0, sa, sb, a0, b0);
 
+    constexpr int kCopies = Cfg::kPiecesA + Cfg::kPiecesB + Cfg::kWordsA + Cfg::kWordsB;
     int kc = 0;
     for (; kc + 1 < nchunks; kc += 2) {
       // chunk kc (in f0; stage s0), chunk kc+1 in flight into s1
-      pipelined_chunk(f0, f1, sa, sb, a0, b0, a1, b1, sh, acc, [&](Frags<FM, FN>& n) {
-        sync_and_read(s1, a_frag, b_frag, a_scl, b_scl, n);
-        issue_chunk<Cfg>(p, ro, min(kc + 2, last), s0);
-      });
+      pipelined_chunk<true, kCopies>(f0, f1, s1, a_frag, b_frag, a_scl, b_scl, sa, sb, a0, b0,
+                                     a1, b1, sh, acc,
+                                     [&] { issue_chunk<Cfg>(p, ro, min(kc + 2, last), s0); });
       // chunk kc+1 (in f1; stage s1), chunk kc+2 in flight into s0
-      pipelined_chunk(f1, f0, sa, sb, a0, b0, a1, b1, sh, acc, [&](Frags<FM, FN>& n) {
-        sync_and_read(s0, a_frag, b_frag, a_scl, b_scl, n);
-        issue_chunk<Cfg>(p, ro, min(kc + 3, last), s1);
-      });
+      pipelined_chunk<true, kCopies>(f1, f0, s0, a_frag, b_frag, a_scl, b_scl, sa, sb, a0, b0,
+                                     a1, b1, sh, acc,
+                                     [&] { issue_chunk<Cfg>(p, ro, min(kc + 3, last), s1); });
     }
     if (kc < nchunks)  // odd number of chunks: the last one is in f0
-      pipelined_chunk(f0, f1, sa, sb, a0, b0, a1, b1, sh, acc, [&](Frags<FM, FN>& n) {});
+      pipelined_chunk<false, kCopies>(f0, f1, s1, a_frag, b_frag, a_scl, b_scl, sa, sb, a0, b0,
+                                      a1, b1, sh, acc, [] {});
     // this lane's redundant copies past the last chunk have landed before its stages are reused
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0x3F70);
