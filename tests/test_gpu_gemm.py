@@ -114,6 +114,35 @@ def test_output_view_with_row_pitch(M, N, K, pad, odt):
         assert np.all(np.abs(C - R) <= 2.0 ** -8 * np.abs(R) + 1e-4 * B)
 
 
+@pytest.mark.parametrize("M,N,K", [
+    (1, 5000, 1024), (4, 4100, 2048), (16, 8100, 1024), (3, 9000, 1024), (8, 3000, 7168),
+    (2, 4500, 8192), (16, 5123, 1024),
+])
+def test_skinny_column_split(M, N, K):
+    """Decode-shaped products whose columns are split evenly over the compute units: workgroups of
+    more than 16 columns (two MFMA tiles, the second partly empty), more than 32 columns per compute
+    unit, ragged last workgroups, and K up to the largest the skinny kernel takes."""
+    a = random_matrix(M * 11 + K, M, K, outlier_cols=max(1, K // 100))
+    wt = random_matrix(N * 3 + K, N, K, std=0.02)
+    enc = _encode(a, wt, [0, N])
+    _check(*enc, [0, N], f"skinny M={M} N={N} K={K}")
+
+
+def test_skinny_fused_equals_per_segment_calls_bitwise():
+    """On the decode path the fused product (two tiles per workgroup) and the per-segment products
+    (one tile) must agree bit for bit: every column is accumulated the same way."""
+    M, K = 4, 2048
+    sizes = [2048, 2048, 48, 48]
+    segs = list(np.cumsum([0] + sizes))
+    a = random_matrix(40, M, K, outlier_cols=20)
+    wt = random_matrix(41, segs[-1], K, std=0.02)
+    ac, as_, ga, wc, ws, gw = _encode(a, wt, segs)
+    fused = _gpu_product(ac, as_, ga, wc, ws, gw, segs)
+    parts = [_gpu_product(ac, as_, ga, wc[segs[j]:segs[j + 1]], ws[segs[j]:segs[j + 1]], [gw[j]],
+                          [0, sizes[j]]) for j in range(len(sizes))]
+    assert np.array_equal(fused, np.concatenate(parts, axis=1))
+
+
 def test_fused_equals_per_segment_calls_bitwise():
     M, K = 96, 512
     sizes = [64, 64, 128, 48, 48, 7]
