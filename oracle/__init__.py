@@ -25,3 +25,4 @@ from .nvfp4_oracle import (  # noqa: F401
     quantize_segments,
     unpack_codes,
 )
+from .activation import round_to_bf16, silu, silu_mul_activation, silu_mul_quantize  # noqa: F401

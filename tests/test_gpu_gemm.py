@@ -251,7 +251,7 @@ def _sampled_full_size(wid, M=None):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("wid", [2, 3, 5])
+@pytest.mark.parametrize("wid", [2, 3])
 def test_full_size_sampled(wid):
     _sampled_full_size(wid)
 

@@ -141,7 +141,7 @@ def test_determinism():
     assert all(np.array_equal(u, v) for u, v in zip(a, b))
 
 
-@pytest.mark.parametrize("wid", [2, 3, 4, 5])
+@pytest.mark.parametrize("wid", [2, 3, 4])
 def test_full_size_activations_sampled_rows(wid):
     """Full-size activation tensor quantised on the GPU with the static scale the benchmark uses
     (2688 / amax, computed on the host from the generated tensor) and with the dynamic scale;

@@ -4,6 +4,7 @@ from .synthetic import (  # noqa: F401
     WORKLOADS,
     Workload,
     activations,
+    gate_up,
     outlier_channels,
     random_matrix,
     round_bf16,

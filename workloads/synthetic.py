@@ -113,9 +113,9 @@ def _activation_chunk(w: Workload, c: int, chunk: int) -> np.ndarray:
     rng = np.random.Generator(bitgen)
     rows = chunk
     if w.silu_mul:
-        g = rng.standard_normal((rows, w.K), dtype=np.float32)
-        u = rng.standard_normal((rows, w.K), dtype=np.float32)
-        x = (g / (np.float32(1.0) + np.exp(-g))) * u
+        raise ValueError(
+            f"workload {w.name}: its activation is SiLU(g) * u, a step of the method -- draw the "
+            "inputs with gate_up() and form the activation with the encoder under test")
     else:
         x = rng.standard_normal((rows, w.K), dtype=np.float32)
         ch = outlier_channels(w)
@@ -128,6 +128,29 @@ def _activation_chunk(w: Workload, c: int, chunk: int) -> np.ndarray:
                     np.float32)
     x = x.astype(np.float32)
     return round_bf16(x) if w.act_dtype == "bf16" else x
+
+
+def gate_up(w: Workload, M: int | None = None, row0: int = 0):
+    """Gate and up projections ``(g, u)`` (rows ``[row0, row0 + M)``, float32 arrays holding
+    bfloat16 values, each element drawn N(0, 1)) of a workload whose activation is SiLU(g) * u.
+    Rows are drawn in fixed 256-row chunks so any row range reproduces the full tensors."""
+    if not w.silu_mul:
+        raise ValueError(f"workload {w.name} has no gate/up inputs")
+    M = w.M if M is None else M
+    if M == 0:
+        z = np.zeros((0, w.K), dtype=np.float32)
+        return z, z.copy()
+    chunk = 256
+    c0, c1 = row0 // chunk, (row0 + M + chunk - 1) // chunk
+    gs, us = [], []
+    for c in range(c0, c1):
+        rng = np.random.Generator(np.random.PCG64(1000 * w.wid + 1).jumped(c))
+        gs.append(rng.standard_normal((chunk, w.K), dtype=np.float32))
+        us.append(rng.standard_normal((chunk, w.K), dtype=np.float32))
+    off = row0 - c0 * chunk
+    g = np.concatenate(gs, axis=0)[off:off + M]
+    u = np.concatenate(us, axis=0)[off:off + M]
+    return round_bf16(np.ascontiguousarray(g)), round_bf16(np.ascontiguousarray(u))
 
 
 def weights(w: Workload, rows: slice | None = None) -> np.ndarray:
