@@ -164,6 +164,40 @@ def decode(args, torch, nv, W):
     return res
 
 
+def silu_quantize(args, torch, nv, W):
+    """The fused SiLU(g) * u -> NVFP4 encoder on the long-prefill down projection's input
+    (32768 x 17408 bf16 gate and up), static global scale.  Timed over `steps` launches back to
+    back between HIP events; bytes = bf16 gate + up read, codes + scales written."""
+    import numpy as np
+
+    w = W.WORKLOADS[5]
+    dev = "cuda:0"
+    log(f"[bench] generating gate/up {w.M}x{w.K}")
+    g, u = W.gate_up(w)
+    gd = torch.from_numpy(g).to(torch.bfloat16).to(dev)
+    ud = torch.from_numpy(u).to(torch.bfloat16).to(dev)
+    del g, u
+    codes = torch.empty((w.M, w.K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((w.M, w.K // 16), dtype=torch.uint8, device=dev)
+    _, _, ga = nv.nvfp4_silu_mul_quantize(gd, ud, None, codes, scales)  # calibration stand-in
+    for _ in range(args.warmup):
+        nv.nvfp4_silu_mul_quantize(gd, ud, ga, codes, scales)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        nv.nvfp4_silu_mul_quantize(gd, ud, ga, codes, scales)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = w.M * w.K * (2 + 2) + w.M * w.K * 9 // 16
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del gd, ud, codes, scales
+    torch.cuda.empty_cache()
+    return {"bound": "hbm", "shape": [w.M, w.K], "ms": round(ms, 4), "GB/s": round(gbs, 1),
+            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": nbytes}
+
+
 def copy_calibration(args, torch):
     """A plain device-to-device copy of 1 GiB, the reference for scaling HBM byte counters:
     it reads and writes exactly 2^30 bytes per launch."""
@@ -241,7 +275,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--only", choices=("all", "prefill", "decode", "copy"), default="all",
+    ap.add_argument("--only", choices=("all", "prefill", "decode", "silu", "copy"), default="all",
                     help="run one part (for profiler runs); 'copy' is the counter calibration copy")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -266,10 +300,14 @@ def main():
     if args.only == "decode":
         print(json.dumps({"decode": decode(args, torch, nv, W)}), flush=True)
         return
+    if args.only == "silu":
+        print(json.dumps({"silu_mul_quantize": silu_quantize(args, torch, nv, W)}), flush=True)
+        return
 
     p = prefill(args, torch, nv, W)
     run_rest = args.only == "all"
     dec = decode(args, torch, nv, W) if run_rest and not args.no_decode else None
+    silu = silu_quantize(args, torch, nv, W) if run_rest else None
     cpu = cpu_baseline() if run_rest and not args.no_cpu_baseline else None
 
     w = p["w"]
@@ -302,6 +340,7 @@ def main():
         "quantize": {"bound": "hbm", "ms": round(p["quant_ms"], 4), "GB/s": round(q_gbs, 1),
                      "frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4), "bytes": int(p["q_bytes"])},
         "decode": dec,
+        "silu_mul_quantize": silu,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

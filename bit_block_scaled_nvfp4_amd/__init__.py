@@ -8,6 +8,7 @@ library is never replaced by a CPU or PyTorch fallback.
 Entry points (same names as the C ABI):
 
 * ``nvfp4_quantize(x, global_scale=None)`` -> ``(codes, scales, global_scale)``
+* ``nvfp4_silu_mul_quantize(gate, up, global_scale=None)`` -> ``(codes, scales, global_scale)``
 * ``nvfp4_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, out_dtype)`` -> ``C``
 * ``fused_nvfp4_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_gscale, seg_offsets,
   out_dtype)`` -> ``C``
@@ -26,8 +27,8 @@ NVFP4_F32, NVFP4_BF16, NVFP4_F16 = 0, 1, 2
 NVFP4_MAX_SEGMENTS = 16
 
 #: every symbol include/nvfp4.h declares
-EXPORTED_SYMBOLS = ("nvfp4_quantize", "nvfp4_gemm", "fused_nvfp4_gemm", "nvfp4_status_string",
-                    "nvfp4_version")
+EXPORTED_SYMBOLS = ("nvfp4_quantize", "nvfp4_silu_mul_quantize", "nvfp4_gemm", "fused_nvfp4_gemm",
+                    "nvfp4_status_string", "nvfp4_version")
 
 _lib = None
 
@@ -52,6 +53,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     c_i64, c_int, c_vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
     lib.nvfp4_quantize.argtypes = [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_int, c_vp, c_vp, c_vp]
     lib.nvfp4_quantize.restype = c_int
+    lib.nvfp4_silu_mul_quantize.argtypes = [c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_i64, c_vp,
+                                            c_int, c_vp, c_vp, c_vp]
+    lib.nvfp4_silu_mul_quantize.restype = c_int
     lib.nvfp4_gemm.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_int,
                                c_i64, c_vp]
     lib.nvfp4_gemm.restype = c_int
@@ -134,6 +138,34 @@ def nvfp4_quantize(x, global_scale=None, codes=None, scales=None):
     _check(lib.nvfp4_quantize(_ptr(x), _dtype_code(x.dtype), rows, cols, x.stride(0),
                               _ptr(global_scale), int(dynamic), _ptr(codes), _ptr(scales),
                               _stream(x.device)))
+    return codes, scales, global_scale
+
+
+def nvfp4_silu_mul_quantize(gate, up, global_scale=None, codes=None, scales=None):
+    """Encode ``bf16(SiLU(gate) * up)`` as NVFP4 on the GPU in one pass (the activation itself is
+    never written).  ``gate`` and ``up``: 2-D, same shape and dtype (f32/bf16/f16), contiguous
+    rows.  ``global_scale`` as for :func:`nvfp4_quantize`.  Returns ``(codes, scales,
+    global_scale)``."""
+    torch = _torch()
+    lib = load_library()
+    if gate.dim() != 2 or gate.stride(1) != 1 or up.dim() != 2 or up.stride(1) != 1:
+        raise ValueError("gate and up must be 2-D with contiguous rows")
+    if gate.shape != up.shape or gate.dtype != up.dtype:
+        raise ValueError("gate and up must have the same shape and dtype")
+    _require_cuda(gate, up)
+    rows, cols = gate.shape
+    dynamic = global_scale is None
+    if dynamic:
+        global_scale = torch.empty(1, dtype=torch.float32, device=gate.device)
+    _require_cuda(global_scale)
+    if codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=gate.device)
+    if scales is None:
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=gate.device)
+    _check(lib.nvfp4_silu_mul_quantize(_ptr(gate), _ptr(up), _dtype_code(gate.dtype), rows, cols,
+                                       gate.stride(0), up.stride(0), _ptr(global_scale),
+                                       int(dynamic), _ptr(codes), _ptr(scales),
+                                       _stream(gate.device)))
     return codes, scales, global_scale
 
 

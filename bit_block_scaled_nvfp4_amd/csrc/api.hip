@@ -104,6 +104,30 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, in
   return device_status(e);
 }
 
+nvfp4_status nvfp4_silu_mul_quantize(const void* gate, const void* up, nvfp4_dtype dtype,
+                                     int64_t rows, int64_t cols, int64_t ld_gate, int64_t ld_up,
+                                     float* global_scale, int dynamic, uint8_t* codes,
+                                     uint8_t* scales, void* stream) {
+  if (!gate || !up || !global_scale || !codes || !scales) return NVFP4_EINVAL;
+  if (!valid_in_dtype(dtype)) return NVFP4_EINVAL;
+  if (dynamic != 0 && dynamic != 1) return NVFP4_EINVAL;
+  if (rows < 0 || cols < 0 || cols % 16 != 0) return NVFP4_ESHAPE;
+  if (ld_gate < cols || ld_gate < 1 || ld_up < cols || ld_up < 1) return NVFP4_ESHAPE;
+  if (rows * (cols / 16) >= (int64_t(1) << 31)) return NVFP4_ESHAPE;
+  if (rows > 0 && ((rows - 1) * ld_gate + cols > (int64_t(1) << 40) ||
+                   (rows - 1) * ld_up + cols > (int64_t(1) << 40)))
+    return NVFP4_ESHAPE;
+  if (!aligned(gate, 16) || !aligned(up, 16) || (ld_gate * dtype_bytes(dtype)) % 16 != 0 ||
+      (ld_up * dtype_bytes(dtype)) % 16 != 0)
+    return NVFP4_EALIGN;
+  if (!aligned(codes, 8) || !aligned(global_scale, 4)) return NVFP4_EALIGN;
+  if ((rows == 0 || cols == 0) && !dynamic) return NVFP4_OK;
+  hipError_t e = nvfp4::launch_silu_mul_quantize(gate, up, dtype, rows, cols, ld_gate, ld_up,
+                                                 global_scale, dynamic, codes, scales,
+                                                 reinterpret_cast<hipStream_t>(stream));
+  return device_status(e);
+}
+
 nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
                         const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale,
                         int64_t M, int64_t N, int64_t K, void* c, nvfp4_dtype c_dtype, int64_t ldc,

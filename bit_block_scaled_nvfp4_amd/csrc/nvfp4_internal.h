@@ -33,6 +33,10 @@ struct GemmArgs {
 hipError_t launch_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
                            float* g, int dynamic, uint8_t* codes, uint8_t* scales,
                            hipStream_t stream);
+hipError_t launch_silu_mul_quantize(const void* gate, const void* up, nvfp4_dtype dt,
+                                    int64_t rows, int64_t cols, int64_t ldg, int64_t ldu,
+                                    float* g, int dynamic, uint8_t* codes, uint8_t* scales,
+                                    hipStream_t stream);
 hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_general(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);

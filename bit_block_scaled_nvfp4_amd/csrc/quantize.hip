@@ -108,6 +108,72 @@ __device__ __forceinline__ uint32_t e2m1_index(float y) {
   return i > 7u ? 7u : i;
 }
 
+// Encode 16 binary32 values as block b: one E4M3 scale byte and 8 code bytes.
+__device__ __forceinline__ void encode_block(const float (&v)[16], float g, float gs6, uint32_t b,
+                                             uint8_t* __restrict__ codes,
+                                             uint8_t* __restrict__ scales) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const uint32_t sc = e4m3_encode(amax * gs6);
+  const float sd = e4m3_value(sc);
+  // sd == 0: r = 0 makes every magnitude 0 (finite inputs)
+  const float r = sd > 0.0f ? g / sd : 0.0f;
+
+  uint32_t word[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t code = e2m1_index(fabsf(v[i]) * r) | ((__float_as_uint(v[i]) >> 31) << 3);
+    word[i >> 3] |= code << (4 * (i & 7));
+  }
+  uint2 out;
+  out.x = word[0];
+  out.y = word[1];
+  *reinterpret_cast<uint2*>(codes + (int64_t)b * 8) = out;
+  scales[b] = (uint8_t)sc;
+}
+
+// ---- SiLU(g) * u rounded once to bfloat16 ---------------------------------------------------
+
+// Nearest bfloat16 value of a binary64 x (ties to the even significand), returned as the
+// binary32 holding it.  bfloat16 keeps 8 significant bits and binary32's exponent range: in the
+// normal range the binary64 pattern is rounded to 7 explicit mantissa bits (nearest-even on the 45
+// dropped bits; a carry into the exponent is the correct binade change, up to +inf); below 2^-126
+// the grid is the multiples of 2^-133, reached by an exact power-of-two scaling and rint.
+__device__ __forceinline__ float bf16_round_from_f64(double x) {
+  const uint64_t bits = (uint64_t)__double_as_longlong(x);
+  const uint64_t sign = bits & 0x8000000000000000ull;
+  const uint64_t mag = bits ^ sign;
+  if (mag >= 0x47F0000000000000ull) return (float)x;  // |x| >= 2^128, inf, NaN
+  if (mag < 0x3810000000000000ull)                    // |x| < 2^-126
+    return (float)(__builtin_rint(x * 0x1p133) * 0x1p-133);
+  const uint64_t r = (mag + ((1ull << 44) - 1ull) + ((mag >> 45) & 1ull)) & ~((1ull << 45) - 1ull);
+  return (float)__longlong_as_double((long long)(r | sign));
+}
+
+// bfloat16 value of SiLU(g) * u = g / (1 + e^-g) * u, rounded once from the exact value.
+// Fast path (|g| <= 16): binary32 with the hardware 2^x and reciprocal.  Its relative error is
+// below 40 units in the last place of the binary32 result (argument rounding of -g log2(e) with
+// |g| <= 16 contributes at most 16 ulp through 2^x, the 2^x and reciprocal instructions about one
+// ulp each, four roundings half an ulp each), so rounding it to bfloat16 gives the same result as
+// rounding the exact value unless it lies within 64 ulps of a bfloat16 midpoint (low 16 bits
+// 0x8000).  Those cases, |g| > 16 and results that are zero, subnormal or not finite are
+// evaluated in binary64 (g / (1 + exp(-g)) * u, in that order) and rounded from there.
+__device__ __forceinline__ float silu_mul_bf16(float g, float u) {
+  if (fabsf(g) <= 16.0f) {
+    const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
+    const float s = g * __builtin_amdgcn_rcpf(1.0f + e);
+    const float y = s * u;
+    const uint32_t yb = __float_as_uint(y);
+    const uint32_t ex = (yb >> 23) & 0xFFu;
+    const uint32_t low = yb & 0xFFFFu;
+    if (ex != 0u && ex != 0xFFu && (low < 0x8000u - 64u || low > 0x8000u + 64u))
+      return __uint_as_float((yb + 0x7FFFu + ((yb >> 16) & 1u)) & 0xFFFF0000u);
+  }
+  const double gd = g, ud = u;
+  return bf16_round_from_f64(gd / (1.0 + exp(-gd)) * ud);
+}
+
 __device__ __forceinline__ float read_global_scale(const float* g, int dynamic) {
   float v = __builtin_nontemporal_load(g);
   if (!dynamic) return v;
@@ -130,25 +196,7 @@ quantize_kernel(const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t nb, u
   float v[16];
   load_block<DT>(x + (int64_t)row * ldx_bytes + (int64_t)j * 16 * elem_bytes<DT>(), v);
 
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const uint32_t sc = e4m3_encode(amax * gs6);
-  const float sd = e4m3_value(sc);
-  // sd == 0: r = 0 makes every magnitude 0 (finite inputs)
-  const float r = sd > 0.0f ? g / sd : 0.0f;
-
-  uint32_t word[2] = {0u, 0u};
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t code = e2m1_index(fabsf(v[i]) * r) | ((__float_as_uint(v[i]) >> 31) << 3);
-    word[i >> 3] |= code << (4 * (i & 7));
-  }
-  uint2 out;
-  out.x = word[0];
-  out.y = word[1];
-  *reinterpret_cast<uint2*>(codes + (int64_t)b * 8) = out;
-  scales[b] = (uint8_t)sc;
+  encode_block(v, g, gs6, b, codes, scales);
 }
 
 // Tensor-wide max |x| (exact, order-free) into *out as a binary32 bit pattern: for non-negative
@@ -166,6 +214,50 @@ amax_kernel(const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t nb, uint3
     load_block<DT>(x + (int64_t)row * ldx_bytes + (int64_t)j * 16 * elem_bytes<DT>(), v);
 #pragma unroll
     for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0 && m > 0.0f)
+    atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(m));
+}
+
+// Fused SiLU(g) * u -> NVFP4: block b of the activation is formed from blocks b of gate and up
+// (each element rounded once to bfloat16) and encoded exactly like quantize_kernel's blocks.
+template <nvfp4_dtype DT>
+__global__ void __launch_bounds__(kThreads)
+silu_mul_quantize_kernel(const uint8_t* __restrict__ gate, int64_t ldg_bytes,
+                         const uint8_t* __restrict__ up, int64_t ldu_bytes, uint32_t nb,
+                         uint32_t total, const float* __restrict__ gptr, int dynamic,
+                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const uint32_t b = blockIdx.x * kThreads + threadIdx.x;
+  if (b >= total) return;
+  const float g = read_global_scale(gptr, dynamic);
+  const float gs6 = g / 6.0f;
+  const uint32_t row = b / nb;
+  const uint32_t j = b - row * nb;
+  float gv[16], uv[16], v[16];
+  load_block<DT>(gate + (int64_t)row * ldg_bytes + (int64_t)j * 16 * elem_bytes<DT>(), gv);
+  load_block<DT>(up + (int64_t)row * ldu_bytes + (int64_t)j * 16 * elem_bytes<DT>(), uv);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = silu_mul_bf16(gv[i], uv[i]);
+  encode_block(v, g, gs6, b, codes, scales);
+}
+
+// max |SiLU(g) * u| (each element rounded to bfloat16) into *out, as amax_kernel.
+template <nvfp4_dtype DT>
+__global__ void __launch_bounds__(kThreads)
+silu_mul_amax_kernel(const uint8_t* __restrict__ gate, int64_t ldg_bytes,
+                     const uint8_t* __restrict__ up, int64_t ldu_bytes, uint32_t nb,
+                     uint32_t total, float* out) {
+  float m = 0.0f;
+  for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < total; b += gridDim.x * kThreads) {
+    const uint32_t row = b / nb;
+    const uint32_t j = b - row * nb;
+    float gv[16], uv[16];
+    load_block<DT>(gate + (int64_t)row * ldg_bytes + (int64_t)j * 16 * elem_bytes<DT>(), gv);
+    load_block<DT>(up + (int64_t)row * ldu_bytes + (int64_t)j * 16 * elem_bytes<DT>(), uv);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(silu_mul_bf16(gv[i], uv[i])));
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
@@ -205,7 +297,52 @@ hipError_t launch_typed(const void* x, int64_t rows, int64_t cols, int64_t ldx, 
   return hipGetLastError();
 }
 
+template <nvfp4_dtype DT>
+hipError_t launch_silu_typed(const void* gate, const void* up, int64_t rows, int64_t cols,
+                             int64_t ldg, int64_t ldu, float* g, int dynamic, uint8_t* codes,
+                             uint8_t* scales, hipStream_t stream) {
+  const uint32_t nb = (uint32_t)(cols / 16);
+  const uint32_t total = (uint32_t)(rows * (cols / 16));
+  const int64_t ldg_bytes = ldg * elem_bytes<DT>(), ldu_bytes = ldu * elem_bytes<DT>();
+  const uint8_t* gb = reinterpret_cast<const uint8_t*>(gate);
+  const uint8_t* ub = reinterpret_cast<const uint8_t*>(up);
+  if (dynamic) {
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(1), dim3(1), 0, stream, g);
+    if (total > 0) {
+      uint32_t grid = (total + kThreads - 1) / kThreads;
+      grid = grid > 4096u ? 4096u : grid;
+      hipLaunchKernelGGL(silu_mul_amax_kernel<DT>, dim3(grid), dim3(kThreads), 0, stream, gb,
+                         ldg_bytes, ub, ldu_bytes, nb, total, g);
+    }
+  }
+  if (total > 0) {
+    const uint32_t grid = (total + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(silu_mul_quantize_kernel<DT>, dim3(grid), dim3(kThreads), 0, stream, gb,
+                       ldg_bytes, ub, ldu_bytes, nb, total, g, dynamic, codes, scales);
+  }
+  if (dynamic) hipLaunchKernelGGL(finalize_dynamic_scale_kernel, dim3(1), dim3(1), 0, stream, g);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_silu_mul_quantize(const void* gate, const void* up, nvfp4_dtype dt,
+                                    int64_t rows, int64_t cols, int64_t ldg, int64_t ldu,
+                                    float* g, int dynamic, uint8_t* codes, uint8_t* scales,
+                                    hipStream_t stream) {
+  switch (dt) {
+    case NVFP4_F32:
+      return launch_silu_typed<NVFP4_F32>(gate, up, rows, cols, ldg, ldu, g, dynamic, codes,
+                                          scales, stream);
+    case NVFP4_BF16:
+      return launch_silu_typed<NVFP4_BF16>(gate, up, rows, cols, ldg, ldu, g, dynamic, codes,
+                                           scales, stream);
+    case NVFP4_F16:
+      return launch_silu_typed<NVFP4_F16>(gate, up, rows, cols, ldg, ldu, g, dynamic, codes,
+                                          scales, stream);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
                            float* g, int dynamic, uint8_t* codes, uint8_t* scales,

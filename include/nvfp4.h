@@ -92,6 +92,35 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, in
                             uint8_t* scales, void* stream);
 
 /*
+ * nvfp4_silu_mul_quantize -- encode the gated MLP activation a = SiLU(gate) * up to NVFP4 in one
+ * pass, without writing a: the input of the MLP's down projection.
+ *
+ * Source: ai.info summary, "Methodology in Plain English" (all linear layers quantized, 192 of
+ * them MLP projections, so the down projection's input is encoded on the fly like every other
+ * activation).  The pages name no activation function; this entry point takes the reading
+ * SiLU(x) = x / (1 + e^-x) and a bfloat16 activation (the model's type):
+ *
+ *   a = bf16(SiLU(gate) * up)   rounded once, to nearest-even, from the exact real value
+ *   codes, scales = the NVFP4 encoding of a, exactly as nvfp4_quantize encodes a BF16 tensor
+ *
+ * The value is formed in binary32 and, whenever that cannot decide the bfloat16 rounding for
+ * certain (within 64 binary32 ulps of a bfloat16 midpoint, |gate| > 16, zero, subnormal or
+ * non-finite results), in binary64; the result equals the rounding of the exact value except when
+ * the exact value lies within binary64 rounding error of a bfloat16 midpoint.
+ *
+ *   gate, up     device, [rows, cols] of dtype (F32, BF16 or F16), row pitches ld_gate, ld_up
+ *                (elements; >= cols; pitch in bytes a multiple of 16); 16-byte aligned.
+ *   rows, cols   rows >= 0; cols >= 0 and a multiple of 16.
+ *   global_scale, dynamic, codes, scales, stream: as nvfp4_quantize (the dynamic scale is
+ *                2688 / max|a|).
+ * Errors as nvfp4_quantize.
+ */
+nvfp4_status nvfp4_silu_mul_quantize(const void* gate, const void* up, nvfp4_dtype dtype,
+                                     int64_t rows, int64_t cols, int64_t ld_gate, int64_t ld_up,
+                                     float* global_scale, int dynamic, uint8_t* codes,
+                                     uint8_t* scales, void* stream);
+
+/*
  * nvfp4_gemm -- C[m, n] = sum_k a[m,k] * w[n,k] / (gA * gW) for NVFP4 operands; equivalent to
  * fused_nvfp4_gemm with one segment.
  *

@@ -79,6 +79,36 @@ def test_quantize_validation():
     assert _q(cols=0, ldx=16) == nv.NVFP4_OK
 
 
+def _sq(**kw):
+    a = dict(gate=P, up=P + 4096, dt=nv.NVFP4_BF16, rows=4, cols=32, ldg=32, ldu=32, g=P, dyn=0,
+             codes=P, scales=P, s=None)
+    a.update(kw)
+    return nv.load_library().nvfp4_silu_mul_quantize(
+        a["gate"], a["up"], a["dt"], a["rows"], a["cols"], a["ldg"], a["ldu"], a["g"], a["dyn"],
+        a["codes"], a["scales"], a["s"])
+
+
+def test_silu_mul_quantize_validation():
+    assert _sq(gate=None) == nv.NVFP4_EINVAL
+    assert _sq(up=None) == nv.NVFP4_EINVAL
+    assert _sq(g=None) == nv.NVFP4_EINVAL
+    assert _sq(codes=None) == nv.NVFP4_EINVAL
+    assert _sq(scales=None) == nv.NVFP4_EINVAL
+    assert _sq(dt=7) == nv.NVFP4_EINVAL
+    assert _sq(dyn=2) == nv.NVFP4_EINVAL
+    assert _sq(cols=24, ldg=24, ldu=24) == nv.NVFP4_ESHAPE
+    assert _sq(rows=-1) == nv.NVFP4_ESHAPE
+    assert _sq(ldg=16) == nv.NVFP4_ESHAPE
+    assert _sq(ldu=16) == nv.NVFP4_ESHAPE
+    assert _sq(gate=P + 8) == nv.NVFP4_EALIGN
+    assert _sq(up=P + 8) == nv.NVFP4_EALIGN
+    assert _sq(ldu=36) == nv.NVFP4_EALIGN  # 72-byte bf16 row pitch
+    assert _sq(codes=P + 4) == nv.NVFP4_EALIGN
+    assert _sq(rows=1 << 28, cols=1 << 8, ldg=1 << 8, ldu=1 << 8) == nv.NVFP4_ESHAPE
+    assert _sq(rows=0) == nv.NVFP4_OK
+    assert _sq(cols=0, ldg=16, ldu=16) == nv.NVFP4_OK
+
+
 def _g(fused=False, **kw):
     a = dict(ac=P, as_=P, ga=P, wc=P, ws=P, gw=P, M=64, N=96, K=512, c=P, cdt=nv.NVFP4_F32, ldc=96,
              offs=None, nseg=None, s=None)

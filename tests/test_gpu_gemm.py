@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import oracle
-from workloads import WORKLOADS, activations, random_matrix, weights
+from workloads import WORKLOADS, activations, gate_up, random_matrix, weights
 
 from .gpu_util import DEV, check_gemm, log, scalar
 
@@ -202,22 +202,38 @@ def _sampled_full_size(wid, M=None):
     w = WORKLOADS[wid]
     M = w.M if M is None else M
     log(f"workload {wid}: generating A {M}x{w.K}, W {w.N}x{w.K}")
-    a = activations(w, M)
     wt = weights(w)
-    ga = oracle.dynamic_global_scale(a)
     segs = w.seg_offsets
     gw = np.array([oracle.dynamic_global_scale(wt[segs[j]:segs[j + 1]])
                    for j in range(len(segs) - 1)], np.float32)
-    ad = to_device(a, w.act_dtype)
     wd = to_device(wt, w.w_dtype)
     log(f"workload {wid}: encode on GPU")
-    ac_d, as_d, _ = nv.nvfp4_quantize(ad, scalar(ga))
+    if w.silu_mul:
+        # the activation is SiLU(g) * u, encoded by the fused encoder with its dynamic scale
+        g, u = gate_up(w, M)
+        gd, ud = to_device(g, w.act_dtype), to_device(u, w.act_dtype)
+        ac_d, as_d, ga_d = nv.nvfp4_silu_mul_quantize(gd, ud)
+        torch.cuda.synchronize()
+        ga = np.float32(ga_d.item())
+        del gd, ud
+
+        def encode_rows(rows):
+            return oracle.silu_mul_quantize(g[rows], u[rows], ga)[:2]
+    else:
+        a = activations(w, M)
+        ga = oracle.dynamic_global_scale(a)
+        ad = to_device(a, w.act_dtype)
+        ac_d, as_d, _ = nv.nvfp4_quantize(ad, scalar(ga))
+        del ad
+
+        def encode_rows(rows):
+            return oracle.quantize(a[rows], ga)[:2]
     wc_d = torch.empty((w.N, w.K // 2), dtype=torch.uint8, device=DEV)
     ws_d = torch.empty((w.N, w.K // 16), dtype=torch.uint8, device=DEV)
     for j in range(len(segs) - 1):
         nv.nvfp4_quantize(wd[segs[j]:segs[j + 1]], scalar(gw[j]), wc_d[segs[j]:segs[j + 1]],
                           ws_d[segs[j]:segs[j + 1]])
-    del ad, wd
+    del wd
     log(f"workload {wid}: product on GPU")
     C = nv.fused_nvfp4_gemm(ac_d, as_d, scalar(ga), wc_d, ws_d, _up(gw), segs)
     torch.cuda.synchronize()
@@ -231,7 +247,7 @@ def _sampled_full_size(wid, M=None):
                                 replace=False))
     cols = np.unique(np.array(cols))
     log(f"workload {wid}: oracle on {len(rows)} rows x {len(cols)} cols")
-    ac, as_, _ = oracle.quantize(a[rows], ga)
+    ac, as_ = encode_rows(rows)
     assert np.array_equal(ac, ac_d[rows].cpu().numpy()) and np.array_equal(as_, as_d[rows].cpu().numpy())
     seg_of = np.searchsorted(segs, cols, side="right") - 1
     wc = np.zeros((len(cols), w.K // 2), np.uint8)
@@ -251,7 +267,7 @@ def _sampled_full_size(wid, M=None):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("wid", [2, 3])
+@pytest.mark.parametrize("wid", [2, 3, 5])
 def test_full_size_sampled(wid):
     _sampled_full_size(wid)
 
