@@ -26,3 +26,4 @@ from .nvfp4_oracle import (  # noqa: F401
     unpack_codes,
 )
 from .activation import round_to_bf16, silu, silu_mul_activation, silu_mul_quantize  # noqa: F401
+from .kv_cache import kv_calibrated_scale, kv_fp8_decode, kv_fp8_encode  # noqa: F401
