@@ -198,6 +198,49 @@ def silu_quantize(args, torch, nv, W):
             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": nbytes}
 
 
+def kv_store(args, torch, nv, W):
+    """The FP8 KV-cache store on a 32768-token prefill: keys and values [32768, 1024] bf16 encoded
+    under static per-tensor scales (amax / 448 of an independent calibration sample, computed
+    before timing) and scattered into a shuffled paged cache of 65536 slots.  Timed over `steps`
+    launches back to back between HIP events, rotating over 3 copies of inputs and caches (605 MB,
+    beyond the 256 MB last-level cache); bytes = bf16 keys + values read, the slot mapping read,
+    the FP8 rows written."""
+    import numpy as np
+
+    w = W.KV_WORKLOADS[6]
+    dev = "cuda:0"
+    log(f"[bench] generating {w.name}")
+    k, v = W.kv_tokens(w)
+    kcal, vcal = W.kv_tokens(w, 4096, calibration=True)
+    ks = torch.tensor([np.float32(np.abs(kcal).max()) / np.float32(448.0)], device=dev)
+    vs = torch.tensor([np.float32(np.abs(vcal).max()) / np.float32(448.0)], device=dev)
+    kd = torch.from_numpy(k).to(torch.bfloat16).to(dev)
+    vd = torch.from_numpy(v).to(torch.bfloat16).to(dev)
+    slots = torch.from_numpy(W.kv_slot_mapping(w)).to(dev)
+    R = 3
+    sets = []
+    for _ in range(R):
+        kc = torch.zeros((w.num_slots, w.width), dtype=torch.uint8, device=dev)
+        sets.append((kd.clone(), vd.clone(), kc, torch.zeros_like(kc), slots.clone()))
+    del k, v, kcal, vcal, kd, vd
+    for i in range(args.warmup):
+        nv.nvfp4_kv_fp8_store(sets[i % R][0], sets[i % R][1], ks, vs, *sets[i % R][2:])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        nv.nvfp4_kv_fp8_store(sets[i % R][0], sets[i % R][1], ks, vs, *sets[i % R][2:])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = 2 * w.tokens * w.width * (2 + 1) + w.tokens * 8
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del sets, slots
+    torch.cuda.empty_cache()
+    return {"bound": "hbm", "tokens": w.tokens, "width": w.width, "us": round(ms * 1e3, 3),
+            "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": nbytes}
+
+
 def copy_calibration(args, torch):
     """A plain device-to-device copy of 1 GiB, the reference for scaling HBM byte counters:
     it reads and writes exactly 2^30 bytes per launch."""
@@ -275,7 +318,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--only", choices=("all", "prefill", "decode", "silu", "copy"), default="all",
+    ap.add_argument("--only", choices=("all", "prefill", "decode", "silu", "kv", "copy"),
+                    default="all",
                     help="run one part (for profiler runs); 'copy' is the counter calibration copy")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -303,11 +347,15 @@ def main():
     if args.only == "silu":
         print(json.dumps({"silu_mul_quantize": silu_quantize(args, torch, nv, W)}), flush=True)
         return
+    if args.only == "kv":
+        print(json.dumps({"kv_fp8_store": kv_store(args, torch, nv, W)}), flush=True)
+        return
 
     p = prefill(args, torch, nv, W)
     run_rest = args.only == "all"
     dec = decode(args, torch, nv, W) if run_rest and not args.no_decode else None
     silu = silu_quantize(args, torch, nv, W) if run_rest else None
+    kv = kv_store(args, torch, nv, W) if run_rest else None
     cpu = cpu_baseline() if run_rest and not args.no_cpu_baseline else None
 
     w = p["w"]
@@ -341,6 +389,7 @@ def main():
                      "frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4), "bytes": int(p["q_bytes"])},
         "decode": dec,
         "silu_mul_quantize": silu,
+        "kv_fp8_store": kv,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -12,6 +12,8 @@ Entry points (same names as the C ABI):
 * ``nvfp4_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, out_dtype)`` -> ``C``
 * ``fused_nvfp4_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_gscale, seg_offsets,
   out_dtype)`` -> ``C``
+* ``nvfp4_kv_fp8_store(key, value, key_scale, value_scale, key_cache, value_cache, slot_mapping)``
+* ``nvfp4_kv_fp8_load(cache, scale, slot_mapping, out_dtype)`` -> decoded rows
 """
 
 from __future__ import annotations
@@ -28,7 +30,8 @@ NVFP4_MAX_SEGMENTS = 16
 
 #: every symbol include/nvfp4.h declares
 EXPORTED_SYMBOLS = ("nvfp4_quantize", "nvfp4_silu_mul_quantize", "nvfp4_gemm", "fused_nvfp4_gemm",
-                    "nvfp4_status_string", "nvfp4_version")
+                    "nvfp4_kv_fp8_store", "nvfp4_kv_fp8_load", "nvfp4_status_string",
+                    "nvfp4_version")
 
 _lib = None
 
@@ -56,6 +59,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.nvfp4_silu_mul_quantize.argtypes = [c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_i64, c_vp,
                                             c_int, c_vp, c_vp, c_vp]
     lib.nvfp4_silu_mul_quantize.restype = c_int
+    lib.nvfp4_kv_fp8_store.argtypes = [c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp,
+                                       c_vp, c_vp, c_vp, c_i64, c_i64, c_vp]
+    lib.nvfp4_kv_fp8_store.restype = c_int
+    lib.nvfp4_kv_fp8_load.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_int,
+                                      c_i64, c_vp]
+    lib.nvfp4_kv_fp8_load.restype = c_int
     lib.nvfp4_gemm.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_int,
                                c_i64, c_vp]
     lib.nvfp4_gemm.restype = c_int
@@ -212,4 +221,65 @@ def fused_nvfp4_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_gscale,
     _check(lib.fused_nvfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(a_gscale), _ptr(w_codes),
                                 _ptr(w_scales), _ptr(seg_gscale), arr, nseg, M, N, K, _ptr(out),
                                 _dtype_code(out.dtype), out.stride(0), _stream(a_codes.device)))
+    return out
+
+
+def nvfp4_kv_fp8_store(key, value, key_scale, value_scale, key_cache, value_cache,
+                       slot_mapping=None):
+    """Encode ``key`` (and ``value``, or None) ``[tokens, width]`` to FP8 E4M3 under the static
+    decode-direction scales (1-element float32 device tensors) and write token t's row into row
+    ``slot_mapping[t]`` (int64 device tensor, or None for row t) of the uint8 caches
+    ``[num_slots, width]`` (``value_cache`` None with ``value``).  Slots outside the cache are
+    skipped."""
+    lib = load_library()
+    if key.dim() != 2 or key.stride(1) != 1:
+        raise ValueError("key must be 2-D with contiguous rows")
+    tokens, width = key.shape
+    ts = [key, key_scale, key_cache]
+    if value is not None:
+        if value.shape != key.shape or value.dtype != key.dtype or value.stride(1) != 1:
+            raise ValueError("value must match key's shape and dtype, with contiguous rows")
+        ts += [value, value_scale, value_cache]
+    if slot_mapping is not None:
+        ts.append(slot_mapping)
+        if slot_mapping.dtype.itemsize != 8 or slot_mapping.numel() != tokens:
+            raise ValueError("slot_mapping must hold one int64 per token")
+    _require_cuda(*ts)
+    if key_cache.dim() != 2 or key_cache.stride(1) != 1 or key_cache.shape[1] < width:
+        raise ValueError("key_cache must be 2-D [num_slots, >= width] with contiguous rows")
+    if value_cache is not None and (value_cache.shape != key_cache.shape or
+                                    value_cache.stride() != key_cache.stride()):
+        raise ValueError("value_cache must have key_cache's shape and strides")
+    if tokens == 0 or width == 0:
+        return  # torch gives empty tensors a null data pointer; the library has nothing to do
+    _check(lib.nvfp4_kv_fp8_store(_ptr(key), _ptr(value), _dtype_code(key.dtype), tokens, width,
+                                  key.stride(0), value.stride(0) if value is not None else 0,
+                                  _ptr(key_scale), _ptr(value_scale), _ptr(slot_mapping),
+                                  _ptr(key_cache), _ptr(value_cache), key_cache.shape[0],
+                                  key_cache.stride(0), _stream(key.device)))
+
+
+def nvfp4_kv_fp8_load(cache, scale, slot_mapping=None, out_dtype=None, width=None, out=None):
+    """Gather rows ``slot_mapping[t]`` (int64 device tensor; None: every row in order) of the FP8
+    cache ``[num_slots, >= width]`` and decode them with ``scale``; returns ``[tokens, width]``
+    float32 or bfloat16.  Slots outside the cache give rows of zeros."""
+    torch = _torch()
+    lib = load_library()
+    if cache.dim() != 2 or cache.stride(1) != 1:
+        raise ValueError("cache must be 2-D with contiguous rows")
+    width = cache.shape[1] if width is None else int(width)
+    tokens = cache.shape[0] if slot_mapping is None else slot_mapping.numel()
+    ts = [cache, scale]
+    if slot_mapping is not None:
+        ts.append(slot_mapping)
+        if slot_mapping.dtype.itemsize != 8:
+            raise ValueError("slot_mapping must be int64")
+    _require_cuda(*ts)
+    if out is None:
+        out = _out(tokens, width, out_dtype or torch.float32, cache.device)
+    if tokens == 0 or width == 0:
+        return out  # torch gives empty tensors a null data pointer; the library has nothing to do
+    _check(lib.nvfp4_kv_fp8_load(_ptr(cache), cache.shape[0], cache.stride(0), width, _ptr(scale),
+                                 _ptr(slot_mapping), tokens, _ptr(out), _dtype_code(out.dtype),
+                                 out.stride(0), _stream(cache.device)))
     return out

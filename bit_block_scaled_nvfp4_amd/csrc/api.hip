@@ -16,6 +16,10 @@ bool valid_out_dtype(int d) { return d == NVFP4_F32 || d == NVFP4_BF16; }
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 
+// Largest extent (elements) a tensor may span from its base pointer, and the widest KV row.
+constexpr int64_t kMaxSpan = int64_t(1) << 40;
+constexpr int64_t kMaxKvWidth = int64_t(1) << 24;
+
 nvfp4_status device_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_EDEVICE; }
 
 // Validation shared by nvfp4_gemm and fused_nvfp4_gemm.
@@ -125,6 +129,63 @@ nvfp4_status nvfp4_silu_mul_quantize(const void* gate, const void* up, nvfp4_dty
   hipError_t e = nvfp4::launch_silu_mul_quantize(gate, up, dtype, rows, cols, ld_gate, ld_up,
                                                  global_scale, dynamic, codes, scales,
                                                  reinterpret_cast<hipStream_t>(stream));
+  return device_status(e);
+}
+
+nvfp4_status nvfp4_kv_fp8_store(const void* key, const void* value, nvfp4_dtype dtype,
+                                int64_t tokens, int64_t width, int64_t ld_key, int64_t ld_value,
+                                const float* key_scale, const float* value_scale,
+                                const int64_t* slot_mapping, uint8_t* key_cache,
+                                uint8_t* value_cache, int64_t num_slots, int64_t cache_ld,
+                                void* stream) {
+  if (!key || !key_scale || !key_cache) return NVFP4_EINVAL;
+  // the value tensor is optional, but then all three of its arguments are absent
+  if ((value != nullptr) != (value_scale != nullptr) || (value != nullptr) != (value_cache != nullptr))
+    return NVFP4_EINVAL;
+  if (!valid_in_dtype(dtype)) return NVFP4_EINVAL;
+  if (tokens < 0 || width < 0 || width % 16 != 0 || num_slots < 0) return NVFP4_ESHAPE;
+  if (tokens > kMaxDim || width > kMaxKvWidth) return NVFP4_ESHAPE;
+  if (ld_key < width || ld_key < 1 || cache_ld < width || cache_ld < 1) return NVFP4_ESHAPE;
+  if (value && (ld_value < width || ld_value < 1)) return NVFP4_ESHAPE;
+  if (tokens > 0 && ((tokens - 1) * ld_key + width > kMaxSpan ||
+                     (value && (tokens - 1) * ld_value + width > kMaxSpan)))
+    return NVFP4_ESHAPE;
+  if (num_slots > 0 && (num_slots - 1) * cache_ld + width > kMaxSpan) return NVFP4_ESHAPE;
+  const int64_t eb = dtype_bytes(dtype);
+  if (!aligned(key, 16) || (ld_key * eb) % 16 != 0 || !aligned(key_cache, 16) ||
+      cache_ld % 16 != 0 || !aligned(key_scale, 4))
+    return NVFP4_EALIGN;
+  if (value && (!aligned(value, 16) || (ld_value * eb) % 16 != 0 || !aligned(value_cache, 16) ||
+                !aligned(value_scale, 4)))
+    return NVFP4_EALIGN;
+  if (slot_mapping && !aligned(slot_mapping, 8)) return NVFP4_EALIGN;
+  if (tokens == 0 || width == 0) return NVFP4_OK;
+  hipError_t e = nvfp4::launch_kv_store(key, value, dtype, tokens, width, ld_key, ld_value,
+                                        key_scale, value_scale, slot_mapping, key_cache,
+                                        value_cache, num_slots, cache_ld,
+                                        reinterpret_cast<hipStream_t>(stream));
+  return device_status(e);
+}
+
+nvfp4_status nvfp4_kv_fp8_load(const uint8_t* cache, int64_t num_slots, int64_t cache_ld,
+                               int64_t width, const float* scale, const int64_t* slot_mapping,
+                               int64_t tokens, void* out, nvfp4_dtype out_dtype, int64_t ld_out,
+                               void* stream) {
+  if (!cache || !scale || !out) return NVFP4_EINVAL;
+  if (!valid_out_dtype(out_dtype)) return NVFP4_EINVAL;
+  if (tokens < 0 || width < 0 || width % 16 != 0 || num_slots < 0) return NVFP4_ESHAPE;
+  if (tokens > kMaxDim || width > kMaxKvWidth) return NVFP4_ESHAPE;
+  if (cache_ld < width || cache_ld < 1 || ld_out < width || ld_out < 1) return NVFP4_ESHAPE;
+  if (tokens > 0 && (tokens - 1) * ld_out + width > kMaxSpan) return NVFP4_ESHAPE;
+  if (num_slots > 0 && (num_slots - 1) * cache_ld + width > kMaxSpan) return NVFP4_ESHAPE;
+  if (!aligned(cache, 16) || cache_ld % 16 != 0 || !aligned(out, 16) ||
+      (ld_out * dtype_bytes(out_dtype)) % 16 != 0 || !aligned(scale, 4))
+    return NVFP4_EALIGN;
+  if (slot_mapping && !aligned(slot_mapping, 8)) return NVFP4_EALIGN;
+  if (tokens == 0 || width == 0) return NVFP4_OK;
+  hipError_t e = nvfp4::launch_kv_load(cache, num_slots, cache_ld, width, scale, slot_mapping,
+                                       tokens, out, out_dtype, ld_out,
+                                       reinterpret_cast<hipStream_t>(stream));
   return device_status(e);
 }
 

@@ -1,0 +1,256 @@
+// FP8 E4M3 KV cache for gfx950: new tokens' keys and values are encoded under one static
+// (calibrated) scale per tensor and scattered into cache rows; the reverse gathers and decodes.
+//
+// Source: "Why Gated DeltaNet Survives 4-Bit Quantization" (arXiv 2609.04098), ai.info summary,
+// "Key Contributions" (an FP8 KV cache with calibrated per-layer scales) and "Main Findings" (static
+// per-tensor FP8 scales, one for each K and V tensor of the attention layers).  The encoding rules
+// the pages leave open are stated in include/nvfp4.h: decode-direction scale, y = fl(x * fl(1/s)),
+// E4M3 nearest-even saturating at 448, sign copied.
+//
+// The encode uses the CDNA4 conversion v_cvt_pk_fp8_f32 (OCP E4M3, round to nearest even,
+// subnormals kept) on y clamped to [-448, 448] first, so nothing can overflow to NaN; the decode
+// uses v_cvt_pk_f32_fp8, which is exact.
+//
+// Work split: a thread owns 16 consecutive elements of one token's row (32 bytes of bf16/f16 or
+// 64 bytes of f32 in, 16 code bytes out).  A row of width/16 chunks is served by the L lanes of a
+// wave (L the power of two >= width/16, at most 64), so a wave covers 64/L whole tokens when rows are
+// short and a 64-chunk stretch of one token when they are long; loads and stores of a wave are
+// contiguous per token.  The kernels are bound by HBM bandwidth (3 bytes moved per bf16 element).
+#include "nvfp4_internal.h"
+
+namespace nvfp4 {
+namespace {
+
+constexpr int kThreads = 256;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <nvfp4_dtype DT>
+__device__ __forceinline__ void load16(const uint8_t* p, float (&v)[16]) {
+  if constexpr (DT == NVFP4_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 q = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + i);
+      v[4 * i + 0] = q.x;
+      v[4 * i + 1] = q.y;
+      v[4 * i + 2] = q.z;
+      v[4 * i + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + i);
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (DT == NVFP4_BF16) {
+          v[8 * i + 2 * j + 0] = __uint_as_float(w[j] << 16);
+          v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+        } else {
+          v[8 * i + 2 * j + 0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[j] & 0xFFFFu));
+          v[8 * i + 2 * j + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[j] >> 16));
+        }
+      }
+    }
+  }
+}
+
+struct KvStoreArgs {
+  const uint8_t* src[2];  // key, value rows (bytes)
+  int64_t ld_src[2];      // row pitch in bytes
+  const float* scale[2];
+  uint8_t* cache[2];
+  const int64_t* slots;   // nullptr: token t -> slot t
+  int64_t cache_ld;       // bytes
+  int64_t num_slots;
+  int32_t tokens;
+  int32_t chunks;         // width / 16
+  int32_t lane_bits;      // log2 of lanes per token
+};
+
+// Slot of token t, or -1 when the token is not stored (outside [0, num_slots)).
+__device__ __forceinline__ int64_t slot_of(const int64_t* slots, int64_t num_slots, int32_t t) {
+  const int64_t s = slots ? slots[t] : (int64_t)t;
+  return (s >= 0 && s < num_slots) ? s : -1;
+}
+
+// grid: x over groups of 256 >> lane_bits tokens, y over stretches of (1 << lane_bits) chunks,
+// z over the tensors (1: key only, 2: key and value).
+template <nvfp4_dtype DT>
+__global__ void __launch_bounds__(kThreads) kv_store_kernel(KvStoreArgs a) {
+  const int z = blockIdx.z;
+  const int lb = a.lane_bits;
+  const int32_t t = (int32_t)(blockIdx.x * (kThreads >> lb)) + (int32_t)(threadIdx.x >> lb);
+  const int32_t c = (int32_t)(blockIdx.y << lb) + (int32_t)(threadIdx.x & ((1u << lb) - 1));
+  if (t >= a.tokens || c >= a.chunks) return;
+  // the row is loaded before the slot is known, so both loads are in flight together
+  constexpr int kEb = DT == NVFP4_F32 ? 4 : 2;
+  float v[16];
+  load16<DT>(a.src[z] + (int64_t)t * a.ld_src[z] + (int64_t)c * 16 * kEb, v);
+  const int64_t slot = slot_of(a.slots, a.num_slots, t);
+  const float inv = 1.0f / *a.scale[z];  // correctly rounded (built with IEEE division)
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float y[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[j] = __builtin_fminf(__builtin_fmaxf(v[4 * i + j] * inv, -448.0f), 448.0f);
+    int p = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    p = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], p, true);
+    w[i] = (uint32_t)p;
+  }
+  if (slot < 0) return;
+  u32x4 o;
+  o.x = w[0];
+  o.y = w[1];
+  o.z = w[2];
+  o.w = w[3];
+  __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(a.cache[z] + slot * a.cache_ld + (int64_t)c * 16));
+}
+
+struct KvLoadArgs {
+  const uint8_t* cache;
+  int64_t cache_ld;  // bytes
+  int64_t num_slots;
+  const float* scale;
+  const int64_t* slots;
+  uint8_t* out;
+  int64_t ld_out;    // bytes
+  int32_t tokens;
+  int32_t chunks;
+  int32_t lane_bits;
+};
+
+__device__ __forceinline__ uint32_t bf16_pair_rne(float lo, float hi) {
+  // nearest-even rounding of finite binary32 values to bfloat16, two per word
+  const uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
+  const uint32_t ra = (a + 0x7FFFu + ((a >> 16) & 1u)) >> 16;
+  const uint32_t rb = (b + 0x7FFFu + ((b >> 16) & 1u)) & 0xFFFF0000u;
+  return ra | rb;
+}
+
+template <bool BF16_OUT>
+__global__ void __launch_bounds__(kThreads) kv_load_kernel(KvLoadArgs a) {
+  const int lb = a.lane_bits;
+  const int32_t t = (int32_t)(blockIdx.x * (kThreads >> lb)) + (int32_t)(threadIdx.x >> lb);
+  const int32_t c = (int32_t)(blockIdx.y << lb) + (int32_t)(threadIdx.x & ((1u << lb) - 1));
+  if (t >= a.tokens || c >= a.chunks) return;
+  const int64_t slot = slot_of(a.slots, a.num_slots, t);
+  float v[16];
+  if (slot >= 0) {
+    const u32x4 q = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(a.cache + slot * a.cache_ld + (int64_t)c * 16));
+    const float s = *a.scale;
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+      v[4 * i + 0] = lo[0] * s;
+      v[4 * i + 1] = lo[1] * s;
+      v[4 * i + 2] = hi[0] * s;
+      v[4 * i + 3] = hi[1] * s;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+  }
+  uint8_t* dst = a.out + (int64_t)t * a.ld_out;
+  if constexpr (BF16_OUT) {
+    u32x4* d = reinterpret_cast<u32x4*>(dst + (int64_t)c * 32);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      u32x4 o;
+      o.x = bf16_pair_rne(v[8 * i + 0], v[8 * i + 1]);
+      o.y = bf16_pair_rne(v[8 * i + 2], v[8 * i + 3]);
+      o.z = bf16_pair_rne(v[8 * i + 4], v[8 * i + 5]);
+      o.w = bf16_pair_rne(v[8 * i + 6], v[8 * i + 7]);
+      __builtin_nontemporal_store(o, d + i);
+    }
+  } else {
+    f32x4* d = reinterpret_cast<f32x4*>(dst + (int64_t)c * 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4 o;
+      o.x = v[4 * i + 0];
+      o.y = v[4 * i + 1];
+      o.z = v[4 * i + 2];
+      o.w = v[4 * i + 3];
+      __builtin_nontemporal_store(o, d + i);
+    }
+  }
+}
+
+// Lanes per token: the power of two >= chunks, at most 64 (a wavefront).
+int lane_bits_for(int64_t chunks) {
+  int lb = 0;
+  while (lb < 6 && (int64_t(1) << lb) < chunks) ++lb;
+  return lb;
+}
+
+}  // namespace
+
+hipError_t launch_kv_store(const void* key, const void* value, nvfp4_dtype dt, int64_t tokens,
+                           int64_t width, int64_t ld_key, int64_t ld_value, const float* key_scale,
+                           const float* value_scale, const int64_t* slots, uint8_t* key_cache,
+                           uint8_t* value_cache, int64_t num_slots, int64_t cache_ld,
+                           hipStream_t stream) {
+  const int64_t eb = dt == NVFP4_F32 ? 4 : 2;
+  KvStoreArgs a{};
+  a.src[0] = static_cast<const uint8_t*>(key);
+  a.src[1] = static_cast<const uint8_t*>(value);
+  a.ld_src[0] = ld_key * eb;
+  a.ld_src[1] = ld_value * eb;
+  a.scale[0] = key_scale;
+  a.scale[1] = value_scale;
+  a.cache[0] = key_cache;
+  a.cache[1] = value_cache;
+  a.slots = slots;
+  a.cache_ld = cache_ld;
+  a.num_slots = num_slots;
+  a.tokens = (int32_t)tokens;
+  a.chunks = (int32_t)(width / 16);
+  a.lane_bits = lane_bits_for(a.chunks);
+  const int64_t tok_per_block = kThreads >> a.lane_bits;
+  const dim3 grid((uint32_t)((tokens + tok_per_block - 1) / tok_per_block),
+                  (uint32_t)((a.chunks + (1 << a.lane_bits) - 1) >> a.lane_bits), value ? 2u : 1u);
+  switch (dt) {
+    case NVFP4_F32:
+      hipLaunchKernelGGL(kv_store_kernel<NVFP4_F32>, grid, dim3(kThreads), 0, stream, a);
+      break;
+    case NVFP4_BF16:
+      hipLaunchKernelGGL(kv_store_kernel<NVFP4_BF16>, grid, dim3(kThreads), 0, stream, a);
+      break;
+    default:
+      hipLaunchKernelGGL(kv_store_kernel<NVFP4_F16>, grid, dim3(kThreads), 0, stream, a);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_load(const uint8_t* cache, int64_t num_slots, int64_t cache_ld,
+                          int64_t width, const float* scale, const int64_t* slots, int64_t tokens,
+                          void* out, nvfp4_dtype out_dt, int64_t ld_out, hipStream_t stream) {
+  KvLoadArgs a{};
+  a.cache = cache;
+  a.cache_ld = cache_ld;
+  a.num_slots = num_slots;
+  a.scale = scale;
+  a.slots = slots;
+  a.out = static_cast<uint8_t*>(out);
+  a.ld_out = ld_out * (out_dt == NVFP4_F32 ? 4 : 2);
+  a.tokens = (int32_t)tokens;
+  a.chunks = (int32_t)(width / 16);
+  a.lane_bits = lane_bits_for(a.chunks);
+  const int64_t tok_per_block = kThreads >> a.lane_bits;
+  const dim3 grid((uint32_t)((tokens + tok_per_block - 1) / tok_per_block),
+                  (uint32_t)((a.chunks + (1 << a.lane_bits) - 1) >> a.lane_bits), 1u);
+  if (out_dt == NVFP4_BF16)
+    hipLaunchKernelGGL(kv_load_kernel<true>, grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(kv_load_kernel<false>, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

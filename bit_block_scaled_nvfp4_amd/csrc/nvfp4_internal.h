@@ -37,6 +37,14 @@ hipError_t launch_silu_mul_quantize(const void* gate, const void* up, nvfp4_dtyp
                                     int64_t rows, int64_t cols, int64_t ldg, int64_t ldu,
                                     float* g, int dynamic, uint8_t* codes, uint8_t* scales,
                                     hipStream_t stream);
+hipError_t launch_kv_store(const void* key, const void* value, nvfp4_dtype dt, int64_t tokens,
+                           int64_t width, int64_t ld_key, int64_t ld_value, const float* key_scale,
+                           const float* value_scale, const int64_t* slots, uint8_t* key_cache,
+                           uint8_t* value_cache, int64_t num_slots, int64_t cache_ld,
+                           hipStream_t stream);
+hipError_t launch_kv_load(const uint8_t* cache, int64_t num_slots, int64_t cache_ld,
+                          int64_t width, const float* scale, const int64_t* slots, int64_t tokens,
+                          void* out, nvfp4_dtype out_dt, int64_t ld_out, hipStream_t stream);
 hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_general(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);

@@ -167,6 +167,61 @@ nvfp4_status fused_nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                               const int64_t* seg_offsets, int nseg, int64_t M, int64_t N,
                               int64_t K, void* c, nvfp4_dtype c_dtype, int64_t ldc, void* stream);
 
+/*
+ * nvfp4_kv_fp8_store -- encode new tokens' keys (and values) to FP8 E4M3 under one static scale per
+ * tensor and write each token's row into its cache slot.
+ *
+ * Source: ai.info summary, "Key Contributions" (an FP8 KV cache with calibrated per-layer scales
+ * that cost nothing at serving time) and "Main Findings" (static per-tensor FP8 scales: one for the
+ * K and one for the V tensor of each of the 16 attention layers).  The pages fix the format and the
+ * granularity; the rules below are this library's reading:
+ *   - the scale is decode-direction: code c stands for E4M3(c) * scale; an uncalibrated FP8 cache
+ *     is scale 1, a calibrated one amax / 448 of calibration data;
+ *   - code = sign(y) << 7 | E4M3(|y|), y = fl(x * fl(1 / scale)) in binary32; E4M3 nearest with
+ *     ties to the even code, |y| >= 448 saturates to 0x7E, subnormal codes kept; the sign bit is
+ *     copied, so -0.0 and negatives that round to zero give 0x80.  Codes are bit-exact.
+ *
+ *   key, value    device, [tokens, width] of dtype (F32, BF16 or F16), row pitches ld_key,
+ *                 ld_value (elements, >= width, a multiple of 16 bytes); 16-byte aligned.  value
+ *                 may be NULL (keys only); then value_scale and value_cache are NULL as well.
+ *   tokens, width tokens >= 0; width >= 0, a multiple of 16, at most 2^24.
+ *   key_scale, value_scale  device, one float each, positive and finite (not checked).
+ *   slot_mapping  device, tokens int64 (8-byte aligned), or NULL for slot t = token t.  Token t's
+ *                 row goes to cache row slot_mapping[t]; a slot outside [0, num_slots) -- e.g. -1
+ *                 for a padding token -- is skipped.  Two tokens with one slot race.
+ *   key_cache, value_cache  device, [num_slots, width] bytes with row pitch cache_ld (bytes,
+ *                 >= width, a multiple of 16); 16-byte aligned.  A paged cache
+ *                 [blocks, block_size, heads, head_dim] is this table with width = heads*head_dim
+ *                 and slot = block * block_size + position in block.
+ * Errors as nvfp4_quantize; EINVAL also when only some of value/value_scale/value_cache are NULL.
+ */
+nvfp4_status nvfp4_kv_fp8_store(const void* key, const void* value, nvfp4_dtype dtype,
+                                int64_t tokens, int64_t width, int64_t ld_key, int64_t ld_value,
+                                const float* key_scale, const float* value_scale,
+                                const int64_t* slot_mapping, uint8_t* key_cache,
+                                uint8_t* value_cache, int64_t num_slots, int64_t cache_ld,
+                                void* stream);
+
+/*
+ * nvfp4_kv_fp8_load -- gather cache rows and decode them: out[t, i] = fl(E4M3(cache[slot_t, i]) *
+ * scale) in binary32, rounded once to BF16 (nearest-even) when out_dtype is BF16.  The inverse of
+ * nvfp4_kv_fp8_store for one tensor (the FP8 cache as attention reads it).
+ *
+ * Source: as nvfp4_kv_fp8_store.
+ *
+ *   cache         device, [num_slots, width] bytes, row pitch cache_ld (bytes, a multiple of 16).
+ *   scale         device, one float (the tensor's decode-direction scale).
+ *   slot_mapping  device int64[tokens] or NULL (slot t); a slot outside [0, num_slots) gives a
+ *                 row of zeros.
+ *   out           device, [tokens, width] of out_dtype (F32 or BF16), row pitch ld_out (elements,
+ *                 a multiple of 16 bytes); 16-byte aligned.
+ * Errors as nvfp4_kv_fp8_store.
+ */
+nvfp4_status nvfp4_kv_fp8_load(const uint8_t* cache, int64_t num_slots, int64_t cache_ld,
+                               int64_t width, const float* scale, const int64_t* slot_mapping,
+                               int64_t tokens, void* out, nvfp4_dtype out_dtype, int64_t ld_out,
+                               void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* nvfp4_status_string(nvfp4_status s);
 

@@ -17,8 +17,24 @@ import bit_block_scaled_nvfp4_amd as nv
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "nvfp4.h")
 
-pytestmark = pytest.mark.skipif(not os.path.exists(nv.LIB_PATH),
-                                reason="libnvfp4.so not built (run __graft_entry__.build())")
+
+
+def _gpu_visible() -> bool:
+    try:
+        import torch
+
+        return torch.cuda.device_count() > 0
+    except Exception:  # pragma: no cover
+        return False
+
+
+# The calls below pass fake device addresses; should a check ever let one through, it must not
+# reach a real GPU, so on a machine with one these host-only tests do not run.
+pytestmark = [
+    pytest.mark.skipif(not os.path.exists(nv.LIB_PATH),
+                       reason="libnvfp4.so not built (run __graft_entry__.build())"),
+    pytest.mark.skipif(_gpu_visible(), reason="host-only checks with fake device addresses"),
+]
 
 P = 0x10000  # a fake, 256-byte aligned device address (never dereferenced here)
 
@@ -157,3 +173,66 @@ def test_binding_refuses_cpu_tensors():
 
     with pytest.raises(ValueError):
         nv.nvfp4_quantize(torch.zeros(4, 32))
+
+
+def _kvs(**kw):
+    a = dict(k=P, v=P + 4096, dt=nv.NVFP4_BF16, tokens=4, width=32, ldk=32, ldv=32, ks=P, vs=P,
+             slots=P, kc=P, vc=P, num_slots=8, cache_ld=32, s=None)
+    a.update(kw)
+    return nv.load_library().nvfp4_kv_fp8_store(
+        a["k"], a["v"], a["dt"], a["tokens"], a["width"], a["ldk"], a["ldv"], a["ks"], a["vs"],
+        a["slots"], a["kc"], a["vc"], a["num_slots"], a["cache_ld"], a["s"])
+
+
+def test_kv_store_validation():
+    assert _kvs(k=None) == nv.NVFP4_EINVAL
+    assert _kvs(ks=None) == nv.NVFP4_EINVAL
+    assert _kvs(kc=None) == nv.NVFP4_EINVAL
+    assert _kvs(v=None) == nv.NVFP4_EINVAL  # value scale and cache given without values
+    assert _kvs(vc=None) == nv.NVFP4_EINVAL
+    assert _kvs(vs=None) == nv.NVFP4_EINVAL
+    assert _kvs(dt=7) == nv.NVFP4_EINVAL
+    assert _kvs(width=24, ldk=24, ldv=24, cache_ld=32) == nv.NVFP4_ESHAPE
+    assert _kvs(tokens=-1) == nv.NVFP4_ESHAPE
+    assert _kvs(num_slots=-1) == nv.NVFP4_ESHAPE
+    assert _kvs(ldk=16) == nv.NVFP4_ESHAPE
+    assert _kvs(ldv=16) == nv.NVFP4_ESHAPE
+    assert _kvs(cache_ld=16) == nv.NVFP4_ESHAPE
+    assert _kvs(width=1 << 25, ldk=1 << 25, ldv=1 << 25, cache_ld=1 << 25) == nv.NVFP4_ESHAPE
+    assert _kvs(k=P + 8) == nv.NVFP4_EALIGN
+    assert _kvs(v=P + 8) == nv.NVFP4_EALIGN
+    assert _kvs(ldk=36) == nv.NVFP4_EALIGN  # 72-byte bf16 row pitch
+    assert _kvs(kc=P + 4) == nv.NVFP4_EALIGN
+    assert _kvs(cache_ld=40) == nv.NVFP4_EALIGN
+    assert _kvs(slots=P + 4) == nv.NVFP4_EALIGN
+    assert _kvs(ks=P + 2) == nv.NVFP4_EALIGN
+    # keys only, and empty problems, are valid (nothing enqueued for empty ones)
+    assert _kvs(tokens=0) == nv.NVFP4_OK
+    assert _kvs(width=0, ldk=16, ldv=16, cache_ld=16) == nv.NVFP4_OK
+    assert _kvs(tokens=0, v=None, vs=None, vc=None) == nv.NVFP4_OK
+
+
+def _kvl(**kw):
+    a = dict(c=P, num_slots=8, cache_ld=32, width=32, scale=P, slots=P, tokens=4, out=P,
+             odt=nv.NVFP4_F32, ld_out=32, s=None)
+    a.update(kw)
+    return nv.load_library().nvfp4_kv_fp8_load(
+        a["c"], a["num_slots"], a["cache_ld"], a["width"], a["scale"], a["slots"], a["tokens"],
+        a["out"], a["odt"], a["ld_out"], a["s"])
+
+
+def test_kv_load_validation():
+    assert _kvl(c=None) == nv.NVFP4_EINVAL
+    assert _kvl(scale=None) == nv.NVFP4_EINVAL
+    assert _kvl(out=None) == nv.NVFP4_EINVAL
+    assert _kvl(odt=nv.NVFP4_F16) == nv.NVFP4_EINVAL
+    assert _kvl(width=24, cache_ld=32, ld_out=32) == nv.NVFP4_ESHAPE
+    assert _kvl(tokens=-1) == nv.NVFP4_ESHAPE
+    assert _kvl(cache_ld=16) == nv.NVFP4_ESHAPE
+    assert _kvl(ld_out=16) == nv.NVFP4_ESHAPE
+    assert _kvl(c=P + 8) == nv.NVFP4_EALIGN
+    assert _kvl(out=P + 8) == nv.NVFP4_EALIGN
+    assert _kvl(cache_ld=40) == nv.NVFP4_EALIGN
+    assert _kvl(ld_out=33) == nv.NVFP4_EALIGN  # 132-byte f32 row pitch
+    assert _kvl(slots=P + 4) == nv.NVFP4_EALIGN
+    assert _kvl(tokens=0) == nv.NVFP4_OK

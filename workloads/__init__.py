@@ -1,10 +1,15 @@
 """Seeded synthetic workloads shared by the tests, the benchmark and the smoke check."""
 
 from .synthetic import (  # noqa: F401
+    KV_WORKLOADS,
     WORKLOADS,
+    KvWorkload,
     Workload,
     activations,
     gate_up,
+    kv_key_channels,
+    kv_slot_mapping,
+    kv_tokens,
     outlier_channels,
     random_matrix,
     round_bf16,

@@ -191,3 +191,78 @@ def random_matrix(seed: int, rows: int, cols: int, std: float = 1.0, outlier_col
         ch = rng.choice(cols, size=min(outlier_cols, cols), replace=False)
         x[:, ch] *= np.float32(outlier_gain)
     return round_bf16(x) if dtype == "bf16" else x
+
+
+# ---- FP8 KV cache --------------------------------------------------------------------------
+
+
+@dataclass(frozen=True)
+class KvWorkload:
+    """Keys and values of new tokens written into a paged FP8 KV cache.
+
+    Shape (reading; the pages give the attention layers' count, 16, and the context, 32K, but no
+    head shape): a prefill of ``tokens`` tokens, rows of ``width`` = heads * head_dim elements for
+    each of K and V, a paged cache of ``num_blocks`` blocks of ``block_size`` slots whose blocks the
+    sequence occupies in a shuffled order.  Keys carry a few hot channels; values do not."""
+
+    wid: int
+    name: str
+    tokens: int
+    width: int
+    block_size: int
+    num_blocks: int
+    key_outlier_frac: float
+    key_outlier_gain: float
+
+    @property
+    def num_slots(self) -> int:
+        return self.num_blocks * self.block_size
+
+
+KV_WORKLOADS = {
+    # 32K-token prefill, 4 KV heads x 256 dims, bf16 keys/values, 2% of key channels x8.
+    6: KvWorkload(6, "kv_fp8_store_32768x1024", 32768, 1024, 16, 4096, 0.02, 8.0),
+}
+
+
+def kv_key_channels(w: KvWorkload) -> np.ndarray:
+    n = int(round(w.key_outlier_frac * w.width))
+    return np.sort(_rng(w.wid, 3).choice(w.width, size=n, replace=False))
+
+
+def kv_tokens(w: KvWorkload, tokens: int | None = None, row0: int = 0, calibration=False):
+    """Keys and values ``(k, v)`` of tokens ``[row0, row0 + tokens)`` as float32 arrays holding
+    bfloat16 values: N(0, 1), key hot channels times the gain.  ``calibration=True`` draws an
+    independent sample of the same distribution (the calibration set).  256-token chunks, so any
+    range reproduces the full tensors."""
+    tokens = w.tokens if tokens is None else tokens
+    if tokens == 0:
+        z = np.zeros((0, w.width), dtype=np.float32)
+        return z, z.copy()
+    chunk = 256
+    c0, c1 = row0 // chunk, (row0 + tokens + chunk - 1) // chunk
+    ch = kv_key_channels(w)
+    ks, vs = [], []
+    for c in range(c0, c1):
+        rng = np.random.Generator(np.random.PCG64(1000 * w.wid + (5 if calibration else 1)).jumped(c))
+        k = rng.standard_normal((chunk, w.width), dtype=np.float32)
+        k[:, ch] *= np.float32(w.key_outlier_gain)
+        ks.append(k)
+        vs.append(rng.standard_normal((chunk, w.width), dtype=np.float32))
+    off = row0 - c0 * chunk
+    k = np.concatenate(ks, axis=0)[off:off + tokens]
+    v = np.concatenate(vs, axis=0)[off:off + tokens]
+    return round_bf16(np.ascontiguousarray(k)), round_bf16(np.ascontiguousarray(v))
+
+
+def kv_slot_mapping(w: KvWorkload, tokens: int | None = None) -> np.ndarray:
+    """Cache slot of each token (int64): token t sits at position t % block_size of the
+    sequence's (t // block_size)-th block, and the sequence's blocks are a seeded random choice of
+    the cache's blocks."""
+    tokens = w.tokens if tokens is None else tokens
+    nblk = (tokens + w.block_size - 1) // w.block_size
+    if nblk > w.num_blocks:
+        raise ValueError("the cache is too small for this many tokens")
+    table = _rng(w.wid, 2).permutation(w.num_blocks)[:nblk].astype(np.int64)
+    t = np.arange(tokens, dtype=np.int64)
+    return table[t // w.block_size] * w.block_size + t % w.block_size
