@@ -27,3 +27,11 @@ from .nvfp4_oracle import (  # noqa: F401
 )
 from .activation import round_to_bf16, silu, silu_mul_activation, silu_mul_quantize  # noqa: F401
 from .kv_cache import kv_calibrated_scale, kv_fp8_decode, kv_fp8_encode  # noqa: F401
+from .fake_quant import (  # noqa: F401
+    dequantize_f32,
+    dominated_blocks,
+    fake_quantize,
+    harmonize_segments,
+    quant_error_stats,
+    requantize,
+)

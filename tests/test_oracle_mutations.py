@@ -109,3 +109,65 @@ def test_planted_mistake_is_caught(name):
             except Exception as e:  # AssertionError or a crash: either way the pin fired
                 caught.append((getattr(pin, "__name__", "lambda"), type(e).__name__))
     assert caught, f"no pin caught mutation {name}"
+
+
+# ---- the fake-quantization / statistics / harmonization oracle --------------------------------
+
+import oracle.fake_quant as _fq_mod  # noqa: E402
+
+from . import test_oracle_fake_quant as T_fq  # noqa: E402
+
+_FQ_PATH = inspect.getsourcefile(_fq_mod)
+with open(_FQ_PATH) as _f:
+    _FQ_SRC = _f.read()
+
+FQ_MUTATIONS = {
+    "dequant_multiplies_by_g": ("(q / np.float32(g))", "(q * np.float32(g))"),
+    "dominated_tie_counts": ("2.0 * amax * amax > total", "2.0 * amax * amax >= total"),
+    "dominated_factor_dropped": ("2.0 * amax * amax > total", "amax * amax > total"),
+    "error_sum_of_abs": ("err2 = (d * d).sum(axis=1)", "err2 = np.abs(d).sum(axis=1)"),
+    "harmonize_to_the_largest_scale": ("gs = np.float32(seg_g.min())", "gs = np.float32(seg_g.max())"),
+    "requantize_keeps_input_scale": ("return quantize(dequantize_f32(codes, scales, g_in), g_out)[:2]",
+                                     "return quantize(dequantize_f32(codes, scales, g_in), g_in)[:2]"),
+}
+
+
+@contextlib.contextmanager
+def _fq_mutated(old, new):
+    assert _FQ_SRC.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    mod = types.ModuleType("oracle.fake_quant_mutant")
+    mod.__file__ = _FQ_PATH
+    mod.__package__ = "oracle"
+    exec(compile(_FQ_SRC.replace(old, new), _FQ_PATH, "exec"), mod.__dict__)
+    saved = {}
+    for name, v in list(vars(_fq_mod).items()):
+        if not name.startswith("_") and callable(v) and hasattr(mod, name):
+            saved[name] = v
+            setattr(_fq_mod, name, getattr(mod, name))
+    try:
+        yield
+    finally:
+        for name, v in saved.items():
+            setattr(_fq_mod, name, v)
+
+
+def _fq_pins():
+    return [getattr(T_fq, n) for n in dir(T_fq) if n.startswith("test_")]
+
+
+def test_unmutated_fake_quant_oracle_passes_every_pin():
+    for pin in _fq_pins():
+        pin()
+
+
+@pytest.mark.parametrize("name", sorted(FQ_MUTATIONS))
+def test_planted_fake_quant_mistake_is_caught(name):
+    old, new = FQ_MUTATIONS[name]
+    caught = []
+    with _fq_mutated(old, new):
+        for pin in _fq_pins():
+            try:
+                pin()
+            except Exception as e:
+                caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin caught mutation {name}"
