@@ -12,6 +12,10 @@ Entry points (same names as the C ABI):
 * ``nvfp4_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, out_dtype)`` -> ``C``
 * ``fused_nvfp4_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_gscale, seg_offsets,
   out_dtype)`` -> ``C``
+* ``nvfp4_fake_quantize(x, global_scale=None, out_dtype=None)`` -> ``(xh, global_scale)``
+* ``nvfp4_quant_error_stats(x, global_scale=None)`` -> ``(err2, norm2, dominated, global_scale)``
+* ``nvfp4_requantize(codes, scales, g_in, g_out)`` -> ``(codes, scales)``
+* ``nvfp4_harmonize_segments(codes, scales, seg_gscale, seg_offsets)`` -> ``(codes, scales, g)``
 * ``nvfp4_kv_fp8_store(key, value, key_scale, value_scale, key_cache, value_cache, slot_mapping)``
 * ``nvfp4_kv_fp8_load(cache, scale, slot_mapping, out_dtype)`` -> decoded rows
 """
@@ -30,8 +34,9 @@ NVFP4_MAX_SEGMENTS = 16
 
 #: every symbol include/nvfp4.h declares
 EXPORTED_SYMBOLS = ("nvfp4_quantize", "nvfp4_silu_mul_quantize", "nvfp4_gemm", "fused_nvfp4_gemm",
-                    "nvfp4_kv_fp8_store", "nvfp4_kv_fp8_load", "nvfp4_status_string",
-                    "nvfp4_version")
+                    "nvfp4_fake_quantize", "nvfp4_quant_error_stats", "nvfp4_requantize",
+                    "nvfp4_harmonize_segments", "nvfp4_kv_fp8_store", "nvfp4_kv_fp8_load",
+                    "nvfp4_status_string", "nvfp4_version")
 
 _lib = None
 
@@ -59,6 +64,17 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.nvfp4_silu_mul_quantize.argtypes = [c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_i64, c_vp,
                                             c_int, c_vp, c_vp, c_vp]
     lib.nvfp4_silu_mul_quantize.restype = c_int
+    lib.nvfp4_fake_quantize.argtypes = [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_int, c_vp, c_int,
+                                        c_i64, c_vp]
+    lib.nvfp4_fake_quantize.restype = c_int
+    lib.nvfp4_quant_error_stats.argtypes = [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_int, c_vp,
+                                            c_vp, c_vp, c_vp]
+    lib.nvfp4_quant_error_stats.restype = c_int
+    lib.nvfp4_requantize.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp]
+    lib.nvfp4_requantize.restype = c_int
+    lib.nvfp4_harmonize_segments.argtypes = [c_vp, c_vp, c_vp, ctypes.POINTER(c_i64), c_int, c_i64,
+                                             c_i64, c_vp, c_vp, c_vp, c_vp]
+    lib.nvfp4_harmonize_segments.restype = c_int
     lib.nvfp4_kv_fp8_store.argtypes = [c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp,
                                        c_vp, c_vp, c_vp, c_i64, c_i64, c_vp]
     lib.nvfp4_kv_fp8_store.restype = c_int
@@ -224,6 +240,87 @@ def fused_nvfp4_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_gscale,
     return out
 
 
+def nvfp4_fake_quantize(x, global_scale=None, out_dtype=None, out=None):
+    """``dequantize(quantize(x))`` on the GPU: ``x[rows, cols]`` (f32/bf16/f16, contiguous rows)
+    with its NVFP4 rounding error, as float32 (default) or bfloat16.  ``global_scale`` as for
+    :func:`nvfp4_quantize`.  Returns ``(xh, global_scale)``."""
+    torch = _torch()
+    lib = load_library()
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with contiguous rows")
+    _require_cuda(x)
+    rows, cols = x.shape
+    dynamic = global_scale is None
+    if dynamic:
+        global_scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    _require_cuda(global_scale)
+    if out is None:
+        out = _out(rows, cols, out_dtype or torch.float32, x.device)
+    _check(lib.nvfp4_fake_quantize(_ptr(x), _dtype_code(x.dtype), rows, cols, x.stride(0),
+                                   _ptr(global_scale), int(dynamic), _ptr(out),
+                                   _dtype_code(out.dtype), out.stride(0), _stream(x.device)))
+    return out, global_scale
+
+
+def nvfp4_quant_error_stats(x, global_scale=None):
+    """Per-row NVFP4 quantization-error statistics of ``x``: ``(err2 f64[rows], norm2 f64[rows],
+    dominated int32[rows], global_scale)``."""
+    torch = _torch()
+    lib = load_library()
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with contiguous rows")
+    _require_cuda(x)
+    rows, cols = x.shape
+    dynamic = global_scale is None
+    if dynamic:
+        global_scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    _require_cuda(global_scale)
+    err2 = torch.zeros(rows, dtype=torch.float64, device=x.device)
+    norm2 = torch.zeros(rows, dtype=torch.float64, device=x.device)
+    dom = torch.zeros(rows, dtype=torch.int32, device=x.device)
+    _check(lib.nvfp4_quant_error_stats(_ptr(x), _dtype_code(x.dtype), rows, cols, x.stride(0),
+                                       _ptr(global_scale), int(dynamic), _ptr(err2), _ptr(norm2),
+                                       _ptr(dom), _stream(x.device)))
+    return err2, norm2, dom, global_scale
+
+
+def nvfp4_requantize(codes, scales, g_in, g_out, codes_out=None, scales_out=None):
+    """Re-encode NVFP4 ``(codes [rows, cols/2], scales [rows, cols/16])`` from global scale
+    ``g_in`` to ``g_out`` (1-element float32 device tensors).  The outputs may be the inputs."""
+    lib = load_library()
+    _require_cuda(codes, scales, g_in, g_out)
+    rows, cols = codes.shape[0], codes.shape[1] * 2
+    if codes_out is None:
+        codes_out = codes.new_empty(codes.shape)
+    if scales_out is None:
+        scales_out = scales.new_empty(scales.shape)
+    _check(lib.nvfp4_requantize(_ptr(codes), _ptr(scales), _ptr(g_in), _ptr(g_out), rows, cols,
+                                _ptr(codes_out), _ptr(scales_out), _stream(codes.device)))
+    return codes_out, scales_out
+
+
+def nvfp4_harmonize_segments(codes, scales, seg_gscale, seg_offsets, codes_out=None,
+                             scales_out=None, shared_gscale=None):
+    """Re-encode every module of a fused NVFP4 weight under the smallest module scale.  Returns
+    ``(codes, scales, shared_gscale)``; the outputs may be the inputs."""
+    torch = _torch()
+    lib = load_library()
+    _require_cuda(codes, scales, seg_gscale)
+    N, K = codes.shape[0], codes.shape[1] * 2
+    offs = [int(o) for o in seg_offsets]
+    arr = (ctypes.c_int64 * len(offs))(*offs)
+    if codes_out is None:
+        codes_out = codes.new_empty(codes.shape)
+    if scales_out is None:
+        scales_out = scales.new_empty(scales.shape)
+    if shared_gscale is None:
+        shared_gscale = torch.empty(1, dtype=torch.float32, device=codes.device)
+    _check(lib.nvfp4_harmonize_segments(_ptr(codes), _ptr(scales), _ptr(seg_gscale), arr,
+                                        len(offs) - 1, N, K, _ptr(shared_gscale), _ptr(codes_out),
+                                        _ptr(scales_out), _stream(codes.device)))
+    return codes_out, scales_out, shared_gscale
+
+
 def nvfp4_kv_fp8_store(key, value, key_scale, value_scale, key_cache, value_cache,
                        slot_mapping=None):
     """Encode ``key`` (and ``value``, or None) ``[tokens, width]`` to FP8 E4M3 under the static
@@ -250,8 +347,6 @@ def nvfp4_kv_fp8_store(key, value, key_scale, value_scale, key_cache, value_cach
     if value_cache is not None and (value_cache.shape != key_cache.shape or
                                     value_cache.stride() != key_cache.stride()):
         raise ValueError("value_cache must have key_cache's shape and strides")
-    if tokens == 0 or width == 0:
-        return  # torch gives empty tensors a null data pointer; the library has nothing to do
     _check(lib.nvfp4_kv_fp8_store(_ptr(key), _ptr(value), _dtype_code(key.dtype), tokens, width,
                                   key.stride(0), value.stride(0) if value is not None else 0,
                                   _ptr(key_scale), _ptr(value_scale), _ptr(slot_mapping),
@@ -277,8 +372,6 @@ def nvfp4_kv_fp8_load(cache, scale, slot_mapping=None, out_dtype=None, width=Non
     _require_cuda(*ts)
     if out is None:
         out = _out(tokens, width, out_dtype or torch.float32, cache.device)
-    if tokens == 0 or width == 0:
-        return out  # torch gives empty tensors a null data pointer; the library has nothing to do
     _check(lib.nvfp4_kv_fp8_load(_ptr(cache), cache.shape[0], cache.stride(0), width, _ptr(scale),
                                  _ptr(slot_mapping), tokens, _ptr(out), _dtype_code(out.dtype),
                                  out.stride(0), _stream(cache.device)))

@@ -93,7 +93,8 @@ extern "C" {
 nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols,
                             int64_t ldx, float* global_scale, int dynamic, uint8_t* codes,
                             uint8_t* scales, void* stream) {
-  if (!x || !global_scale || !codes || !scales) return NVFP4_EINVAL;
+  if (!global_scale) return NVFP4_EINVAL;
+  if (!(rows == 0 || cols == 0) && (!x || !codes || !scales)) return NVFP4_EINVAL;
   if (!valid_in_dtype(x_dtype)) return NVFP4_EINVAL;
   if (dynamic != 0 && dynamic != 1) return NVFP4_EINVAL;
   if (rows < 0 || cols < 0 || cols % 16 != 0) return NVFP4_ESHAPE;
@@ -112,7 +113,8 @@ nvfp4_status nvfp4_silu_mul_quantize(const void* gate, const void* up, nvfp4_dty
                                      int64_t rows, int64_t cols, int64_t ld_gate, int64_t ld_up,
                                      float* global_scale, int dynamic, uint8_t* codes,
                                      uint8_t* scales, void* stream) {
-  if (!gate || !up || !global_scale || !codes || !scales) return NVFP4_EINVAL;
+  if (!global_scale) return NVFP4_EINVAL;
+  if (!(rows == 0 || cols == 0) && (!gate || !up || !codes || !scales)) return NVFP4_EINVAL;
   if (!valid_in_dtype(dtype)) return NVFP4_EINVAL;
   if (dynamic != 0 && dynamic != 1) return NVFP4_EINVAL;
   if (rows < 0 || cols < 0 || cols % 16 != 0) return NVFP4_ESHAPE;
@@ -132,34 +134,135 @@ nvfp4_status nvfp4_silu_mul_quantize(const void* gate, const void* up, nvfp4_dty
   return device_status(e);
 }
 
+nvfp4_status nvfp4_fake_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols,
+                                 int64_t ldx, float* global_scale, int dynamic, void* out,
+                                 nvfp4_dtype out_dtype, int64_t ldo, void* stream) {
+  if (!global_scale) return NVFP4_EINVAL;
+  if (!(rows == 0 || cols == 0) && (!x || !out)) return NVFP4_EINVAL;
+  if (!valid_in_dtype(x_dtype) || !valid_out_dtype(out_dtype)) return NVFP4_EINVAL;
+  if (dynamic != 0 && dynamic != 1) return NVFP4_EINVAL;
+  if (rows < 0 || cols < 0 || cols % 16 != 0) return NVFP4_ESHAPE;
+  if (ldx < cols || ldx < 1 || ldo < cols || ldo < 1) return NVFP4_ESHAPE;
+  if (rows * (cols / 16) >= (int64_t(1) << 31)) return NVFP4_ESHAPE;
+  if (rows > 0 && ((rows - 1) * ldx + cols > kMaxSpan || (rows - 1) * ldo + cols > kMaxSpan))
+    return NVFP4_ESHAPE;
+  if (!aligned(x, 16) || (ldx * dtype_bytes(x_dtype)) % 16 != 0) return NVFP4_EALIGN;
+  if (!aligned(out, 16) || (ldo * dtype_bytes(out_dtype)) % 16 != 0) return NVFP4_EALIGN;
+  if (!aligned(global_scale, 4)) return NVFP4_EALIGN;
+  if ((rows == 0 || cols == 0) && !dynamic) return NVFP4_OK;
+  hipError_t e = nvfp4::launch_fake_quantize(x, x_dtype, rows, cols, ldx, global_scale, dynamic,
+                                             out, out_dtype, ldo,
+                                             reinterpret_cast<hipStream_t>(stream));
+  return device_status(e);
+}
+
+nvfp4_status nvfp4_quant_error_stats(const void* x, nvfp4_dtype x_dtype, int64_t rows,
+                                     int64_t cols, int64_t ldx, float* global_scale, int dynamic,
+                                     double* err2, double* norm2, int32_t* dominated,
+                                     void* stream) {
+  if (!global_scale) return NVFP4_EINVAL;
+  if (rows != 0 && (!err2 || !norm2 || !dominated)) return NVFP4_EINVAL;
+  if (!(rows == 0 || cols == 0) && !x) return NVFP4_EINVAL;
+  if (!valid_in_dtype(x_dtype)) return NVFP4_EINVAL;
+  if (dynamic != 0 && dynamic != 1) return NVFP4_EINVAL;
+  if (rows < 0 || cols < 0 || cols % 16 != 0) return NVFP4_ESHAPE;
+  if (ldx < cols || ldx < 1) return NVFP4_ESHAPE;
+  if (rows * (cols / 16) >= (int64_t(1) << 31)) return NVFP4_ESHAPE;
+  if (rows > 0 && (rows - 1) * ldx + cols > kMaxSpan) return NVFP4_ESHAPE;
+  if (!aligned(x, 16) || (ldx * dtype_bytes(x_dtype)) % 16 != 0) return NVFP4_EALIGN;
+  if (!aligned(err2, 8) || !aligned(norm2, 8) || !aligned(dominated, 4) ||
+      !aligned(global_scale, 4))
+    return NVFP4_EALIGN;
+  if (rows == 0 && !dynamic) return NVFP4_OK;
+  hipError_t e = nvfp4::launch_quant_error_stats(x, x_dtype, rows, cols, ldx, global_scale,
+                                                 dynamic, err2, norm2, dominated,
+                                                 reinterpret_cast<hipStream_t>(stream));
+  return device_status(e);
+}
+
+nvfp4_status nvfp4_requantize(const uint8_t* codes, const uint8_t* scales, const float* g_in,
+                              const float* g_out, int64_t rows, int64_t cols, uint8_t* codes_out,
+                              uint8_t* scales_out, void* stream) {
+  if (!g_in || !g_out) return NVFP4_EINVAL;
+  if (rows != 0 && cols != 0 && (!codes || !scales || !codes_out || !scales_out))
+    return NVFP4_EINVAL;
+  if (rows < 0 || cols < 0 || cols % 16 != 0) return NVFP4_ESHAPE;
+  if (rows > kMaxDim || rows * (cols / 16) >= (int64_t(1) << 31)) return NVFP4_ESHAPE;
+  if (!aligned(codes, 8) || !aligned(codes_out, 8) || !aligned(g_in, 4) || !aligned(g_out, 4))
+    return NVFP4_EALIGN;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  nvfp4::SegTable seg{};
+  seg.nseg = 1;
+  seg.off[0] = 0;
+  for (int j = 1; j <= NVFP4_MAX_SEGMENTS; ++j) seg.off[j] = (int32_t)rows;
+  hipError_t e = nvfp4::launch_requantize(codes, scales, rows, cols, seg, g_in, g_out, nullptr,
+                                          codes_out, scales_out,
+                                          reinterpret_cast<hipStream_t>(stream));
+  return device_status(e);
+}
+
+nvfp4_status nvfp4_harmonize_segments(const uint8_t* codes, const uint8_t* scales,
+                                      const float* seg_gscale, const int64_t* seg_offsets,
+                                      int nseg, int64_t N, int64_t K, float* shared_gscale,
+                                      uint8_t* codes_out, uint8_t* scales_out, void* stream) {
+  if (!seg_gscale || !seg_offsets || !shared_gscale) return NVFP4_EINVAL;
+  if (N != 0 && K != 0 && (!codes || !scales || !codes_out || !scales_out)) return NVFP4_EINVAL;
+  if (nseg < 1 || nseg > NVFP4_MAX_SEGMENTS) return NVFP4_EINVAL;
+  // the shared scale is written while the kernel reads the segment scales
+  if (shared_gscale >= seg_gscale && shared_gscale < seg_gscale + nseg) return NVFP4_EINVAL;
+  if (N < 0 || K < 0 || K % 16 != 0) return NVFP4_ESHAPE;
+  if (N > kMaxDim || N * (K / 16) >= (int64_t(1) << 31)) return NVFP4_ESHAPE;
+  if (seg_offsets[0] != 0 || seg_offsets[nseg] != N) return NVFP4_ESHAPE;
+  for (int j = 0; j < nseg; ++j) {
+    const bool empty_problem = (N == 0 && nseg == 1);
+    if (!(seg_offsets[j + 1] > seg_offsets[j]) && !empty_problem) return NVFP4_ESHAPE;
+  }
+  if (!aligned(codes, 8) || !aligned(codes_out, 8) || !aligned(seg_gscale, 4) ||
+      !aligned(shared_gscale, 4))
+    return NVFP4_EALIGN;
+  if (N == 0 || K == 0) return NVFP4_OK;
+  nvfp4::SegTable seg{};
+  seg.nseg = nseg;
+  for (int j = 0; j <= nseg; ++j) seg.off[j] = (int32_t)seg_offsets[j];
+  for (int j = nseg + 1; j <= NVFP4_MAX_SEGMENTS; ++j) seg.off[j] = (int32_t)N;
+  hipError_t e = nvfp4::launch_requantize(codes, scales, N, K, seg, seg_gscale, nullptr,
+                                          shared_gscale, codes_out, scales_out,
+                                          reinterpret_cast<hipStream_t>(stream));
+  return device_status(e);
+}
+
 nvfp4_status nvfp4_kv_fp8_store(const void* key, const void* value, nvfp4_dtype dtype,
                                 int64_t tokens, int64_t width, int64_t ld_key, int64_t ld_value,
                                 const float* key_scale, const float* value_scale,
                                 const int64_t* slot_mapping, uint8_t* key_cache,
                                 uint8_t* value_cache, int64_t num_slots, int64_t cache_ld,
                                 void* stream) {
-  if (!key || !key_scale || !key_cache) return NVFP4_EINVAL;
-  // the value tensor is optional, but then all three of its arguments are absent
-  if ((value != nullptr) != (value_scale != nullptr) || (value != nullptr) != (value_cache != nullptr))
-    return NVFP4_EINVAL;
+  if (!key_scale) return NVFP4_EINVAL;
+  // the value tensor is optional: value_scale says whether it is there; then value and
+  // value_cache are required (unless the problem is empty), else all three are absent
+  const bool has_value = value_scale != nullptr;
+  const bool empty = tokens == 0 || width == 0;
+  if (!empty && (!key || (!key_cache && num_slots > 0))) return NVFP4_EINVAL;
+  if (has_value && !empty && (!value || (!value_cache && num_slots > 0))) return NVFP4_EINVAL;
+  if (!has_value && (value || value_cache)) return NVFP4_EINVAL;
   if (!valid_in_dtype(dtype)) return NVFP4_EINVAL;
   if (tokens < 0 || width < 0 || width % 16 != 0 || num_slots < 0) return NVFP4_ESHAPE;
   if (tokens > kMaxDim || width > kMaxKvWidth) return NVFP4_ESHAPE;
   if (ld_key < width || ld_key < 1 || cache_ld < width || cache_ld < 1) return NVFP4_ESHAPE;
-  if (value && (ld_value < width || ld_value < 1)) return NVFP4_ESHAPE;
+  if (has_value && (ld_value < width || ld_value < 1)) return NVFP4_ESHAPE;
   if (tokens > 0 && ((tokens - 1) * ld_key + width > kMaxSpan ||
-                     (value && (tokens - 1) * ld_value + width > kMaxSpan)))
+                     (has_value && (tokens - 1) * ld_value + width > kMaxSpan)))
     return NVFP4_ESHAPE;
   if (num_slots > 0 && (num_slots - 1) * cache_ld + width > kMaxSpan) return NVFP4_ESHAPE;
   const int64_t eb = dtype_bytes(dtype);
   if (!aligned(key, 16) || (ld_key * eb) % 16 != 0 || !aligned(key_cache, 16) ||
       cache_ld % 16 != 0 || !aligned(key_scale, 4))
     return NVFP4_EALIGN;
-  if (value && (!aligned(value, 16) || (ld_value * eb) % 16 != 0 || !aligned(value_cache, 16) ||
-                !aligned(value_scale, 4)))
+  if (has_value && (!aligned(value, 16) || (ld_value * eb) % 16 != 0 ||
+                    !aligned(value_cache, 16) || !aligned(value_scale, 4)))
     return NVFP4_EALIGN;
   if (slot_mapping && !aligned(slot_mapping, 8)) return NVFP4_EALIGN;
-  if (tokens == 0 || width == 0) return NVFP4_OK;
+  if (empty) return NVFP4_OK;
   hipError_t e = nvfp4::launch_kv_store(key, value, dtype, tokens, width, ld_key, ld_value,
                                         key_scale, value_scale, slot_mapping, key_cache,
                                         value_cache, num_slots, cache_ld,
@@ -171,7 +274,8 @@ nvfp4_status nvfp4_kv_fp8_load(const uint8_t* cache, int64_t num_slots, int64_t 
                                int64_t width, const float* scale, const int64_t* slot_mapping,
                                int64_t tokens, void* out, nvfp4_dtype out_dtype, int64_t ld_out,
                                void* stream) {
-  if (!cache || !scale || !out) return NVFP4_EINVAL;
+  if (!scale) return NVFP4_EINVAL;
+  if (tokens != 0 && width != 0 && (!out || (!cache && num_slots > 0))) return NVFP4_EINVAL;
   if (!valid_out_dtype(out_dtype)) return NVFP4_EINVAL;
   if (tokens < 0 || width < 0 || width % 16 != 0 || num_slots < 0) return NVFP4_ESHAPE;
   if (tokens > kMaxDim || width > kMaxKvWidth) return NVFP4_ESHAPE;

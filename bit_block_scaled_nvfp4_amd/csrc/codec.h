@@ -1,0 +1,144 @@
+// NVFP4 codec helpers shared by the encoding kernels (gfx950): element loading, the E4M3 and E2M1
+// roundings, block encoding and decoding.  The rounding rules are the ones stated in
+// include/nvfp4.h; every operation is one IEEE binary32 operation in the order written (the
+// library is built with -ffp-contract=off and correctly rounded division), so results are
+// bit-exact with the CPU reference encoder.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nvfp4.h"
+
+namespace nvfp4 {
+namespace codec {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---- element loading: 16 consecutive elements widened exactly to f32 --------------------------
+
+template <nvfp4_dtype DT>
+__device__ __forceinline__ void load_block(const void* base, float (&v)[16]);
+
+template <>
+__device__ __forceinline__ void load_block<NVFP4_F32>(const void* base, float (&v)[16]) {
+  const f32x4* p = reinterpret_cast<const f32x4*>(base);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f32x4 q = __builtin_nontemporal_load(p + i);
+    v[4 * i + 0] = q.x;
+    v[4 * i + 1] = q.y;
+    v[4 * i + 2] = q.z;
+    v[4 * i + 3] = q.w;
+  }
+}
+
+template <>
+__device__ __forceinline__ void load_block<NVFP4_BF16>(const void* base, float (&v)[16]) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(base);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    u32x4 q = __builtin_nontemporal_load(p + i);
+    uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * i + 2 * j + 0] = __uint_as_float(w[j] << 16);
+      v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  }
+}
+
+template <>
+__device__ __forceinline__ void load_block<NVFP4_F16>(const void* base, float (&v)[16]) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(base);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    u32x4 q = __builtin_nontemporal_load(p + i);
+    uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      _Float16 lo = __builtin_bit_cast(_Float16, (uint16_t)(w[j] & 0xFFFFu));
+      _Float16 hi = __builtin_bit_cast(_Float16, (uint16_t)(w[j] >> 16));
+      v[8 * i + 2 * j + 0] = (float)lo;
+      v[8 * i + 2 * j + 1] = (float)hi;
+    }
+  }
+}
+
+template <nvfp4_dtype DT>
+constexpr int elem_bytes() {
+  return DT == NVFP4_F32 ? 4 : 2;
+}
+
+// ---- the two codecs ------------------------------------------------------------------------
+
+// Non-negative binary32 -> OCP E4M3 code: nearest, ties to the even code, >= 448 saturates to
+// 0x7E, subnormal codes kept.  Below 2^-6 the E4M3 grid is the multiples of 2^-9, so the code is
+// round-to-nearest-even of s * 512 (exact product).  In the normal range the code is the binary32
+// pattern rounded to 3 mantissa bits (nearest-even on the 20 dropped bits, carries into the
+// exponent are the correct binade change) and rebiased: code = (bits >> 20) - ((127 - 7) << 3).
+__device__ __forceinline__ uint32_t e4m3_encode(float s) {
+  if (!(s < 448.0f)) return 0x7Eu;
+  if (s < 0.015625f) return (uint32_t)__builtin_rintf(s * 512.0f);
+  uint32_t u = __float_as_uint(s);
+  u = u + 0x7FFFFu + ((u >> 20) & 1u);
+  return (u >> 20) - 960u;
+}
+
+// Exact binary32 value of an E4M3 code 0x00..0x7E.
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  return c < 8u ? (float)c * 0.001953125f : __uint_as_float((c + 960u) << 20);
+}
+
+// Non-negative binary32 (or +inf) -> E2M1 magnitude index: nearest, ties to the even index,
+// saturating at 6.  Below 1 the grid is {0, 0.5, 1}: round-to-nearest-even of 2y.  From 1 up the
+// grid keeps one mantissa bit: round the pattern to 1 mantissa bit (nearest-even on 22 dropped
+// bits) and read exponent and that bit as the index, (bits >> 22) - 252, clamped at 7.
+__device__ __forceinline__ uint32_t e2m1_index(float y) {
+  if (y < 1.0f) return (uint32_t)__builtin_rintf(y * 2.0f);
+  uint32_t u = __float_as_uint(y);
+  u = (u + 0x1FFFFFu + ((u >> 22) & 1u)) >> 22;
+  uint32_t i = u - 252u;
+  return i > 7u ? 7u : i;
+}
+
+// Encode 16 binary32 values as block b: one E4M3 scale byte and 8 code bytes.
+__device__ __forceinline__ void encode_block(const float (&v)[16], float g, float gs6, uint32_t b,
+                                             uint8_t* __restrict__ codes,
+                                             uint8_t* __restrict__ scales) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const uint32_t sc = e4m3_encode(amax * gs6);
+  const float sd = e4m3_value(sc);
+  // sd == 0: r = 0 makes every magnitude 0 (finite inputs)
+  const float r = sd > 0.0f ? g / sd : 0.0f;
+
+  uint32_t word[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t code = e2m1_index(fabsf(v[i]) * r) | ((__float_as_uint(v[i]) >> 31) << 3);
+    word[i >> 3] |= code << (4 * (i & 7));
+  }
+  uint2 out;
+  out.x = word[0];
+  out.y = word[1];
+  *reinterpret_cast<uint2*>(codes + (int64_t)b * 8) = out;
+  scales[b] = (uint8_t)sc;
+}
+
+// Exact binary32 value of an E2M1 magnitude index 0..7: {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+__device__ __forceinline__ float e2m1_value(uint32_t i) {
+  return i < 2u ? 0.5f * (float)i : __uint_as_float((((i >> 1) + 126u) << 23) | ((i & 1u) << 22));
+}
+
+__device__ __forceinline__ float read_global_scale(const float* g, int dynamic) {
+  float v = __builtin_nontemporal_load(g);
+  if (!dynamic) return v;
+  // dynamic: *g holds amax(|x|) at this point (written by amax_kernel)
+  return v == 0.0f ? 1.0f : 2688.0f / v;
+}
+
+}  // namespace codec
+}  // namespace nvfp4

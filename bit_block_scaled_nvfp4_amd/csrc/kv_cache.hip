@@ -214,7 +214,8 @@ hipError_t launch_kv_store(const void* key, const void* value, nvfp4_dtype dt, i
   a.lane_bits = lane_bits_for(a.chunks);
   const int64_t tok_per_block = kThreads >> a.lane_bits;
   const dim3 grid((uint32_t)((tokens + tok_per_block - 1) / tok_per_block),
-                  (uint32_t)((a.chunks + (1 << a.lane_bits) - 1) >> a.lane_bits), value ? 2u : 1u);
+                  (uint32_t)((a.chunks + (1 << a.lane_bits) - 1) >> a.lane_bits),
+                  value_scale ? 2u : 1u);
   switch (dt) {
     case NVFP4_F32:
       hipLaunchKernelGGL(kv_store_kernel<NVFP4_F32>, grid, dim3(kThreads), 0, stream, a);

@@ -37,6 +37,24 @@ hipError_t launch_silu_mul_quantize(const void* gate, const void* up, nvfp4_dtyp
                                     int64_t rows, int64_t cols, int64_t ldg, int64_t ldu,
                                     float* g, int dynamic, uint8_t* codes, uint8_t* scales,
                                     hipStream_t stream);
+// Dynamic global scale in three steps around an encoding kernel: launch_dynamic_amax clears *cell
+// and leaves max|x| in it; the encoding kernel reads it as 2688 / amax (codec::read_global_scale);
+// launch_finalize_dynamic then replaces it with that scale.
+hipError_t launch_dynamic_amax(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols,
+                               int64_t ldx, float* cell, hipStream_t stream);
+hipError_t launch_finalize_dynamic(float* cell, hipStream_t stream);
+hipError_t launch_fake_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols,
+                                int64_t ldx, float* g, int dynamic, void* out, nvfp4_dtype out_dt,
+                                int64_t ldo, hipStream_t stream);
+hipError_t launch_quant_error_stats(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols,
+                                    int64_t ldx, float* g, int dynamic, double* err2,
+                                    double* norm2, int32_t* dominated, hipStream_t stream);
+// Re-encode rows [seg.off[j], seg.off[j+1]) from global scale g_in[j] to *g_out, or, when g_out is
+// null, to min_j g_in[j] (written to *g_shared when it is not null).
+hipError_t launch_requantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                             int64_t cols, const SegTable& seg, const float* g_in,
+                             const float* g_out, float* g_shared, uint8_t* codes_out,
+                             uint8_t* scales_out, hipStream_t stream);
 hipError_t launch_kv_store(const void* key, const void* value, nvfp4_dtype dt, int64_t tokens,
                            int64_t width, int64_t ld_key, int64_t ld_value, const float* key_scale,
                            const float* value_scale, const int64_t* slots, uint8_t* key_cache,

@@ -30,15 +30,18 @@
  *     product: along the contraction dimension K of both operands).
  *
  * Conventions shared by every entry point:
- *   - All tensor pointers are DEVICE pointers, except the segment-offset array of
- *     fused_nvfp4_gemm, which is a HOST array.  The caller owns every buffer; the library
+ *   - All tensor pointers are DEVICE pointers, except the segment-offset arrays of
+ *     fused_nvfp4_gemm and nvfp4_harmonize_segments, which are HOST arrays.  The caller owns every buffer; the library
  *     allocates nothing, keeps no mutable global state, is thread-safe, and enqueues its work
  *     asynchronously on `stream` (a hipStream_t; NULL = the null stream).  Nothing synchronises
  *     with the host.
  *   - Every argument check happens on the host before any HIP call: a non-OK status other than
  *     NVFP4_EDEVICE means nothing was enqueued.  NVFP4_EDEVICE reports a HIP launch error.
  *   - Sizes are element counts; leading dimensions (ld*) are in elements of that tensor.
- *   - Empty problems (rows, M or N equal to 0) are valid and enqueue nothing.
+ *   - Empty problems (rows, M or N equal to 0) are valid and enqueue nothing, except that a
+ *     dynamic global scale is still written (1, the scale of an all-zero tensor).  The data
+ *     pointers of an empty problem may be NULL (an empty tensor may have no storage); global-scale
+ *     pointers may not.
  *   - NaN and infinite inputs are unsupported: their codes are unspecified (no error is raised).
  *   - Results are deterministic: identical inputs give identical bits on every call.
  */
@@ -168,6 +171,99 @@ nvfp4_status fused_nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                               int64_t K, void* c, nvfp4_dtype c_dtype, int64_t ldc, void* stream);
 
 /*
+ * nvfp4_fake_quantize -- out = dequantize(quantize(x)): the NVFP4 rounding error injected into a
+ * high-precision tensor, without storing codes.
+ *
+ * Source: ai.info summary, "Methodology in Plain English" (fake quantization: quantize, dequantize,
+ * continue in high precision).  Reading: each element is encoded exactly as nvfp4_quantize
+ * encodes it and decoded as
+ *   out = fl(V * sd / g)     (V * sd is exact; one correctly rounded binary32 division by g;
+ *                             the sign bit is copied, so code 0x8 gives -0.0)
+ * rounded once more to BF16 (nearest-even) when out_dtype is BF16.
+ *
+ *   x, x_dtype, rows, cols, ldx, global_scale, dynamic   as nvfp4_quantize.
+ *   out          device, [rows, cols] of out_dtype (F32 or BF16), row pitch ldo (elements; >= cols;
+ *                a multiple of 16 bytes); 16-byte aligned.  May not overlap x.
+ * Errors as nvfp4_quantize.  Bit-exact.
+ */
+nvfp4_status nvfp4_fake_quantize(const void* x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols,
+                                 int64_t ldx, float* global_scale, int dynamic, void* out,
+                                 nvfp4_dtype out_dtype, int64_t ldo, void* stream);
+
+/*
+ * nvfp4_quant_error_stats -- per-row statistics of the NVFP4 quantization error of x, the
+ * quantities the pages report at NVFP4 granularity.
+ *
+ * Source: ai.info summary, "Main Findings" (per-token activation error 7.5-9.2 %, weight error
+ * 10.5-11.9 %, 10-32 % of 16-element blocks dominated by a single value).  Readings:
+ *   err2[r]      = sum_k (xh[r,k] - x[r,k])^2, xh = nvfp4_fake_quantize(x) in binary32, summed in
+ *                  binary64 (per-token relative error: sqrt(err2 / norm2); a tensor's error:
+ *                  sqrt(sum err2 / sum norm2));
+ *   norm2[r]     = sum_k x[r,k]^2 in binary64;
+ *   dominated[r] = number of 16-element blocks of row r whose largest magnitude a satisfies
+ *                  2 a^2 > (sum of the block's 16 squares), in binary64 with the squares summed in
+ *                  element order (all-zero blocks are not dominated).
+ * The binary64 sums are deterministic; their summation order is unspecified (relative error below
+ * cols * 2^-53).  dominated is exact.
+ *
+ *   x, x_dtype, rows, cols, ldx, global_scale, dynamic   as nvfp4_quantize.
+ *   err2, norm2  device, rows doubles each, 8-byte aligned.
+ *   dominated    device, rows int32, 4-byte aligned.
+ * Errors as nvfp4_quantize.
+ */
+nvfp4_status nvfp4_quant_error_stats(const void* x, nvfp4_dtype x_dtype, int64_t rows,
+                                     int64_t cols, int64_t ldx, float* global_scale, int dynamic,
+                                     double* err2, double* norm2, int32_t* dominated,
+                                     void* stream);
+
+/*
+ * nvfp4_requantize -- re-encode an NVFP4 tensor from global scale *g_in to *g_out:
+ * codes_out, scales_out = quantize(fake-dequantized values of (codes, scales) under g_in, g_out),
+ * the dequantized values formed as in nvfp4_fake_quantize.
+ *
+ * Source: ai.info summary, "Methodology in Plain English" (harmonizing fused global scales on the
+ * checkpoint side); the single-module building block of nvfp4_harmonize_segments.
+ *
+ *   codes, scales        device, [rows, cols/2] and [rows, cols/16], contiguous rows; codes 8-byte
+ *                        aligned.
+ *   g_in, g_out          device, one float each.
+ *   codes_out, scales_out  device, same shapes; may be the input buffers themselves (in place),
+ *                        but must not overlap them otherwise.  codes_out 8-byte aligned.
+ *   rows >= 0; cols >= 0, a multiple of 16; rows * cols/16 < 2^31.
+ * Bit-exact.  Errors: EINVAL (NULL), ESHAPE, EALIGN as above; an empty tensor enqueues nothing.
+ */
+nvfp4_status nvfp4_requantize(const uint8_t* codes, const uint8_t* scales, const float* g_in,
+                              const float* g_out, int64_t rows, int64_t cols, uint8_t* codes_out,
+                              uint8_t* scales_out, void* stream);
+
+/*
+ * nvfp4_harmonize_segments -- checkpoint-side repair of a fused weight: every module j (rows
+ * [seg_offsets[j], seg_offsets[j+1]) of the [N, K] weight, encoded under seg_gscale[j]) is
+ * re-encoded as nvfp4_requantize does under the shared scale g* = min_j seg_gscale[j], which is
+ * written to *shared_gscale.  The fused product may then use g* for every segment (a
+ * fused_nvfp4_gemm table filled with g*, or nvfp4_gemm with g*).
+ *
+ * Source: ai.info summary, "Methodology in Plain English" (harmonizing fused global scales on the
+ * checkpoint side) and "Main Findings" (one calibrated global scale per module; fused serving).
+ * Reading: the smallest encode-direction scale belongs to the module with the widest calibrated
+ * range, so no block scale of any module saturates when re-encoded under it; the module that owns
+ * g* keeps its bytes.
+ *
+ *   codes, scales, codes_out, scales_out   as nvfp4_requantize, rows = N, cols = K.
+ *   seg_gscale   device, nseg floats.
+ *   seg_offsets  HOST, nseg + 1 int64 rising strictly from 0 to N (read during the call only).
+ *   nseg         1 .. NVFP4_MAX_SEGMENTS.
+ *   shared_gscale  device, one float, not one of seg_gscale[0 .. nseg).  Not written when N or K
+ *                is 0 (nothing is enqueued).
+ * Bit-exact.  Errors as fused_nvfp4_gemm for the segment table; EINVAL when shared_gscale lies
+ * inside the seg_gscale table.
+ */
+nvfp4_status nvfp4_harmonize_segments(const uint8_t* codes, const uint8_t* scales,
+                                      const float* seg_gscale, const int64_t* seg_offsets,
+                                      int nseg, int64_t N, int64_t K, float* shared_gscale,
+                                      uint8_t* codes_out, uint8_t* scales_out, void* stream);
+
+/*
  * nvfp4_kv_fp8_store -- encode new tokens' keys (and values) to FP8 E4M3 under one static scale per
  * tensor and write each token's row into its cache slot.
  *
@@ -183,7 +279,8 @@ nvfp4_status fused_nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
  *
  *   key, value    device, [tokens, width] of dtype (F32, BF16 or F16), row pitches ld_key,
  *                 ld_value (elements, >= width, a multiple of 16 bytes); 16-byte aligned.  value
- *                 may be NULL (keys only); then value_scale and value_cache are NULL as well.
+ *                 may be absent (keys only): value_scale NULL, and then value and value_cache
+ *                 NULL as well.
  *   tokens, width tokens >= 0; width >= 0, a multiple of 16, at most 2^24.
  *   key_scale, value_scale  device, one float each, positive and finite (not checked).
  *   slot_mapping  device, tokens int64 (8-byte aligned), or NULL for slot t = token t.  Token t's
@@ -193,7 +290,9 @@ nvfp4_status fused_nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
  *                 >= width, a multiple of 16); 16-byte aligned.  A paged cache
  *                 [blocks, block_size, heads, head_dim] is this table with width = heads*head_dim
  *                 and slot = block * block_size + position in block.
- * Errors as nvfp4_quantize; EINVAL also when only some of value/value_scale/value_cache are NULL.
+ * Errors as nvfp4_quantize; EINVAL also when value_scale is NULL but value or value_cache is not,
+ * or value_scale is given for a non-empty problem without value or value_cache.  The cache
+ * pointers may be NULL when num_slots is 0 (nothing is stored).
  */
 nvfp4_status nvfp4_kv_fp8_store(const void* key, const void* value, nvfp4_dtype dtype,
                                 int64_t tokens, int64_t width, int64_t ld_key, int64_t ld_value,

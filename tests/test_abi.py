@@ -236,3 +236,91 @@ def test_kv_load_validation():
     assert _kvl(ld_out=33) == nv.NVFP4_EALIGN  # 132-byte f32 row pitch
     assert _kvl(slots=P + 4) == nv.NVFP4_EALIGN
     assert _kvl(tokens=0) == nv.NVFP4_OK
+
+
+def test_empty_problems_accept_null_data_pointers():
+    lib = nv.load_library()
+    assert _q(x=None, codes=None, scales=None, rows=0) == nv.NVFP4_OK
+    assert _q(x=None, codes=None, scales=None, rows=4) == nv.NVFP4_EINVAL
+    assert _kvs(k=None, v=None, kc=None, vc=None, slots=None, tokens=0) == nv.NVFP4_OK
+    assert _kvl(c=None, out=None, slots=None, tokens=0) == nv.NVFP4_OK
+    assert lib.nvfp4_requantize(None, None, P, P, 0, 32, None, None, None) == nv.NVFP4_OK
+
+
+def _fk(**kw):
+    a = dict(x=P, dt=nv.NVFP4_BF16, rows=4, cols=32, ldx=32, g=P, dyn=0, out=P,
+             odt=nv.NVFP4_F32, ldo=32, s=None)
+    a.update(kw)
+    return nv.load_library().nvfp4_fake_quantize(a["x"], a["dt"], a["rows"], a["cols"], a["ldx"],
+                                                 a["g"], a["dyn"], a["out"], a["odt"], a["ldo"],
+                                                 a["s"])
+
+
+def test_fake_quantize_validation():
+    assert _fk(x=None) == nv.NVFP4_EINVAL
+    assert _fk(g=None) == nv.NVFP4_EINVAL
+    assert _fk(out=None) == nv.NVFP4_EINVAL
+    assert _fk(dt=7) == nv.NVFP4_EINVAL
+    assert _fk(odt=nv.NVFP4_F16) == nv.NVFP4_EINVAL
+    assert _fk(dyn=3) == nv.NVFP4_EINVAL
+    assert _fk(cols=24, ldx=24, ldo=24) == nv.NVFP4_ESHAPE
+    assert _fk(ldo=16) == nv.NVFP4_ESHAPE
+    assert _fk(ldx=16) == nv.NVFP4_ESHAPE
+    assert _fk(out=P + 8) == nv.NVFP4_EALIGN
+    assert _fk(ldo=33) == nv.NVFP4_EALIGN
+    assert _fk(x=P + 4) == nv.NVFP4_EALIGN
+    assert _fk(rows=0) == nv.NVFP4_OK
+
+
+def _st(**kw):
+    a = dict(x=P, dt=nv.NVFP4_F32, rows=4, cols=32, ldx=32, g=P, dyn=0, e=P, n=P, d=P, s=None)
+    a.update(kw)
+    return nv.load_library().nvfp4_quant_error_stats(a["x"], a["dt"], a["rows"], a["cols"], a["ldx"],
+                                                     a["g"], a["dyn"], a["e"], a["n"], a["d"],
+                                                     a["s"])
+
+
+def test_quant_error_stats_validation():
+    for k in ("x", "g", "e", "n", "d"):
+        assert _st(**{k: None}) == nv.NVFP4_EINVAL, k
+    assert _st(dt=9) == nv.NVFP4_EINVAL
+    assert _st(cols=8, ldx=8) == nv.NVFP4_ESHAPE
+    assert _st(rows=-2) == nv.NVFP4_ESHAPE
+    assert _st(e=P + 4) == nv.NVFP4_EALIGN
+    assert _st(d=P + 2) == nv.NVFP4_EALIGN
+    assert _st(ldx=33) == nv.NVFP4_EALIGN  # 132-byte f32 row pitch
+    assert _st(rows=0, e=None, n=None, d=None, x=None) == nv.NVFP4_OK
+
+
+def test_requantize_and_harmonize_validation():
+    lib = nv.load_library()
+    rq = lambda **kw: lib.nvfp4_requantize(*[kw.get(k, v) for k, v in (
+        ("c", P), ("sc", P), ("gi", P), ("go", P), ("rows", 4), ("cols", 32), ("co", P),
+        ("so", P), ("s", None))])
+    assert rq(gi=None) == nv.NVFP4_EINVAL
+    assert rq(go=None) == nv.NVFP4_EINVAL
+    assert rq(c=None) == nv.NVFP4_EINVAL
+    assert rq(so=None) == nv.NVFP4_EINVAL
+    assert rq(cols=20) == nv.NVFP4_ESHAPE
+    assert rq(rows=-1) == nv.NVFP4_ESHAPE
+    assert rq(c=P + 4) == nv.NVFP4_EALIGN
+    assert rq(co=P + 2) == nv.NVFP4_EALIGN
+    assert rq(rows=0) == nv.NVFP4_OK
+
+    def hz(offs=(0, 16, 32), nseg=None, N=32, K=64, g=P, sh=P + 256, **kw):
+        arr = (ctypes.c_int64 * len(offs))(*offs)
+        nseg = len(offs) - 1 if nseg is None else nseg
+        return lib.nvfp4_harmonize_segments(kw.get("c", P), kw.get("sc", P), g, arr, nseg, N, K, sh,
+                                            kw.get("co", P), kw.get("so", P), None)
+    assert hz(g=None) == nv.NVFP4_EINVAL
+    assert hz(sh=None) == nv.NVFP4_EINVAL
+    assert hz(sh=P + 4) == nv.NVFP4_EINVAL  # inside the segment-scale table
+    assert hz(nseg=0) == nv.NVFP4_EINVAL
+    assert hz(nseg=17) == nv.NVFP4_EINVAL
+    assert hz(offs=(0, 16, 16)) == nv.NVFP4_ESHAPE
+    assert hz(offs=(0, 40, 32)) == nv.NVFP4_ESHAPE
+    assert hz(offs=(1, 16, 32)) == nv.NVFP4_ESHAPE
+    assert hz(K=40) == nv.NVFP4_ESHAPE
+    assert hz(c=P + 4) == nv.NVFP4_EALIGN
+    assert hz(g=P + 2) == nv.NVFP4_EALIGN
+    assert hz(N=0, offs=(0, 0), c=None, sc=None, co=None, so=None) == nv.NVFP4_OK
