@@ -241,6 +241,120 @@ def kv_store(args, torch, nv, W):
             "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": nbytes}
 
 
+def _timed(torch, steps, fn):
+    """Mean milliseconds per call of fn(i) over `steps` calls back to back between HIP events."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def error_tools(args, torch, nv, W):
+    """Fake quantization, error statistics and harmonization: their throughput, and the error
+    figures they produce on the synthetic workloads next to the bands the pages report.
+
+    * fake_quantize: the 8192 x 5120 bf16 prefill activations -> f32, static scale (bytes: bf16 in,
+      f32 out); 3 rotating input/output sets (755 MB, beyond the last-level cache).
+    * error_stats: the same activations, 3 rotating inputs (bytes: bf16 in).
+    * harmonize: the five-module GDN in_proj weight (8288 x 5120 NVFP4), 8 rotating sets (bytes:
+      codes + scales read and written).
+    * statistics: per-token activation error (mean over tokens of sqrt(err2 / norm2)) and the share
+      of dominated blocks for the GDN in_proj and MLP gate+up activations; the weight error of each
+      GDN in_proj module; the fused GDN in_proj product (M = 4096) with the exact per-module
+      epilogue, after harmonization with one shared scale, and with the defective maximum scale,
+      as relative Frobenius errors against the exact per-module product."""
+    import numpy as np
+
+    dev = "cuda:0"
+    out = {}
+    w3 = W.WORKLOADS[3]
+    a = W.activations(w3)
+    ga = torch.tensor([np.float32(2688.0 / np.abs(a).max())], device=dev)
+    R = 3
+    ins = [torch.from_numpy(a).to(torch.bfloat16).to(dev) for _ in range(R)]
+    outs = [torch.empty((w3.M, w3.K), dtype=torch.float32, device=dev) for _ in range(R)]
+    del a
+    for i in range(args.warmup):
+        nv.nvfp4_fake_quantize(ins[i % R], ga, out=outs[i % R])
+    torch.cuda.synchronize()
+    ms = _timed(torch, args.steps, lambda i: nv.nvfp4_fake_quantize(ins[i % R], ga, out=outs[i % R]))
+    nbytes = w3.M * w3.K * (2 + 4)
+    out["fake_quantize"] = {"bound": "hbm", "shape": [w3.M, w3.K], "us": round(ms * 1e3, 2),
+                            "GB/s": round(nbytes / ms / 1e6, 1),
+                            "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "bytes": nbytes}
+    del outs
+    for i in range(args.warmup):
+        nv.nvfp4_quant_error_stats(ins[i % R], ga)
+    torch.cuda.synchronize()
+    ms = _timed(torch, args.steps, lambda i: nv.nvfp4_quant_error_stats(ins[i % R], ga))
+    nbytes = w3.M * w3.K * 2
+    out["error_stats"] = {"bound": "hbm", "shape": [w3.M, w3.K], "us": round(ms * 1e3, 2),
+                          "GB/s": round(nbytes / ms / 1e6, 1),
+                          "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "bytes": nbytes}
+    stats = {}
+    e2, n2, dom, _ = nv.nvfp4_quant_error_stats(ins[0], None)
+    stats["mlp_gate_up_act_per_token_err"] = round(float(torch.sqrt(e2 / n2).mean()), 4)
+    stats["mlp_gate_up_dominated_block_share"] = round(float(dom.sum()) / (w3.M * w3.K / 16), 4)
+    del ins
+
+    w2 = W.WORKLOADS[2]
+    a2 = torch.from_numpy(W.activations(w2)).to(torch.bfloat16).to(dev)
+    e2, n2, dom, _ = nv.nvfp4_quant_error_stats(a2, None)
+    stats["gdn_in_proj_act_per_token_err"] = round(float(torch.sqrt(e2 / n2).mean()), 4)
+    stats["gdn_in_proj_dominated_block_share"] = round(float(dom.sum()) / (w2.M * w2.K / 16), 4)
+    segs = w2.seg_offsets
+    wc = torch.empty((w2.N, w2.K // 2), dtype=torch.uint8, device=dev)
+    wsc = torch.empty((w2.N, w2.K // 16), dtype=torch.uint8, device=dev)
+    gw = torch.empty(len(segs) - 1, dtype=torch.float32, device=dev)
+    werr = []
+    for j in range(len(segs) - 1):
+        wd = torch.from_numpy(W.weights(w2, slice(segs[j], segs[j + 1]))).to(torch.bfloat16).to(dev)
+        _, _, g = nv.nvfp4_quantize(wd, None, wc[segs[j]:segs[j + 1]], wsc[segs[j]:segs[j + 1]])
+        gw[j:j + 1].copy_(g)
+        e2, n2, _, _ = nv.nvfp4_quant_error_stats(wd, g)
+        werr.append(round(float(torch.sqrt(e2.sum() / n2.sum())), 4))
+        del wd
+    stats["gdn_in_proj_weight_err_per_module"] = werr
+    ac, as_, gA = nv.nvfp4_quantize(a2)
+    exact = nv.fused_nvfp4_gemm(ac, as_, gA, wc, wsc, gw, segs)
+    hc, hs, gs = nv.nvfp4_harmonize_segments(wc, wsc, gw, segs)
+    harm = nv.fused_nvfp4_gemm(ac, as_, gA, hc, hs, gs.repeat(len(segs) - 1), segs)
+    bug = nv.fused_nvfp4_gemm(ac, as_, gA, wc, wsc, gw.max().repeat(len(segs) - 1), segs)
+    nrm = torch.linalg.vector_norm(exact)
+    stats["gdn_in_proj_fused_product_rel_err"] = {
+        "per_module_epilogue": 0.0,
+        "harmonized_shared_scale": round(float(torch.linalg.vector_norm(harm - exact) / nrm), 5),
+        "defective_max_scale": round(float(torch.linalg.vector_norm(bug - exact) / nrm), 5)}
+    stats["pages_bands"] = {"per_token_act_err": [0.075, 0.092], "weight_err": [0.105, 0.119],
+                            "dominated_block_share": [0.10, 0.32]}
+    out["statistics"] = stats
+    del a2, ac, as_, exact, harm, bug, hc, hs
+
+    RH = 8
+    sets = [(wc.clone(), wsc.clone(), torch.empty_like(wc), torch.empty_like(wsc),
+             torch.empty(1, dtype=torch.float32, device=dev)) for _ in range(RH)]
+    for i in range(args.warmup):
+        c, sc, co, so, g1 = sets[i % RH]
+        nv.nvfp4_harmonize_segments(c, sc, gw, segs, co, so, g1)
+    torch.cuda.synchronize()
+
+    def harm_call(i):
+        c, sc, co, so, g1 = sets[i % RH]
+        nv.nvfp4_harmonize_segments(c, sc, gw, segs, co, so, g1)
+
+    ms = _timed(torch, args.steps, harm_call)
+    nbytes = 2 * w2.N * w2.K * 9 // 16
+    out["harmonize"] = {"bound": "hbm", "shape": [w2.N, w2.K], "us": round(ms * 1e3, 2),
+                        "GB/s": round(nbytes / ms / 1e6, 1),
+                        "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "bytes": nbytes}
+    del sets, wc, wsc
+    torch.cuda.empty_cache()
+    return out
+
+
 def copy_calibration(args, torch):
     """A plain device-to-device copy of 1 GiB, the reference for scaling HBM byte counters:
     it reads and writes exactly 2^30 bytes per launch."""
@@ -318,7 +432,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--only", choices=("all", "prefill", "decode", "silu", "kv", "copy"),
+    ap.add_argument("--only", choices=("all", "prefill", "decode", "silu", "kv", "errors",
+                                      "copy"),
                     default="all",
                     help="run one part (for profiler runs); 'copy' is the counter calibration copy")
     args = ap.parse_args()
@@ -350,12 +465,16 @@ def main():
     if args.only == "kv":
         print(json.dumps({"kv_fp8_store": kv_store(args, torch, nv, W)}), flush=True)
         return
+    if args.only == "errors":
+        print(json.dumps(error_tools(args, torch, nv, W)), flush=True)
+        return
 
     p = prefill(args, torch, nv, W)
     run_rest = args.only == "all"
     dec = decode(args, torch, nv, W) if run_rest and not args.no_decode else None
     silu = silu_quantize(args, torch, nv, W) if run_rest else None
     kv = kv_store(args, torch, nv, W) if run_rest else None
+    errs = error_tools(args, torch, nv, W) if run_rest else None
     cpu = cpu_baseline() if run_rest and not args.no_cpu_baseline else None
 
     w = p["w"]
@@ -390,6 +509,10 @@ def main():
         "decode": dec,
         "silu_mul_quantize": silu,
         "kv_fp8_store": kv,
+        "fake_quantize": errs and errs["fake_quantize"],
+        "error_stats": errs and errs["error_stats"],
+        "harmonize": errs and errs["harmonize"],
+        "error_statistics": errs and errs["statistics"],
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -78,29 +78,33 @@ constexpr int elem_bytes() {
 // round-to-nearest-even of s * 512 (exact product).  In the normal range the code is the binary32
 // pattern rounded to 3 mantissa bits (nearest-even on the 20 dropped bits, carries into the
 // exponent are the correct binade change) and rebiased: code = (bits >> 20) - ((127 - 7) << 3).
+// Both candidates are formed and one is selected, so the code has no branches (a per-element
+// branch costs a divergent exec-mask sequence on this target).
 __device__ __forceinline__ uint32_t e4m3_encode(float s) {
-  if (!(s < 448.0f)) return 0x7Eu;
-  if (s < 0.015625f) return (uint32_t)__builtin_rintf(s * 512.0f);
-  uint32_t u = __float_as_uint(s);
-  u = u + 0x7FFFFu + ((u >> 20) & 1u);
-  return (u >> 20) - 960u;
+  const uint32_t sub = (uint32_t)__builtin_rintf(s * 512.0f);
+  const uint32_t u = __float_as_uint(s);
+  const uint32_t nrm = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - 960u;
+  const uint32_t c = s < 0.015625f ? sub : nrm;
+  return s < 448.0f ? c : 0x7Eu;
 }
 
 // Exact binary32 value of an E4M3 code 0x00..0x7E.
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
-  return c < 8u ? (float)c * 0.001953125f : __uint_as_float((c + 960u) << 20);
+  const float sub = (float)c * 0.001953125f;
+  const float nrm = __uint_as_float((c + 960u) << 20);
+  return c < 8u ? sub : nrm;
 }
 
 // Non-negative binary32 (or +inf) -> E2M1 magnitude index: nearest, ties to the even index,
 // saturating at 6.  Below 1 the grid is {0, 0.5, 1}: round-to-nearest-even of 2y.  From 1 up the
 // grid keeps one mantissa bit: round the pattern to 1 mantissa bit (nearest-even on 22 dropped
 // bits) and read exponent and that bit as the index, (bits >> 22) - 252, clamped at 7.
+// Branch-free as e4m3_encode.
 __device__ __forceinline__ uint32_t e2m1_index(float y) {
-  if (y < 1.0f) return (uint32_t)__builtin_rintf(y * 2.0f);
-  uint32_t u = __float_as_uint(y);
-  u = (u + 0x1FFFFFu + ((u >> 22) & 1u)) >> 22;
-  uint32_t i = u - 252u;
-  return i > 7u ? 7u : i;
+  const uint32_t lo = (uint32_t)__builtin_rintf(y * 2.0f);
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t hi = min(((u + 0x1FFFFFu + ((u >> 22) & 1u)) >> 22) - 252u, 7u);
+  return y < 1.0f ? lo : hi;
 }
 
 // Encode 16 binary32 values as block b: one E4M3 scale byte and 8 code bytes.
@@ -130,7 +134,9 @@ __device__ __forceinline__ void encode_block(const float (&v)[16], float g, floa
 
 // Exact binary32 value of an E2M1 magnitude index 0..7: {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
 __device__ __forceinline__ float e2m1_value(uint32_t i) {
-  return i < 2u ? 0.5f * (float)i : __uint_as_float((((i >> 1) + 126u) << 23) | ((i & 1u) << 22));
+  const float lo = 0.5f * (float)i;
+  const float hi = __uint_as_float((((i >> 1) + 126u) << 23) | ((i & 1u) << 22));
+  return i < 2u ? lo : hi;
 }
 
 __device__ __forceinline__ float read_global_scale(const float* g, int dynamic) {

@@ -11,7 +11,10 @@
 //   dominated block    2 * amax^2 > sum of the 16 squares, in binary64, summed in element order.
 //
 // Work split.  Fake quantization and re-encoding: one thread per 16-element block, consecutive
-// threads on consecutive blocks of a row (as the encoder), bound by HBM.  Statistics: one wavefront
+// threads on consecutive blocks of a row (as the encoder), bound by HBM.  The fake-quantized
+// output (64 or 32 bytes per thread) leaves through LDS so that every store instruction of a
+// wavefront writes 1 KiB of consecutive memory; a lane writing its own 64 bytes in four 16-byte
+// stores runs at less than half the rate.  Statistics: one wavefront
 // per row, lane l taking blocks l, l + 64, ... and accumulating in binary64; the lanes' sums meet in
 // a fixed butterfly, so the result is deterministic.
 #include "codec.h"
@@ -24,6 +27,35 @@ using namespace codec;
 
 constexpr int kThreads = 256;
 
+// Dequantized values fl(V * sd / g) of the 16 E2M1 codes c[i] (sign in bit 3) of a block with
+// decoded scale sd under global scale g.  Every E2M1 magnitude is 2^k * m with m in {1, 1.5} and
+// k in {-1, 0, 1, 2}, and in the binary32 normal range rounding commutes with scaling by a power
+// of two, so fl(2^k * m * sd / g) = 2^k * fl(m * sd / g): two correctly rounded divisions per
+// block (t1 = fl(sd / g), t15 = fl(1.5 sd / g)) and an exact ldexp per element.  When t1 / 2 or
+// 4 * t15 would leave the normal range (then some scaled value might), every element is divided
+// on its own instead.
+__device__ __forceinline__ void dequant_block(const uint32_t (&c)[16], float sd, float g,
+                                              float (&xh)[16]) {
+  const float t1 = sd / g;
+  const float t15 = (1.5f * sd) / g;  // 1.5 * sd is exact
+  if (t1 >= 0x1p-125f && t15 <= 0x1p125f) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t i = c[k] & 7u;
+      const float base = (i & 1u) && i >= 2u ? t15 : t1;
+      const int e = i >= 2u ? (int)(i >> 1) - 1 : -1;
+      const float v = i == 0u ? 0.0f : __builtin_ldexpf(base, e);
+      xh[k] = __uint_as_float(__float_as_uint(v) | ((c[k] & 8u) << 28));
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float v = (e2m1_value(c[k] & 7u) * sd) / g;  // V * sd is exact
+      xh[k] = __uint_as_float(__float_as_uint(v) | ((c[k] & 8u) << 28));
+    }
+  }
+}
+
 // Encode the 16 values of a block (as the encoder does) and return their dequantized values.
 __device__ __forceinline__ void fake_quantize_block(const float (&v)[16], float g, float gs6,
                                                     float (&xh)[16]) {
@@ -32,12 +64,11 @@ __device__ __forceinline__ void fake_quantize_block(const float (&v)[16], float 
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
   const float sd = e4m3_value(e4m3_encode(amax * gs6));
   const float r = sd > 0.0f ? g / sd : 0.0f;
+  uint32_t c[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float q = e2m1_value(e2m1_index(fabsf(v[i]) * r)) * sd;  // exact
-    const float qs = __uint_as_float(__float_as_uint(q) | (__float_as_uint(v[i]) & 0x80000000u));
-    xh[i] = qs / g;  // correctly rounded division
-  }
+  for (int i = 0; i < 16; ++i)
+    c[i] = e2m1_index(fabsf(v[i]) * r) | ((__float_as_uint(v[i]) >> 28) & 8u);
+  dequant_block(c, sd, g, xh);
 }
 
 __device__ __forceinline__ uint32_t bf16_rne(float x) {
@@ -50,17 +81,25 @@ __global__ void __launch_bounds__(kThreads)
 fake_quantize_kernel(const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t nb, uint32_t total,
                      const float* __restrict__ gptr, int dynamic, uint8_t* __restrict__ out,
                      int64_t ldo_bytes) {
+  // per-thread output: 64 bytes (f32) or 32 bytes (bf16), staged in LDS so that each store
+  // instruction of a wavefront writes 64 consecutive 16-byte pieces
+  constexpr int kOutBytes = BF16_OUT ? 32 : 64;
+  constexpr int kPieces = kOutBytes / 16;
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kThreads * kOutBytes];
   const uint32_t b = blockIdx.x * kThreads + threadIdx.x;
-  if (b >= total) return;
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t wave = threadIdx.x >> 6;
+  uint8_t* ws = stage + wave * 64 * kOutBytes;
   const float g = read_global_scale(gptr, dynamic);
   const float gs6 = g / 6.0f;
-  const uint32_t row = b / nb;
-  const uint32_t j = b - row * nb;
+  const uint32_t bb = b < total ? b : total - 1;
+  const uint32_t row = bb / nb;
+  const uint32_t j = bb - row * nb;
   float v[16], xh[16];
   load_block<DT>(x + (int64_t)row * ldx_bytes + (int64_t)j * 16 * elem_bytes<DT>(), v);
   fake_quantize_block(v, g, gs6, xh);
   if constexpr (BF16_OUT) {
-    u32x4* d = reinterpret_cast<u32x4*>(out + (int64_t)row * ldo_bytes + (int64_t)j * 32);
+    u32x4* d = reinterpret_cast<u32x4*>(ws + lane * 32);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       u32x4 o;
@@ -68,10 +107,10 @@ fake_quantize_kernel(const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t 
       o.y = bf16_rne(xh[8 * i + 2]) | (bf16_rne(xh[8 * i + 3]) << 16);
       o.z = bf16_rne(xh[8 * i + 4]) | (bf16_rne(xh[8 * i + 5]) << 16);
       o.w = bf16_rne(xh[8 * i + 6]) | (bf16_rne(xh[8 * i + 7]) << 16);
-      __builtin_nontemporal_store(o, d + i);
+      d[i] = o;
     }
   } else {
-    f32x4* d = reinterpret_cast<f32x4*>(out + (int64_t)row * ldo_bytes + (int64_t)j * 64);
+    f32x4* d = reinterpret_cast<f32x4*>(ws + lane * 64);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f32x4 o;
@@ -79,7 +118,22 @@ fake_quantize_kernel(const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t 
       o.y = xh[4 * i + 1];
       o.z = xh[4 * i + 2];
       o.w = xh[4 * i + 3];
-      __builtin_nontemporal_store(o, d + i);
+      d[i] = o;
+    }
+  }
+  // LDS accesses of one wavefront complete in order; the stage rows belong to this wavefront
+  const uint32_t wb = blockIdx.x * kThreads + wave * 64;  // first block of the wavefront
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i) {
+    const uint32_t q = i * 64 + lane;           // piece index within the wavefront's output
+    const uint32_t t = q / kPieces;             // owning lane
+    const uint32_t ob = wb + t;
+    if (ob < total) {
+      const uint32_t orow = ob / nb;
+      const uint32_t oj = ob - orow * nb;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(ws + q * 16);
+      __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(
+          out + (int64_t)orow * ldo_bytes + (int64_t)oj * kOutBytes + (q % kPieces) * 16));
     }
   }
 }
@@ -149,15 +203,12 @@ requantize_kernel(const uint8_t* codes, const uint8_t* scales, uint32_t nb, uint
   const float go = g_out ? *g_out : gmin;
   if (g_shared && b == 0) *g_shared = go;
   const uint2 cw = *reinterpret_cast<const uint2*>(codes + (int64_t)b * 8);
-  const float sd = e4m3_value(scales[b]);
   const uint32_t w[2] = {cw.x, cw.y};
-  float xh[16];
+  uint32_t c[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t c = (w[i >> 3] >> (4 * (i & 7))) & 0xFu;
-    const float q = e2m1_value(c & 7u) * sd;  // exact
-    xh[i] = __uint_as_float(__float_as_uint(q) | ((c & 8u) << 28)) / gi;
-  }
+  for (int i = 0; i < 16; ++i) c[i] = (w[i >> 3] >> (4 * (i & 7))) & 0xFu;
+  float xh[16];
+  dequant_block(c, e4m3_value(scales[b]), gi, xh);
   encode_block(xh, go, go / 6.0f, b, codes_out, scales_out);
 }
 

@@ -79,6 +79,33 @@ def test_fake_quantize_edge_cases(out):
         _assert_bits(got, ref, f"edge g={g} out={out}")
 
 
+def test_fake_quantize_extreme_scales():
+    """Blocks whose dequantized values leave the binary32 normal range (tiny values under a huge
+    scale, huge values under a tiny one): the kernel divides each element there instead of scaling
+    two per-block quotients."""
+    rng = np.random.default_rng(91)
+    tiny = (rng.uniform(-1, 1, (8, 32)) * 2.3e-38).astype(np.float32)
+    huge = (rng.uniform(-1, 1, (8, 32)) * 3e38).astype(np.float32)
+    mixed = np.concatenate([tiny[:, :16], huge[:, :16]], axis=1)
+    for x, g in ((tiny, 1e36), (huge, 1e-36), (mixed, 1e-36), (mixed, 1e36), (huge, 8.9e-36)):
+        log(f"fake quantize extreme g={g}")
+        for out in ("f32", "bf16"):
+            got, _ = _fake(x, "f32", np.float32(g), out)
+            ref, _ = _ref_fake(x, np.float32(g), out)
+            _assert_bits(got, ref, f"extreme g={g} out={out}")
+    c, s_, gg = oracle.quantize(huge, np.float32(1e-36))
+    for g_out in (np.float32(2e-36), np.float32(1e-37)):
+        import torch
+
+        import bit_block_scaled_nvfp4_amd as nv
+
+        rc, rs = oracle.requantize(c, s_, gg, g_out)
+        oc, os_ = nv.nvfp4_requantize(torch.from_numpy(c).to(DEV), torch.from_numpy(s_).to(DEV),
+                                      scalar(gg), scalar(g_out))
+        torch.cuda.synchronize()
+        assert_codes_equal((oc.cpu().numpy(), os_.cpu().numpy(), 0), (rc, rs, 0), "extreme requantize")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("shape", [(1, 16), (37, 144), (300, 1024), (64, 5120)])
 def test_fake_quantize_ragged(dtype, shape):
