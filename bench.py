@@ -355,6 +355,23 @@ def error_tools(args, torch, nv, W):
     return out
 
 
+def vendor_bf16_gemm(args, torch, W):
+    """The vendor dense bf16 GEMM (torch.matmul -> hipBLASLt) on the prefill shape, M = 8192,
+    K = 5120, N = 34816, operands already bf16 in HBM: a calibration of the MFMA rate this GPU
+    sustains under its power limit, beside the NVFP4 product (which also decodes its operands)."""
+    w = W.WORKLOADS[3]
+    a = torch.randn(w.M, w.K, device="cuda:0", dtype=torch.bfloat16)
+    b = torch.randn(w.N, w.K, device="cuda:0", dtype=torch.bfloat16)
+    for _ in range(max(args.warmup, 2)):
+        c = a @ b.t()
+    torch.cuda.synchronize()
+    ms = _timed(torch, args.steps, lambda i: a @ b.t())
+    del a, b, c
+    torch.cuda.empty_cache()
+    tf = w.flops / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "TFLOP/s": round(tf, 1), "frac_of_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+
+
 def copy_calibration(args, torch):
     """A plain device-to-device copy of 1 GiB, the reference for scaling HBM byte counters:
     it reads and writes exactly 2^30 bytes per launch."""
@@ -433,7 +450,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--only", choices=("all", "prefill", "decode", "silu", "kv", "errors",
-                                      "copy"),
+                                      "vendor", "copy"),
                     default="all",
                     help="run one part (for profiler runs); 'copy' is the counter calibration copy")
     args = ap.parse_args()
@@ -468,6 +485,9 @@ def main():
     if args.only == "errors":
         print(json.dumps(error_tools(args, torch, nv, W)), flush=True)
         return
+    if args.only == "vendor":
+        print(json.dumps({"vendor_bf16_gemm": vendor_bf16_gemm(args, torch, W)}), flush=True)
+        return
 
     p = prefill(args, torch, nv, W)
     run_rest = args.only == "all"
@@ -475,6 +495,7 @@ def main():
     silu = silu_quantize(args, torch, nv, W) if run_rest else None
     kv = kv_store(args, torch, nv, W) if run_rest else None
     errs = error_tools(args, torch, nv, W) if run_rest else None
+    vendor = vendor_bf16_gemm(args, torch, W) if run_rest else None
     cpu = cpu_baseline() if run_rest and not args.no_cpu_baseline else None
 
     w = p["w"]
@@ -513,6 +534,8 @@ def main():
         "error_stats": errs and errs["error_stats"],
         "harmonize": errs and errs["harmonize"],
         "error_statistics": errs and errs["statistics"],
+        "vendor_bf16_gemm": vendor and dict(vendor, nvfp4_product_over_vendor=round(
+            achieved / vendor["TFLOP/s"], 4)),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
