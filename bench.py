@@ -95,7 +95,25 @@ def prefill(args, torch, nv, W):
     q_ms = e0.elapsed_time(e1) / args.steps
     flops = w.flops
     q_bytes = w.M * w.K * (2 + 9 / 16)
-    return dict(w=w, ms_step=ms_step, gemm_ms=g_ms, quant_ms=q_ms, flops=flops, q_bytes=q_bytes)
+    # the vendor dense bf16 GEMM of the same shape (torch.matmul -> hipBLASLt), timed in turns with
+    # the NVFP4 product so both see the same clock and temperature
+    wb = torch.randn(w.N, w.K, device=dev, dtype=torch.bfloat16)
+    for _ in range(2):
+        ad @ wb.t()
+    torch.cuda.synchronize()
+    ours, vend = [], []
+    for _ in range(3):
+        ours.append(_timed(torch, args.steps,
+                           lambda i: nv.fused_nvfp4_gemm(ac, as_, ga, wc, ws, gw, segs, out=C)))
+        vend.append(_timed(torch, args.steps, lambda i: ad @ wb.t()))
+    del wb
+    torch.cuda.empty_cache()
+    vendor = {"ms": round(min(vend), 4), "TFLOP/s": round(flops / min(vend) / 1e9, 1),
+              "frac_of_peak": round(flops / min(vend) / 1e9 / MFMA_F16_PEAK_TFLOPS, 4),
+              "nvfp4_product_ms_same_turns": round(min(ours), 4),
+              "nvfp4_product_over_vendor": round(min(vend) / min(ours), 4)}
+    return dict(w=w, ms_step=ms_step, gemm_ms=g_ms, quant_ms=q_ms, flops=flops, q_bytes=q_bytes,
+                vendor=vendor)
 
 
 def decode(args, torch, nv, W):
@@ -410,7 +428,7 @@ def traffic_from_profile(kernel_files, summary):
         return None
 
 
-def cpu_baseline(rows: int = 48):
+def cpu_baseline(rows: int = 112):
     """The oracle as it stands, on a bounded sample of the same workload: encode `rows` activation
     rows and form their exact product with all 34816 output columns (the weights are encoded
     beforehand, untimed, as on the GPU).  NumPy's int64 matmul runs on one thread."""
@@ -495,7 +513,6 @@ def main():
     silu = silu_quantize(args, torch, nv, W) if run_rest else None
     kv = kv_store(args, torch, nv, W) if run_rest else None
     errs = error_tools(args, torch, nv, W) if run_rest else None
-    vendor = vendor_bf16_gemm(args, torch, W) if run_rest else None
     cpu = cpu_baseline() if run_rest and not args.no_cpu_baseline else None
 
     w = p["w"]
@@ -534,8 +551,7 @@ def main():
         "error_stats": errs and errs["error_stats"],
         "harmonize": errs and errs["harmonize"],
         "error_statistics": errs and errs["statistics"],
-        "vendor_bf16_gemm": vendor and dict(vendor, nvfp4_product_over_vendor=round(
-            achieved / vendor["TFLOP/s"], 4)),
+        "vendor_bf16_gemm": p["vendor"],
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
