@@ -27,9 +27,11 @@ nvfp4_status check_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const f
                         const uint8_t* w_codes, const uint8_t* w_scales, const float* seg_gscale,
                         const int64_t* seg_offsets, int nseg, int64_t M, int64_t N, int64_t K,
                         const void* c, int c_dtype, int64_t ldc) {
-  if (!a_codes || !a_scales || !a_gscale || !w_codes || !w_scales || !seg_gscale || !seg_offsets ||
-      !c)
-    return NVFP4_EINVAL;
+  if (!a_gscale || !seg_gscale || !seg_offsets) return NVFP4_EINVAL;
+  // operands of an empty product may have no storage
+  if (M != 0 && (!a_codes || !a_scales)) return NVFP4_EINVAL;
+  if (N != 0 && (!w_codes || !w_scales)) return NVFP4_EINVAL;
+  if (M != 0 && N != 0 && !c) return NVFP4_EINVAL;
   if (!valid_out_dtype(c_dtype)) return NVFP4_EINVAL;
   if (nseg < 1 || nseg > NVFP4_MAX_SEGMENTS) return NVFP4_EINVAL;
   if (M < 0 || N < 0 || K <= 0 || K % 16 != 0) return NVFP4_ESHAPE;
@@ -335,6 +337,6 @@ const char* nvfp4_status_string(nvfp4_status s) {
   return "NVFP4: unknown status";
 }
 
-int nvfp4_version(void) { return 100; }
+int nvfp4_version(void) { return 200; }
 
 }  // extern "C"

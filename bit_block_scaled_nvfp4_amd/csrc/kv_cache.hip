@@ -16,45 +16,15 @@
 // wave (L the power of two >= width/16, at most 64), so a wave covers 64/L whole tokens when rows are
 // short and a 64-chunk stretch of one token when they are long; loads and stores of a wave are
 // contiguous per token.  The kernels are bound by HBM bandwidth (3 bytes moved per bf16 element).
+#include "codec.h"
 #include "nvfp4_internal.h"
 
 namespace nvfp4 {
 namespace {
 
+using namespace codec;
+
 constexpr int kThreads = 256;
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-template <nvfp4_dtype DT>
-__device__ __forceinline__ void load16(const uint8_t* p, float (&v)[16]) {
-  if constexpr (DT == NVFP4_F32) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 q = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + i);
-      v[4 * i + 0] = q.x;
-      v[4 * i + 1] = q.y;
-      v[4 * i + 2] = q.z;
-      v[4 * i + 3] = q.w;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + i);
-      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if constexpr (DT == NVFP4_BF16) {
-          v[8 * i + 2 * j + 0] = __uint_as_float(w[j] << 16);
-          v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-        } else {
-          v[8 * i + 2 * j + 0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[j] & 0xFFFFu));
-          v[8 * i + 2 * j + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[j] >> 16));
-        }
-      }
-    }
-  }
-}
 
 struct KvStoreArgs {
   const uint8_t* src[2];  // key, value rows (bytes)
@@ -87,7 +57,7 @@ __global__ void __launch_bounds__(kThreads) kv_store_kernel(KvStoreArgs a) {
   // the row is loaded before the slot is known, so both loads are in flight together
   constexpr int kEb = DT == NVFP4_F32 ? 4 : 2;
   float v[16];
-  load16<DT>(a.src[z] + (int64_t)t * a.ld_src[z] + (int64_t)c * 16 * kEb, v);
+  load_block<DT>(a.src[z] + (int64_t)t * a.ld_src[z] + (int64_t)c * 16 * kEb, v);
   const int64_t slot = slot_of(a.slots, a.num_slots, t);
   const float inv = 1.0f / *a.scale[z];  // correctly rounded (built with IEEE division)
   uint32_t w[4];

@@ -155,6 +155,8 @@ def test_gemm_validation(fused):
     assert _g(fused, ws=P + 4) == E.NVFP4_EALIGN
     assert _g(fused, c=P + 4) == E.NVFP4_EALIGN
     assert _g(fused, M=0) == E.NVFP4_OK  # empty: nothing enqueued
+    assert _g(fused, M=0, ac=None, as_=None, c=None) == E.NVFP4_OK  # no storage when empty
+    assert _g(fused, M=0, ga=None) == E.NVFP4_EINVAL  # global scales are always required
 
 
 def test_fused_segment_validation():
