@@ -47,13 +47,18 @@ __device__ __forceinline__ half8_t decode8(uint32_t q, _Float16 s) {
   return r;
 }
 
-// Epilogue factor of output column n: 1 / (gA * gW[seg(n)]).
-__device__ __forceinline__ float column_alpha(const SegTable& seg, const float* seg_g, float ga,
-                                              int n) {
+// Segment (calibrated module) of output column n.
+__device__ __forceinline__ int column_segment(const SegTable& seg, int n) {
   int j = 0;
 #pragma unroll 1
   for (int t = 1; t < seg.nseg; ++t) j += (n >= seg.off[t]) ? 1 : 0;
-  return 1.0f / (ga * seg_g[j]);
+  return j;
+}
+
+// Epilogue factor of output column n: 1 / (gA * gW[seg(n)]).
+__device__ __forceinline__ float column_alpha(const SegTable& seg, const float* seg_g, float ga,
+                                              int n) {
+  return 1.0f / (ga * seg_g[column_segment(seg, n)]);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {

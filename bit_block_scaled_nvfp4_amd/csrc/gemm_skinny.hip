@@ -159,12 +159,6 @@ gemm_skinny_kernel(GemmArgs p, int ncols) {
   const int clast = cend - 1;
   const bool arow_valid = r < p.M;
 
-  // epilogue factors of this lane's columns, loaded first so their latency hides under the stream
-  float alpha[T];
-#pragma unroll
-  for (int tile = 0; tile < T; ++tile)
-    alpha[tile] = column_alpha(p.seg, p.seg_g, *p.a_g, min(c0 + tile * 16 + r, clast));
-
   // all block scales of the weight rows and of the M activation rows, copied once (coalesced:
   // 16-byte pieces of consecutive rows); older than every phase's instructions, so each phase's
   // wait covers them
@@ -184,6 +178,18 @@ gemm_skinny_kernel(GemmArgs p, int ncols) {
                                        asc + (s & ~63) * 16, 16, 0, 0);
     }
   }
+  // global scales for the epilogue factors 1 / (gA * gW[seg(n)]) of this lane's columns: issued
+  // here as vector loads, older than every phase's copies (so the phase waits cover them), and
+  // used only at the end -- nothing waits on them before the weight stream is under way
+  int zero = 0;
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(zero));  // a lane-varying index keeps the gA load a vector load
+#endif
+  const float ga = p.a_g[zero];
+  float gw[T];
+#pragma unroll
+  for (int tile = 0; tile < T; ++tile)
+    gw[tile] = p.seg_g[column_segment(p.seg, min(c0 + tile * 16 + r, clast))];
   __builtin_amdgcn_sched_barrier(0);
 
   uint4 aw[8];  // entries >= NPH are never touched
@@ -238,7 +244,7 @@ gemm_skinny_kernel(GemmArgs p, int ncols) {
   // output tile `wave`: lane holds column c0 + 16 * wave + (l % 16), rows 4 * (l / 16) + e
   const int n = c0 + wave * 16 + r;
   if (n >= cend) return;
-  const float al = wave == 0 ? alpha[0] : alpha[T - 1];
+  const float al = 1.0f / (ga * (wave == 0 ? gw[0] : gw[T - 1]));
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int m = 4 * g + e;
