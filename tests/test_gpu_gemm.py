@@ -83,7 +83,8 @@ def test_bf16_output():
         ac, as_, ga, wc, ws, gw, [0, 72]))
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 260, 256), (3, 70, 1024), (40, 33, 80)])
+@pytest.mark.parametrize("M,N,K", [(300, 260, 256), (3, 70, 1024), (40, 33, 80), (1, 70, 1024),
+                                   (2, 45, 2048)])
 @pytest.mark.parametrize("pad", [3, 8])
 @pytest.mark.parametrize("odt", ["f32", "bf16"])
 def test_output_view_with_row_pitch(M, N, K, pad, odt):
@@ -117,11 +118,15 @@ def test_output_view_with_row_pitch(M, N, K, pad, odt):
 @pytest.mark.parametrize("M,N,K", [
     (1, 5000, 1024), (4, 4100, 2048), (16, 8100, 1024), (3, 9000, 1024), (8, 3000, 7168),
     (2, 4500, 8192), (16, 5123, 1024),
+    # one or two activation rows: padding of 15 or 14 MFMA rows
+    (1, 5120, 5120), (2, 3001, 7168), (1, 7, 1024), (2, 33, 3072), (2, 9000, 2048),
+    (1, 16, 4096), (2, 40000, 1024),
 ])
 def test_skinny_column_split(M, N, K):
     """Decode-shaped products whose columns are split evenly over the compute units: workgroups of
     more than 16 columns (two MFMA tiles, the second partly empty), more than 32 columns per compute
-    unit, ragged last workgroups, and K up to the largest the skinny kernel takes."""
+    unit, ragged last workgroups, one column per workgroup, and K up to the largest the skinny
+    kernels take."""
     a = random_matrix(M * 11 + K, M, K, outlier_cols=max(1, K // 100))
     wt = random_matrix(N * 3 + K, N, K, std=0.02)
     enc = _encode(a, wt, [0, N])
@@ -141,6 +146,24 @@ def test_skinny_fused_equals_per_segment_calls_bitwise():
     parts = [_gpu_product(ac, as_, ga, wc[segs[j]:segs[j + 1]], ws[segs[j]:segs[j + 1]], [gw[j]],
                           [0, sizes[j]]) for j in range(len(sizes))]
     assert np.array_equal(fused, np.concatenate(parts, axis=1))
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_single_row_fused_equals_per_segment_calls_bitwise(M):
+    """One or two activation rows on the decode path: the fused product and the per-segment
+    products use different column splits and must agree bit for bit."""
+    K = 3072
+    sizes = [2048, 2048, 48, 48, 5]
+    segs = list(np.cumsum([0] + sizes))
+    a = random_matrix(50 + M, M, K, outlier_cols=20)
+    wt = random_matrix(51, segs[-1], K, std=0.02)
+    ac, as_, ga, wc, ws, gw = _encode(a, wt, segs)
+    fused = _gpu_product(ac, as_, ga, wc, ws, gw, segs)
+    parts = [_gpu_product(ac, as_, ga, wc[segs[j]:segs[j + 1]], ws[segs[j]:segs[j + 1]], [gw[j]],
+                          [0, sizes[j]]) for j in range(len(sizes))]
+    assert np.array_equal(fused, np.concatenate(parts, axis=1))
+    R = oracle.gemm_exact(ac, as_, ga, wc, ws, gw, segs)
+    check_gemm(fused, R, oracle.gemm_abs_bound(ac, as_, ga, wc, ws, gw, segs), f"decode M={M}")
 
 
 def test_fused_equals_per_segment_calls_bitwise():
