@@ -107,10 +107,32 @@ __device__ __forceinline__ uint32_t e2m1_index(float y) {
   return y < 1.0f ? lo : hi;
 }
 
-// Encode 16 binary32 values as block b: one E4M3 scale byte and 8 code bytes.
-__device__ __forceinline__ void encode_block(const float (&v)[16], float g, float gs6, uint32_t b,
-                                             uint8_t* __restrict__ codes,
-                                             uint8_t* __restrict__ scales) {
+// Signed E2M1 codes of fl(v[i] * r) for 16 values, packed two per byte with the even element in
+// the low nibble.  Each pair goes through the gfx950 conversion v_cvt_scalef32_pk_fp4_f32 at unit
+// scale (the byte it fills is the last operand).  For every binary32 input other than NaN that
+// conversion gives exactly e2m1_index(|y|) with the sign bit of y on top, zeros and subnormals
+// included; RNE is symmetric, so fl(x * r) carries the sign of x and the magnitude fl(|x| * r).
+// A NaN product (0 * inf, only when r is infinite) is the caller's to avoid.
+__device__ __forceinline__ void e2m1_pack16(const float (&v)[16], float r, uint32_t (&word)[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float* p = v + 8 * h;
+    uint32_t w = 0u;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p[0] * r, p[1] * r, 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p[2] * r, p[3] * r, 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p[4] * r, p[5] * r, 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p[6] * r, p[7] * r, 1.0f, 3);
+    word[h] = w;
+  }
+}
+
+// Scale code and packed element codes of a block: amax, the E4M3 code of fl(amax * gs6), its
+// value sd, the element factor r = fl(g / sd) (0 if sd is 0), then the codes of fl(x * r).
+// r overflows to +inf only for global scales above about 2^119; there 0 * r is NaN, so such
+// blocks take the element-by-element path, whose e2m1_index maps NaN to index 7 as the reference
+// encoder does.
+__device__ __forceinline__ uint32_t encode_codes(const float (&v)[16], float g, float gs6,
+                                                 uint32_t (&word)[2]) {
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
@@ -118,13 +140,26 @@ __device__ __forceinline__ void encode_block(const float (&v)[16], float g, floa
   const float sd = e4m3_value(sc);
   // sd == 0: r = 0 makes every magnitude 0 (finite inputs)
   const float r = sd > 0.0f ? g / sd : 0.0f;
-
-  uint32_t word[2] = {0u, 0u};
+  if (r < __builtin_inff()) {
+    e2m1_pack16(v, r, word);
+  } else {
+    word[0] = 0u;
+    word[1] = 0u;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t code = e2m1_index(fabsf(v[i]) * r) | ((__float_as_uint(v[i]) >> 31) << 3);
-    word[i >> 3] |= code << (4 * (i & 7));
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t code = e2m1_index(fabsf(v[i]) * r) | ((__float_as_uint(v[i]) >> 31) << 3);
+      word[i >> 3] |= code << (4 * (i & 7));
+    }
   }
+  return sc;
+}
+
+// Encode 16 binary32 values as block b: one E4M3 scale byte and 8 code bytes.
+__device__ __forceinline__ void encode_block(const float (&v)[16], float g, float gs6, uint32_t b,
+                                             uint8_t* __restrict__ codes,
+                                             uint8_t* __restrict__ scales) {
+  uint32_t word[2];
+  const uint32_t sc = encode_codes(v, g, gs6, word);
   uint2 out;
   out.x = word[0];
   out.y = word[1];

@@ -59,15 +59,11 @@ __device__ __forceinline__ void dequant_block(const uint32_t (&c)[16], float sd,
 // Encode the 16 values of a block (as the encoder does) and return their dequantized values.
 __device__ __forceinline__ void fake_quantize_block(const float (&v)[16], float g, float gs6,
                                                     float (&xh)[16]) {
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const float sd = e4m3_value(e4m3_encode(amax * gs6));
-  const float r = sd > 0.0f ? g / sd : 0.0f;
+  uint32_t word[2];
+  const float sd = e4m3_value(encode_codes(v, g, gs6, word));
   uint32_t c[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    c[i] = e2m1_index(fabsf(v[i]) * r) | ((__float_as_uint(v[i]) >> 28) & 8u);
+  for (int i = 0; i < 16; ++i) c[i] = (word[i >> 3] >> (4 * (i & 7))) & 0xFu;
   dequant_block(c, sd, g, xh);
 }
 

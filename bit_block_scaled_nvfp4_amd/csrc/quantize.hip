@@ -4,9 +4,11 @@
 // Source: "Why Gated DeltaNet Survives 4-Bit Quantization" (arXiv 2609.04098), ai.info summary,
 // "Methodology in Plain English" (E2M1 values with an E4M3 scale per 16-element block; the block's
 // largest value fixes the scale) and "Main Findings" (one FP32 global scale per module).  The
-// rounding rules the pages leave open are the ones stated in include/nvfp4.h; every operation
-// below is one IEEE binary32 operation in that order (this file is built with -ffp-contract=off
-// and correctly rounded division), so the codes are bit-exact with the CPU reference encoder.
+// rounding rules the pages leave open are the ones stated in include/nvfp4.h; every arithmetic
+// operation below is one IEEE binary32 operation in that order (this file is built with
+// -ffp-contract=off and correctly rounded division) and the E2M1 and bfloat16 roundings are gfx950
+// conversions that round to nearest-even, so the codes are bit-exact with the CPU reference
+// encoder.
 //
 // Work split: one thread encodes one 16-element block (32 bytes of bf16/f16 or 64 bytes of f32 in,
 // 8 code bytes and 1 scale byte out).  Consecutive threads take consecutive blocks of a row, so
@@ -40,26 +42,50 @@ __device__ __forceinline__ float bf16_round_from_f64(double x) {
 }
 
 // bfloat16 value of SiLU(g) * u = g / (1 + e^-g) * u, rounded once from the exact value.
-// Fast path (|g| <= 16): binary32 with the hardware 2^x and reciprocal.  Its relative error is
-// below 40 units in the last place of the binary32 result (argument rounding of -g log2(e) with
-// |g| <= 16 contributes at most 16 ulp through 2^x, the 2^x and reciprocal instructions about one
-// ulp each, four roundings half an ulp each), so rounding it to bfloat16 gives the same result as
-// rounding the exact value unless it lies within 64 ulps of a bfloat16 midpoint (low 16 bits
-// 0x8000).  Those cases, |g| > 16 and results that are zero, subnormal or not finite are
-// evaluated in binary64 (g / (1 + exp(-g)) * u, in that order) and rounded from there.
-__device__ __forceinline__ float silu_mul_bf16(float g, float u) {
-  if (fabsf(g) <= 16.0f) {
-    const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
-    const float s = g * __builtin_amdgcn_rcpf(1.0f + e);
-    const float y = s * u;
-    const uint32_t yb = __float_as_uint(y);
-    const uint32_t ex = (yb >> 23) & 0xFFu;
-    const uint32_t low = yb & 0xFFFFu;
-    if (ex != 0u && ex != 0xFFu && (low < 0x8000u - 64u || low > 0x8000u + 64u))
-      return __uint_as_float((yb + 0x7FFFu + ((yb >> 16) & 1u)) & 0xFFFF0000u);
-  }
+//
+// Fast path: y = fl(fl(g * rcp(fl(1 + exp2(fl(g * c))))) * u) in binary32, c = fl(-log2 e), with
+// the hardware 2^x and reciprocal (each within one ulp).  Rounding g * c moves the argument of 2^x
+// by at most 2|g| units of 2^-24 relative to e^-g; that error reaches 1 + e^-g scaled by
+// e^-g / (1 + e^-g) < 1.  With the two instruction errors and four roundings, y is within
+// (2|g| + 7) units of 2^-24 relative to the exact value, i.e. under 40 ulps for |g| <= 16.  So when
+// y is a normal number whose low 16 bits are more than 64 away from 0x8000 (a bfloat16 midpoint),
+// its nearest-even bfloat16 (v_cvt_pk_bf16_f32, two values at a time) is the rounding of the exact
+// value.  Every other case (|g| > 16; y zero, subnormal, infinite or NaN; y near a midpoint) is
+// evaluated in binary64 as g / (1 + exp(-g)) * u, in that order, and rounded from there.
+//
+// Each element's check is a single predicate and the binary64 path a single branch per element:
+// with the fast values formed without branches the compiler interleaves the elements, which nested
+// per-element branches prevent.
+__device__ __forceinline__ float silu_mul_bf16_exact(float g, float u) {
   const double gd = g, ud = u;
   return bf16_round_from_f64(gd / (1.0 + exp(-gd)) * ud);
+}
+
+// The binary32 fast value y and whether its bfloat16 rounding is certified.
+__device__ __forceinline__ float silu_mul_f32(float g, float u, bool& ok) {
+  const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
+  const float s = g * __builtin_amdgcn_rcpf(1.0f + e);
+  const float y = s * u;
+  const uint32_t yb = __float_as_uint(y);
+  const bool normal = __builtin_amdgcn_classf(y, (1 << 3) | (1 << 8));  // -normal, +normal
+  const bool off_mid = ((yb - (0x8000u - 64u)) & 0xFFFFu) > 128u;
+  ok = (fabsf(g) <= 16.0f) & normal & off_mid;
+  return y;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// bfloat16 values (as binary32) of SiLU(g0) * u0 and SiLU(g1) * u1.
+__device__ __forceinline__ void silu_mul_pair(float g0, float u0, float g1, float u1, float& r0,
+                                              float& r1) {
+  bool ok0, ok1;
+  const float y0 = silu_mul_f32(g0, u0, ok0);
+  const float y1 = silu_mul_f32(g1, u1, ok1);
+  const bf16x2_t b = __builtin_convertvector((f32x2_t){y0, y1}, bf16x2_t);
+  const uint32_t w = __builtin_bit_cast(uint32_t, b);
+  r0 = ok0 ? __uint_as_float(w << 16) : silu_mul_bf16_exact(g0, u0);
+  r1 = ok1 ? __uint_as_float(w & 0xFFFF0000u) : silu_mul_bf16_exact(g1, u1);
 }
 
 template <nvfp4_dtype DT>
@@ -120,7 +146,7 @@ silu_mul_quantize_kernel(const uint8_t* __restrict__ gate, int64_t ldg_bytes,
   load_block<DT>(gate + (int64_t)row * ldg_bytes + (int64_t)j * 16 * elem_bytes<DT>(), gv);
   load_block<DT>(up + (int64_t)row * ldu_bytes + (int64_t)j * 16 * elem_bytes<DT>(), uv);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = silu_mul_bf16(gv[i], uv[i]);
+  for (int i = 0; i < 16; i += 2) silu_mul_pair(gv[i], uv[i], gv[i + 1], uv[i + 1], v[i], v[i + 1]);
   encode_block(v, g, gs6, b, codes, scales);
 }
 
@@ -137,8 +163,11 @@ silu_mul_amax_kernel(const uint8_t* __restrict__ gate, int64_t ldg_bytes,
     float gv[16], uv[16];
     load_block<DT>(gate + (int64_t)row * ldg_bytes + (int64_t)j * 16 * elem_bytes<DT>(), gv);
     load_block<DT>(up + (int64_t)row * ldu_bytes + (int64_t)j * 16 * elem_bytes<DT>(), uv);
+    float v[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(silu_mul_bf16(gv[i], uv[i])));
+    for (int i = 0; i < 16; i += 2) silu_mul_pair(gv[i], uv[i], gv[i + 1], uv[i + 1], v[i], v[i + 1]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
