@@ -273,7 +273,7 @@ def gemm_exact(a_codes, a_scales, a_g, w_codes, w_scales, seg_g, seg_offsets=Non
         raise ValueError("one global scale per segment")
     S = A @ W.T  # int64, exact
     C = np.empty((M, N), dtype=np.float64)
-    ga = np.float64(np.float32(a_g))
+    ga = np.float64(np.asarray(a_g, dtype=np.float32).item())
     for j in range(len(seg_g)):
         lo, hi = off[j], off[j + 1]
         denom = ga * np.float64(seg_g[j])
@@ -290,7 +290,7 @@ def gemm_abs_bound(a_codes, a_scales, a_g, w_codes, w_scales, seg_g, seg_offsets
     off = _check_segments([0, N] if seg_offsets is None else seg_offsets, N)
     S = A @ W.T
     B = np.empty(S.shape, dtype=np.float64)
-    ga = np.float64(np.float32(a_g))
+    ga = np.float64(np.asarray(a_g, dtype=np.float32).item())
     for j in range(len(seg_g)):
         lo, hi = off[j], off[j + 1]
         B[:, lo:hi] = S[:, lo:hi].astype(np.float64) * 2.0 ** -20 / (ga * np.float64(seg_g[j]))
