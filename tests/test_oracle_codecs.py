@@ -1,13 +1,14 @@
 """Pins of the oracle's two element codecs against things other than themselves.
 
 * E4M3 (block scale) encoder and decoder: PyTorch's ``float8_e4m3fn`` cast (a library routine that
-  rounds to nearest-even) on every non-negative bf16 pattern, on dense fp32 windows around every
-  rounding midpoint and on random fp32 patterns; the saturation rule above the largest finite value.
+  rounds to nearest-even) on every non-negative binary32 pattern below 464 (and, cheaply, every bf16
+  pattern, dense windows around every rounding midpoint and random patterns); the saturation rule
+  above the largest finite value.
 * E2M1 (element) encoder: the closed-form threshold rule
   ``i = [y>0.25]+[y>=0.75]+[y>1.25]+[y>=1.75]+[y>2.5]+[y>=3.5]+[y>5]``, derived by hand from the
-  value set {0, 0.5, 1, 1.5, 2, 3, 4, 6} with ties to the even code, on every non-negative bf16
-  pattern, dense fp32 windows around every threshold and random fp32 patterns; and an exact
-  rational brute-force argmin on the tie points.
+  value set {0, 0.5, 1, 1.5, 2, 3, 4, 6} with ties to the even code, on every non-negative binary32
+  pattern from +0 to +inf (and, cheaply, every bf16 pattern, dense windows around every threshold
+  and random patterns); and an exact rational brute-force argmin on the tie points.
 
 The value sets are the public OCP definitions of the format names the pages use (ai.info summary,
 "Methodology in Plain English": 4-bit E2M1 values with an E4M3 scale per 16-element block).
@@ -107,6 +108,34 @@ def test_e4m3_encode_random_patterns():
     assert oracle.e4m3_encode(np.nextafter(np.float32(2.0 ** -10), np.float32(1)).reshape(1))[0] == 1
 
 
+def _e4m3_chunk(start: int) -> tuple[int, int]:
+    """Mismatches of the oracle against torch's cast on patterns [start, start + 2^24), below 464."""
+    torch.set_num_threads(1)
+    stop = min(start + (1 << 24), _E4M3_STOP)
+    x = _f32(np.arange(start, stop, dtype=np.uint32))
+    bad = np.nonzero(oracle.e4m3_encode(x) != _torch_e4m3(x))[0]
+    return int(bad.size), (int(start + bad[0]) if bad.size else -1)
+
+
+_E4M3_STOP = int(np.float32(_TORCH_LIMIT).view(np.uint32))
+
+
+def test_e4m3_encode_every_binary32_pattern_below_464():
+    # exhaustive from +0 up to the library's limit: every pattern (about 1.14e9), the subnormal
+    # scales and the 448 saturation included, in 2^24-pattern chunks over the host's cores
+    import multiprocessing as mp
+    import os
+
+    starts = list(range(0, _E4M3_STOP, 1 << 24))
+    workers = max(1, min(8, len(os.sched_getaffinity(0))))
+    # fresh interpreters: torch's thread pool does not survive a fork
+    with mp.get_context("spawn").Pool(workers) as pool:
+        res = pool.map(_e4m3_chunk, starts)
+    total = sum(n for n, _ in res)
+    first = [b for n, b in res if n]
+    assert total == 0, f"{total} mismatches, first pattern {first[0]:#010x}"
+
+
 def test_e4m3_encode_saturates_at_448():
     big = np.array([448.0, 448.5, 463.9, 464.0, 479.0, 480.0, 1e6, 3.0e38, np.inf], np.float32)
     assert np.all(oracle.e4m3_encode(big) == 0x7E)
@@ -143,6 +172,29 @@ def test_e2m1_windows_around_every_threshold():
 def test_e2m1_random_patterns():
     _check_e2m1(_random_nonneg_f32(2_000_000, 13, 8.0))
     _check_e2m1(_random_nonneg_f32(200_000, 14, 3.0e38))
+
+
+def _e2m1_chunk(start: int) -> tuple[int, int]:
+    """Mismatches of the oracle against the threshold rule on patterns [start, start + 2^24)."""
+    stop = min(start + (1 << 24), 0x7F800001)
+    y = _f32(np.arange(start, stop, dtype=np.uint32))
+    bad = np.nonzero(oracle.e2m1_encode_magnitude(y) != _threshold_rule(y))[0]
+    return int(bad.size), (int(start + bad[0]) if bad.size else -1)
+
+
+def test_e2m1_every_nonnegative_binary32_pattern():
+    # exhaustive: +0 through +inf, every pattern (2^31 - 2^23 + 1 of them), in 2^24-pattern chunks
+    # over the host's cores (about two minutes of single-core work)
+    import multiprocessing as mp
+    import os
+
+    starts = list(range(0, 0x7F800001, 1 << 24))
+    workers = max(1, min(8, len(os.sched_getaffinity(0))))
+    with mp.get_context("fork").Pool(workers) as pool:
+        res = pool.map(_e2m1_chunk, starts)
+    total = sum(n for n, _ in res)
+    first = [b for n, b in res if n]
+    assert total == 0, f"{total} mismatches, first pattern {first[0]:#010x}"
 
 
 def _brute_force_e2m1(y: Fraction) -> int:
