@@ -267,7 +267,7 @@ def gemm_exact(a_codes, a_scales, a_g, w_codes, w_scales, seg_g, seg_offsets=Non
         raise ValueError("A and W disagree on K")
     if K >= 1 << 19:
         raise ValueError("K too large for the exact int64 sum")
-    seg_g = np.atleast_1d(np.asarray(seg_g, dtype=np.float32))
+    seg_g = np.asarray(seg_g, dtype=np.float32).reshape(-1)
     off = _check_segments([0, N] if seg_offsets is None else seg_offsets, N)
     if len(seg_g) != len(off) - 1:
         raise ValueError("one global scale per segment")
@@ -286,7 +286,7 @@ def gemm_abs_bound(a_codes, a_scales, a_g, w_codes, w_scales, seg_g, seg_offsets
     A = np.abs(decode_integers(a_codes, a_scales))
     W = np.abs(decode_integers(w_codes, w_scales))
     N = W.shape[0]
-    seg_g = np.atleast_1d(np.asarray(seg_g, dtype=np.float32))
+    seg_g = np.asarray(seg_g, dtype=np.float32).reshape(-1)
     off = _check_segments([0, N] if seg_offsets is None else seg_offsets, N)
     S = A @ W.T
     B = np.empty(S.shape, dtype=np.float64)
@@ -301,7 +301,7 @@ def gemm_dequant_f64(a_codes, a_scales, a_g, w_codes, w_scales, seg_g, seg_offse
     """Second, independent route: dequantise both operands in float64 and call ``np.matmul``."""
     Af = dequantize(a_codes, a_scales, a_g)
     N = np.asarray(w_codes).shape[0]
-    seg_g = np.atleast_1d(np.asarray(seg_g, dtype=np.float32))
+    seg_g = np.asarray(seg_g, dtype=np.float32).reshape(-1)
     off = _check_segments([0, N] if seg_offsets is None else seg_offsets, N)
     Wf = decode_values(w_codes, w_scales)
     for j in range(len(seg_g)):
@@ -312,7 +312,7 @@ def gemm_dequant_f64(a_codes, a_scales, a_g, w_codes, w_scales, seg_g, seg_offse
 def fused_scale_defect(seg_g) -> np.ndarray:
     """The defective fused serving path of [ai.info, Main Findings]: every segment takes the
     largest of the constituent modules' global scales, block scales untouched."""
-    seg_g = np.atleast_1d(np.asarray(seg_g, dtype=np.float32))
+    seg_g = np.asarray(seg_g, dtype=np.float32).reshape(-1)
     return np.full_like(seg_g, seg_g.max())
 
 
