@@ -373,7 +373,7 @@ constexpr int kEpiStride = FN * 32 + 4;  // floats per staged row; the pad sprea
 template <bool BF16, int FM, int FN>
 __device__ __forceinline__ void store_tile(const GemmArgs& p, const floatx16 (&acc)[FM][FN],
                                            const float* alpha, float* epi, int m0, int n0, int wm,
-                                           int wn, int lane, bool vec) {
+                                           int wn, int lane, bool vec, bool interior) {
   using OutT = typename std::conditional<BF16, uint16_t, float>::type;
   OutT* const c = reinterpret_cast<OutT*>(p.c);
   constexpr int S = kEpiStride<FN>;
@@ -381,6 +381,37 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const floatx16 (&a
   const int cc = (lane & 31) * 4;  // read-back columns of this lane within the wavefront's 128
   const int n = n0 + wn * FN * 32 + cc;
   const floatx4 al = *reinterpret_cast<const floatx4*>(alpha + wn * FN * 32 + cc);
+  if (interior) {
+    // the tile lies inside C and rows are 16-byte aligned: no masks, and the 16 read-backs of a
+    // fragment row are all issued before the first store, so their LDS latency overlaps
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<floatx4*>(epi + r * S + j * 32 + 8 * q + 4 * h) =
+              floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                      acc[i][j][4 * q + 3]};
+      floatx4 x[16];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) x[t] = *reinterpret_cast<const floatx4*>(epi + (2 * t + h) * S + cc);
+      OutT* const dst = c + (int64_t)(m0 + wm * FM * 32 + i * 32 + h) * p.ldc + n;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const floatx4 v = {x[t][0] * al[0], x[t][1] * al[1], x[t][2] * al[2], x[t][3] * al[3]};
+        if constexpr (BF16) {
+          const uint32_t lo = f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+          const uint32_t hi = f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+          *reinterpret_cast<uint2*>(dst + (int64_t)(2 * t) * p.ldc) = uint2{lo, hi};
+        } else {
+          *reinterpret_cast<floatx4*>(dst + (int64_t)(2 * t) * p.ldc) = v;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return;
+  }
   const bool full = vec && n + 3 < p.N;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
@@ -544,12 +575,13 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
       issue_chunk<Cfg>(p, ron, 0, s0);
       issue_chunk<Cfg>(p, ron, min(1, last), s1);
     }
+    const bool interior = vec && tm0 + Cfg::BM <= p.M && tn0 + Cfg::BN <= p.N;
     if (p.c_bf16)
       store_tile<true>(p, acc, alpha_s[par], epi_s[wave_e], tm0, tn0, wave_e / WAVES_N,
-                       wave_e % WAVES_N, lane_e, vec);
+                       wave_e % WAVES_N, lane_e, vec, interior);
     else
       store_tile<false>(p, acc, alpha_s[par], epi_s[wave_e], tm0, tn0, wave_e / WAVES_N,
-                        wave_e % WAVES_N, lane_e, vec);
+                        wave_e % WAVES_N, lane_e, vec, interior);
     if (!more) break;
   }
 }
