@@ -8,8 +8,9 @@ tensors resident in HBM before the timed region starts.
 
 Printed: one JSON line with the prefill throughput (TFLOP/s = 2MNK / step time), the roofline of
 the dominant kernel (the product; its average duration from HIP events recorded on the stream it
-is launched on), the decode-shaped GEMV throughput (GB/s of algorithmic bytes), and the CPU oracle
-timed on a bounded sample of the same workload.
+is launched on), the activation encode with the static and with the dynamic global scale, the
+decode-shaped GEMV throughput (GB/s of algorithmic bytes), and the CPU oracle timed on a bounded
+sample of the same workload.
 """
 
 from __future__ import annotations
@@ -93,8 +94,18 @@ def prefill(args, torch, nv, W):
     torch.cuda.synchronize()
     g_ms = sum(evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(args.steps)) / args.steps
     q_ms = e0.elapsed_time(e1) / args.steps
+    # the same encode with the dynamic scale: clearing the max cell, the max pass over A, the encode
+    # and the scale's finalisation (A is read twice), `steps` calls back to back between events
+    e0.record()
+    for i in range(args.steps):
+        nv.nvfp4_quantize(ad, None, ac, as_)
+    e1.record()
+    torch.cuda.synchronize()
+    qd_ms = e0.elapsed_time(e1) / args.steps
+    nv.nvfp4_quantize(ad, ga, ac, as_)  # back to the static-scale codes the product is timed on
     flops = w.flops
     q_bytes = w.M * w.K * (2 + 9 / 16)
+    qd_bytes = w.M * w.K * (2 + 2 + 9 / 16)
     # the vendor dense bf16 GEMM of the same shape (torch.matmul -> hipBLASLt), timed in turns with
     # the NVFP4 product so both see the same clock and temperature
     wb = torch.randn(w.N, w.K, device=dev, dtype=torch.bfloat16)
@@ -113,7 +124,7 @@ def prefill(args, torch, nv, W):
               "nvfp4_product_ms_same_turns": round(min(ours), 4),
               "nvfp4_product_over_vendor": round(min(vend) / min(ours), 4)}
     return dict(w=w, ms_step=ms_step, gemm_ms=g_ms, quant_ms=q_ms, flops=flops, q_bytes=q_bytes,
-                vendor=vendor)
+                quant_dyn_ms=qd_ms, qd_bytes=qd_bytes, vendor=vendor)
 
 
 def decode(args, torch, nv, W):
@@ -519,6 +530,7 @@ def main():
     value = p["flops"] / (p["ms_step"] * 1e-3) / 1e12
     achieved = p["flops"] / (p["gemm_ms"] * 1e-3) / 1e12
     q_gbs = p["q_bytes"] / (p["quant_ms"] * 1e-3) / 1e9
+    qd_gbs = p["qd_bytes"] / (p["quant_dyn_ms"] * 1e-3) / 1e9
     line = {
         "metric": "NVFP4 W4A4 GEMM TFLOP/s (prefill M=8192) + decode GB/s, % of MI355X roofline",
         "value": round(value, 2),
@@ -543,7 +555,10 @@ def main():
                      "kernel_ms": round(p["gemm_ms"], 4),
                      "frac_of_mxfp4_peak": round(achieved / MFMA_FP4_PEAK_TFLOPS, 4)},
         "quantize": {"bound": "hbm", "ms": round(p["quant_ms"], 4), "GB/s": round(q_gbs, 1),
-                     "frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4), "bytes": int(p["q_bytes"])},
+                     "frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4), "bytes": int(p["q_bytes"]),
+                     "dynamic": {"ms": round(p["quant_dyn_ms"], 4), "GB/s": round(qd_gbs, 1),
+                                 "frac_hbm": round(qd_gbs / HBM_PEAK_GBS, 4),
+                                 "bytes": int(p["qd_bytes"])}},
         "decode": dec,
         "silu_mul_quantize": silu,
         "kv_fp8_store": kv,

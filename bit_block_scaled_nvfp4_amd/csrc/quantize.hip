@@ -106,15 +106,52 @@ quantize_kernel(const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t nb, u
   encode_block(v, g, gs6, b, codes, scales);
 }
 
-// Tensor-wide max |x| (exact, order-free) into *out as a binary32 bit pattern: for non-negative
-// floats the unsigned integer order of the bit patterns is the numeric order, so atomicMax on the
-// pattern is the float max.  *out must hold +0.0 before the launch.
+// Raise *out to the workgroup's largest per-thread value m >= 0.  For non-negative floats the
+// unsigned order of the bit patterns is the numeric order, so atomicMax on the pattern is the
+// float max (exact and order-free).  The workgroup first reduces through shuffles and one LDS slot
+// per wavefront, and its one atomic is skipped when the cell already holds at least m: every
+// workgroup updating one address would otherwise serialise thousands of atomics.  A stale read of
+// the cell can only cost an extra atomic.  Called by every thread of the workgroup.
+__device__ __forceinline__ void publish_max(float m, float* out) {
+  __shared__ float wave_max[kThreads / 64];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, wave_max[w]);
+    unsigned int* cell = reinterpret_cast<unsigned int*>(out);
+    const unsigned int cur = __hip_atomic_load(cell, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__float_as_uint(m) > cur) atomicMax(cell, __float_as_uint(m));
+  }
+}
+
+// Tensor-wide max |x| into *out (as publish_max).  *out must hold +0.0 before the launch.
 template <nvfp4_dtype DT>
 __global__ void __launch_bounds__(kThreads)
 amax_kernel(const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t nb, uint32_t total,
             float* out) {
   float m = 0.0f;
-  for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < total; b += gridDim.x * kThreads) {
+  const uint32_t stride = gridDim.x * kThreads;
+  uint32_t b = blockIdx.x * kThreads + threadIdx.x;
+  // four blocks in flight per thread (the grid is one workgroup per compute unit)
+  const uint32_t unrolled_end = total > 3u * stride ? total - 3u * stride : 0u;
+  for (; b < unrolled_end; b += 4u * stride) {
+    float v[4][16];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t bu = b + (uint32_t)u * stride;
+      const uint32_t row = bu / nb;
+      const uint32_t j = bu - row * nb;
+      load_block<DT>(x + (int64_t)row * ldx_bytes + (int64_t)j * 16 * elem_bytes<DT>(), v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[u][i]));
+  }
+  for (; b < total; b += stride) {
     const uint32_t row = b / nb;
     const uint32_t j = b - row * nb;
     float v[16];
@@ -122,10 +159,7 @@ amax_kernel(const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t nb, uint3
 #pragma unroll
     for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  if ((threadIdx.x & 63) == 0 && m > 0.0f)
-    atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(m));
+  publish_max(m, out);
 }
 
 // Fused SiLU(g) * u -> NVFP4: block b of the activation is formed from blocks b of gate and up
@@ -169,10 +203,7 @@ silu_mul_amax_kernel(const uint8_t* __restrict__ gate, int64_t ldg_bytes,
 #pragma unroll
     for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  if ((threadIdx.x & 63) == 0 && m > 0.0f)
-    atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(m));
+  publish_max(m, out);
 }
 
 __global__ void fill_zero_kernel(float* p) { *p = 0.0f; }
@@ -180,6 +211,18 @@ __global__ void fill_zero_kernel(float* p) { *p = 0.0f; }
 __global__ void finalize_dynamic_scale_kernel(float* p) {
   const float amax = *p;
   *p = amax == 0.0f ? 1.0f : 2688.0f / amax;
+}
+
+// Workgroups of the max pass over `total` blocks: one per compute unit (fewer workgroups mean
+// fewer atomics on the one cell; each thread keeps four blocks of loads in flight instead).
+hipError_t amax_grid(uint32_t total, uint32_t* grid) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const uint32_t need = (total + kThreads - 1) / kThreads;
+  *grid = need < (uint32_t)(cus > 0 ? cus : 1) ? need : (uint32_t)(cus > 0 ? cus : 1);
+  return hipSuccess;
 }
 
 template <nvfp4_dtype DT>
@@ -190,13 +233,15 @@ hipError_t launch_typed(const void* x, int64_t rows, int64_t cols, int64_t ldx, 
   const int64_t ldx_bytes = ldx * elem_bytes<DT>();
   const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
   if (dynamic) {
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(1), dim3(1), 0, stream, g);
+    uint32_t grid = 0;
     if (total > 0) {
-      uint32_t grid = (total + kThreads - 1) / kThreads;
-      grid = grid > 4096u ? 4096u : grid;
+      const hipError_t e = amax_grid(total, &grid);  // before any launch
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(1), dim3(1), 0, stream, g);
+    if (total > 0)
       hipLaunchKernelGGL(amax_kernel<DT>, dim3(grid), dim3(kThreads), 0, stream, xb, ldx_bytes, nb,
                          total, g);
-    }
   }
   if (total > 0) {
     const uint32_t grid = (total + kThreads - 1) / kThreads;
@@ -259,10 +304,13 @@ hipError_t launch_dynamic_amax(const void* x, nvfp4_dtype dt, int64_t rows, int6
   const uint32_t nb = (uint32_t)(cols / 16);
   const uint32_t total = (uint32_t)(rows * (cols / 16));
   const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
+  uint32_t grid = 0;
+  if (total > 0) {
+    const hipError_t e = amax_grid(total, &grid);  // before any launch
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(fill_zero_kernel, dim3(1), dim3(1), 0, stream, cell);
   if (total > 0) {
-    uint32_t grid = (total + kThreads - 1) / kThreads;
-    grid = grid > 4096u ? 4096u : grid;
     switch (dt) {
       case NVFP4_F32:
         hipLaunchKernelGGL(amax_kernel<NVFP4_F32>, dim3(grid), dim3(kThreads), 0, stream, xb,
