@@ -233,7 +233,8 @@ def kv_store(args, torch, nv, W):
     before timing) and scattered into a shuffled paged cache of 65536 slots.  Timed over `steps`
     launches back to back between HIP events, rotating over 3 copies of inputs and caches (605 MB,
     beyond the 256 MB last-level cache); bytes = bf16 keys + values read, the slot mapping read,
-    the FP8 rows written."""
+    the FP8 rows written.  Then the decode direction: both caches gathered back to bf16 through the
+    same slots (two launches per call; bytes = FP8 rows and slots read, bf16 rows written)."""
     import numpy as np
 
     w = W.KV_WORKLOADS[6]
@@ -264,10 +265,27 @@ def kv_store(args, torch, nv, W):
     ms = e0.elapsed_time(e1) / args.steps
     nbytes = 2 * w.tokens * w.width * (2 + 1) + w.tokens * 8
     gbs = nbytes / (ms * 1e-3) / 1e9
-    del sets, slots
+    # the decode direction: gather the sequence's K and V rows back from the paged caches as bf16
+    outs = [(torch.empty((w.tokens, w.width), dtype=torch.bfloat16, device=dev),
+             torch.empty((w.tokens, w.width), dtype=torch.bfloat16, device=dev)) for _ in range(R)]
+
+    def load(i):
+        s_ = sets[i % R]
+        nv.nvfp4_kv_fp8_load(s_[2], ks, s_[4], out=outs[i % R][0])
+        nv.nvfp4_kv_fp8_load(s_[3], vs, s_[4], out=outs[i % R][1])
+
+    for i in range(args.warmup):
+        load(i)
+    lms = _timed(torch, args.steps, load)
+    lbytes = 2 * w.tokens * w.width * (1 + 2) + 2 * w.tokens * 8
+    lgbs = lbytes / (lms * 1e-3) / 1e9
+    del sets, slots, outs
     torch.cuda.empty_cache()
     return {"bound": "hbm", "tokens": w.tokens, "width": w.width, "us": round(ms * 1e3, 3),
-            "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": nbytes}
+            "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": nbytes,
+            "load": {"us": round(lms * 1e3, 3), "GB/s": round(lgbs, 1),
+                     "frac_hbm": round(lgbs / HBM_PEAK_GBS, 4), "bytes": lbytes,
+                     "launches": 2}}
 
 
 def _timed(torch, steps, fn):

@@ -11,11 +11,13 @@
 // subnormals kept) on y clamped to [-448, 448] first, so nothing can overflow to NaN; the decode
 // uses v_cvt_pk_f32_fp8, which is exact.
 //
-// Work split: a thread owns 16 consecutive elements of one token's row (32 bytes of bf16/f16 or
-// 64 bytes of f32 in, 16 code bytes out).  A row of width/16 chunks is served by the L lanes of a
-// wave (L the power of two >= width/16, at most 64), so a wave covers 64/L whole tokens when rows are
-// short and a 64-chunk stretch of one token when they are long; loads and stores of a wave are
-// contiguous per token.  The kernels are bound by HBM bandwidth (3 bytes moved per bf16 element).
+// Work split of the store: a thread owns 16 consecutive elements of one token's row (32 bytes of
+// bf16/f16 or 64 bytes of f32 in, 16 code bytes out).  A row of width/16 chunks is served by the L
+// lanes of a wave (L the power of two >= width/16, at most 64), so a wave covers 64/L whole tokens
+// when rows are short and a 64-chunk stretch of one token when they are long; loads and stores of
+// a wave are contiguous per token.  The load (decode direction) splits rows the same way into
+// pieces of 8 (bf16 out) or 4 (f32 out) codes, so each lane writes one 16-byte piece.  The kernels
+// are bound by HBM bandwidth (3 bytes moved per bf16 element).
 #include "codec.h"
 #include "nvfp4_internal.h"
 
@@ -25,6 +27,8 @@ namespace {
 using namespace codec;
 
 constexpr int kThreads = 256;
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct KvStoreArgs {
   const uint8_t* src[2];  // key, value rows (bytes)
@@ -88,8 +92,8 @@ struct KvLoadArgs {
   uint8_t* out;
   int64_t ld_out;    // bytes
   int32_t tokens;
-  int32_t chunks;
-  int32_t lane_bits;
+  int32_t pieces;     // width / kLoadElems
+  int32_t lane_bits;  // log2 of lanes per token
 };
 
 __device__ __forceinline__ uint32_t bf16_pair_rne(float lo, float hi) {
@@ -100,21 +104,38 @@ __device__ __forceinline__ uint32_t bf16_pair_rne(float lo, float hi) {
   return ra | rb;
 }
 
+// Decode direction.  A lane owns kLoadElems<BF16_OUT> codes of one row: 8 for bfloat16 output and
+// 4 for float32, so that it writes exactly 16 bytes.  A wavefront's loads (8 or 4 bytes per lane)
+// and stores (16 bytes per lane) are then contiguous per token.  With 16 codes per lane, each lane
+// wrote 32 or 64 bytes in several 16-byte stores, and a wavefront store instruction covered only
+// every second or fourth 16-byte piece of the row.
+template <bool BF16_OUT>
+constexpr int kLoadElems = BF16_OUT ? 8 : 4;
+
+// grid: x over groups of 256 >> lane_bits tokens, y over stretches of (1 << lane_bits) pieces of
+// kLoadElems codes.
 template <bool BF16_OUT>
 __global__ void __launch_bounds__(kThreads) kv_load_kernel(KvLoadArgs a) {
+  constexpr int E = kLoadElems<BF16_OUT>;
   const int lb = a.lane_bits;
   const int32_t t = (int32_t)(blockIdx.x * (kThreads >> lb)) + (int32_t)(threadIdx.x >> lb);
   const int32_t c = (int32_t)(blockIdx.y << lb) + (int32_t)(threadIdx.x & ((1u << lb) - 1));
-  if (t >= a.tokens || c >= a.chunks) return;
+  if (t >= a.tokens || c >= a.pieces) return;
   const int64_t slot = slot_of(a.slots, a.num_slots, t);
-  float v[16];
+  float v[E];
   if (slot >= 0) {
-    const u32x4 q = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(a.cache + slot * a.cache_ld + (int64_t)c * 16));
+    const uint8_t* src = a.cache + slot * a.cache_ld + (int64_t)c * E;
+    uint32_t w[E / 4];
+    if constexpr (E == 8) {
+      const u32x2 q = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src));
+      w[0] = q.x;
+      w[1] = q.y;
+    } else {
+      w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(src));
+    }
     const float s = *a.scale;
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < E / 4; ++i) {
       const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
       const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
       v[4 * i + 0] = lo[0] * s;
@@ -124,38 +145,27 @@ __global__ void __launch_bounds__(kThreads) kv_load_kernel(KvLoadArgs a) {
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+    for (int i = 0; i < E; ++i) v[i] = 0.0f;
   }
-  uint8_t* dst = a.out + (int64_t)t * a.ld_out;
+  u32x4 o;
   if constexpr (BF16_OUT) {
-    u32x4* d = reinterpret_cast<u32x4*>(dst + (int64_t)c * 32);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      u32x4 o;
-      o.x = bf16_pair_rne(v[8 * i + 0], v[8 * i + 1]);
-      o.y = bf16_pair_rne(v[8 * i + 2], v[8 * i + 3]);
-      o.z = bf16_pair_rne(v[8 * i + 4], v[8 * i + 5]);
-      o.w = bf16_pair_rne(v[8 * i + 6], v[8 * i + 7]);
-      __builtin_nontemporal_store(o, d + i);
-    }
+    o.x = bf16_pair_rne(v[0], v[1]);
+    o.y = bf16_pair_rne(v[2], v[3]);
+    o.z = bf16_pair_rne(v[4], v[5]);
+    o.w = bf16_pair_rne(v[6], v[7]);
   } else {
-    f32x4* d = reinterpret_cast<f32x4*>(dst + (int64_t)c * 64);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f32x4 o;
-      o.x = v[4 * i + 0];
-      o.y = v[4 * i + 1];
-      o.z = v[4 * i + 2];
-      o.w = v[4 * i + 3];
-      __builtin_nontemporal_store(o, d + i);
-    }
+    o.x = __float_as_uint(v[0]);
+    o.y = __float_as_uint(v[1]);
+    o.z = __float_as_uint(v[2]);
+    o.w = __float_as_uint(v[3]);
   }
+  __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(a.out + (int64_t)t * a.ld_out + (int64_t)c * 16));
 }
 
-// Lanes per token: the power of two >= chunks, at most 64 (a wavefront).
-int lane_bits_for(int64_t chunks) {
+// Lanes per token: the power of two >= the pieces of a row, at most 64 (a wavefront).
+int lane_bits_for(int64_t pieces) {
   int lb = 0;
-  while (lb < 6 && (int64_t(1) << lb) < chunks) ++lb;
+  while (lb < 6 && (int64_t(1) << lb) < pieces) ++lb;
   return lb;
 }
 
@@ -212,11 +222,11 @@ hipError_t launch_kv_load(const uint8_t* cache, int64_t num_slots, int64_t cache
   a.out = static_cast<uint8_t*>(out);
   a.ld_out = ld_out * (out_dt == NVFP4_F32 ? 4 : 2);
   a.tokens = (int32_t)tokens;
-  a.chunks = (int32_t)(width / 16);
-  a.lane_bits = lane_bits_for(a.chunks);
+  a.pieces = (int32_t)(width / (out_dt == NVFP4_BF16 ? kLoadElems<true> : kLoadElems<false>));
+  a.lane_bits = lane_bits_for(a.pieces);
   const int64_t tok_per_block = kThreads >> a.lane_bits;
   const dim3 grid((uint32_t)((tokens + tok_per_block - 1) / tok_per_block),
-                  (uint32_t)((a.chunks + (1 << a.lane_bits) - 1) >> a.lane_bits), 1u);
+                  (uint32_t)((a.pieces + (1 << a.lane_bits) - 1) >> a.lane_bits), 1u);
   if (out_dt == NVFP4_BF16)
     hipLaunchKernelGGL(kv_load_kernel<true>, grid, dim3(kThreads), 0, stream, a);
   else
