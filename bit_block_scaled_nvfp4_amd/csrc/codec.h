@@ -1,8 +1,9 @@
 // NVFP4 codec helpers shared by the encoding kernels (gfx950): element loading, the E4M3 and E2M1
 // roundings, block encoding and decoding.  The rounding rules are the ones stated in
-// include/nvfp4.h; every operation is one IEEE binary32 operation in the order written (the
-// library is built with -ffp-contract=off and correctly rounded division), so results are
-// bit-exact with the CPU reference encoder.
+// include/nvfp4.h.  Every arithmetic operation is one IEEE binary32 operation in the order written
+// (the library is built with -ffp-contract=off and correctly rounded division).  The E2M1 element
+// rounding of a block goes through the gfx950 fp4 conversion, which rounds exactly as e2m1_index
+// below.  So results are bit-exact with the CPU reference encoder.
 #pragma once
 
 #include <hip/hip_runtime.h>
