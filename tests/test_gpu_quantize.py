@@ -44,6 +44,28 @@ def test_ragged_shapes_all_dtypes(dtype, shape):
     assert_codes_equal(*_both(x, dtype, np.float32(37.5)), f"{dtype} {shape} static")
 
 
+@pytest.mark.parametrize("block", [0, 3 * 65536 + 5, 131111, 4099 * 64 - 1])
+def test_dynamic_scale_wherever_the_maximum_sits(block):
+    # 4099 x 1024 (262336 blocks): on 256 compute units the max pass takes four blocks per step
+    # for the first 262144 and one at a time for the rest, so the planted maximum lands in the
+    # first or fourth slot of a step, mid-tensor, or in the last block
+    import torch
+
+    import bit_block_scaled_nvfp4_amd as nv
+
+    x = round_bf16(random_matrix(41, 4099, 1024, outlier_cols=3))
+    r, c = divmod(block * 16, 1024)
+    x[r, c + 7] = np.float32(-32768.0)  # exact in bf16
+    g = oracle.dynamic_global_scale(x)
+    codes, scales, gg = nv.nvfp4_quantize(to_device(x, "bf16"))
+    torch.cuda.synchronize()
+    assert np.float32(gg.item()) == g, f"planted max in block {block}"
+    rows = np.unique([0, r, 4098])
+    ref = oracle.quantize(x[rows], g)
+    got = (codes[rows].cpu().numpy(), scales[rows].cpu().numpy(), np.float32(gg.item()))
+    assert_codes_equal(got, ref, f"planted max in block {block}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_strided_rows(dtype):
     import torch
