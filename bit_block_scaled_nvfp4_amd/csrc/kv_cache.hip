@@ -112,40 +112,38 @@ __device__ __forceinline__ uint32_t bf16_pair_rne(float lo, float hi) {
 template <bool BF16_OUT>
 constexpr int kLoadElems = BF16_OUT ? 8 : 4;
 
-// grid: x over groups of 256 >> lane_bits tokens, y over stretches of (1 << lane_bits) pieces of
-// kLoadElems codes.
+// The kLoadElems codes of one piece, as one or two 32-bit words.
 template <bool BF16_OUT>
-__global__ void __launch_bounds__(kThreads) kv_load_kernel(KvLoadArgs a) {
-  constexpr int E = kLoadElems<BF16_OUT>;
-  const int lb = a.lane_bits;
-  const int32_t t = (int32_t)(blockIdx.x * (kThreads >> lb)) + (int32_t)(threadIdx.x >> lb);
-  const int32_t c = (int32_t)(blockIdx.y << lb) + (int32_t)(threadIdx.x & ((1u << lb) - 1));
-  if (t >= a.tokens || c >= a.pieces) return;
-  const int64_t slot = slot_of(a.slots, a.num_slots, t);
-  float v[E];
-  if (slot >= 0) {
-    const uint8_t* src = a.cache + slot * a.cache_ld + (int64_t)c * E;
-    uint32_t w[E / 4];
-    if constexpr (E == 8) {
-      const u32x2 q = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src));
-      w[0] = q.x;
-      w[1] = q.y;
-    } else {
-      w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(src));
-    }
-    const float s = *a.scale;
-#pragma unroll
-    for (int i = 0; i < E / 4; ++i) {
-      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
-      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
-      v[4 * i + 0] = lo[0] * s;
-      v[4 * i + 1] = lo[1] * s;
-      v[4 * i + 2] = hi[0] * s;
-      v[4 * i + 3] = hi[1] * s;
-    }
+struct KvPiece {
+  uint32_t w[kLoadElems<BF16_OUT> / 4];
+};
+
+template <bool BF16_OUT>
+__device__ __forceinline__ KvPiece<BF16_OUT> kv_load_piece(const uint8_t* src) {
+  KvPiece<BF16_OUT> p;
+  if constexpr (BF16_OUT) {
+    const u32x2 q = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src));
+    p.w[0] = q.x;
+    p.w[1] = q.y;
   } else {
+    p.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(src));
+  }
+  return p;
+}
+
+// Decoded piece (zeros when `valid` is false), packed as the 16 output bytes.
+template <bool BF16_OUT>
+__device__ __forceinline__ u32x4 kv_decode_piece(const KvPiece<BF16_OUT>& p, float s, bool valid) {
+  constexpr int E = kLoadElems<BF16_OUT>;
+  float v[E];
 #pragma unroll
-    for (int i = 0; i < E; ++i) v[i] = 0.0f;
+  for (int i = 0; i < E / 4; ++i) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)p.w[i], false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)p.w[i], true);
+    v[4 * i + 0] = valid ? lo[0] * s : 0.0f;
+    v[4 * i + 1] = valid ? lo[1] * s : 0.0f;
+    v[4 * i + 2] = valid ? hi[0] * s : 0.0f;
+    v[4 * i + 3] = valid ? hi[1] * s : 0.0f;
   }
   u32x4 o;
   if constexpr (BF16_OUT) {
@@ -159,7 +157,38 @@ __global__ void __launch_bounds__(kThreads) kv_load_kernel(KvLoadArgs a) {
     o.z = __float_as_uint(v[2]);
     o.w = __float_as_uint(v[3]);
   }
-  __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(a.out + (int64_t)t * a.ld_out + (int64_t)c * 16));
+  return o;
+}
+
+// grid: x over groups of 2 * (256 >> lane_bits) tokens (each thread takes two tokens, the second
+// 256 >> lane_bits tokens after the first), y over stretches of (1 << lane_bits) pieces.  Both
+// tokens' slots, then both rows, are loaded before anything is decoded, so the two dependent load
+// chains overlap.  A token whose slot is outside the cache reads row 0 (present whenever the cache
+// has rows) and writes zeros.
+template <bool BF16_OUT>
+__global__ void __launch_bounds__(kThreads) kv_load_kernel(KvLoadArgs a) {
+  constexpr int E = kLoadElems<BF16_OUT>;
+  const int lb = a.lane_bits;
+  const int32_t per = kThreads >> lb;
+  const int32_t t0 = (int32_t)(blockIdx.x * 2 * per) + (int32_t)(threadIdx.x >> lb);
+  const int32_t t1 = t0 + per;
+  const int32_t c = (int32_t)(blockIdx.y << lb) + (int32_t)(threadIdx.x & ((1u << lb) - 1));
+  if (t0 >= a.tokens || c >= a.pieces) return;
+  const bool has1 = t1 < a.tokens;
+  const int64_t s0 = slot_of(a.slots, a.num_slots, t0);
+  const int64_t s1 = has1 ? slot_of(a.slots, a.num_slots, t1) : -1;
+  KvPiece<BF16_OUT> p0{}, p1{};
+  if (a.num_slots > 0) {
+    p0 = kv_load_piece<BF16_OUT>(a.cache + (s0 >= 0 ? s0 : 0) * a.cache_ld + (int64_t)c * E);
+    p1 = kv_load_piece<BF16_OUT>(a.cache + (s1 >= 0 ? s1 : 0) * a.cache_ld + (int64_t)c * E);
+  }
+  const float s = *a.scale;
+  const u32x4 o0 = kv_decode_piece<BF16_OUT>(p0, s, s0 >= 0);
+  __builtin_nontemporal_store(o0, reinterpret_cast<u32x4*>(a.out + (int64_t)t0 * a.ld_out + (int64_t)c * 16));
+  if (has1) {
+    const u32x4 o1 = kv_decode_piece<BF16_OUT>(p1, s, s1 >= 0);
+    __builtin_nontemporal_store(o1, reinterpret_cast<u32x4*>(a.out + (int64_t)t1 * a.ld_out + (int64_t)c * 16));
+  }
 }
 
 // Lanes per token: the power of two >= the pieces of a row, at most 64 (a wavefront).
@@ -224,7 +253,7 @@ hipError_t launch_kv_load(const uint8_t* cache, int64_t num_slots, int64_t cache
   a.tokens = (int32_t)tokens;
   a.pieces = (int32_t)(width / (out_dt == NVFP4_BF16 ? kLoadElems<true> : kLoadElems<false>));
   a.lane_bits = lane_bits_for(a.pieces);
-  const int64_t tok_per_block = kThreads >> a.lane_bits;
+  const int64_t tok_per_block = 2 * (kThreads >> a.lane_bits);
   const dim3 grid((uint32_t)((tokens + tok_per_block - 1) / tok_per_block),
                   (uint32_t)((a.pieces + (1 << a.lane_bits) - 1) >> a.lane_bits), 1u);
   if (out_dt == NVFP4_BF16)
