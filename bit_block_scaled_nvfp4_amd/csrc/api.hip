@@ -66,15 +66,17 @@ nvfp4_status run_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const flo
   a.M = (int32_t)M;
   a.N = (int32_t)N;
   a.K = (int32_t)K;
+  a.k_pitch = (int32_t)K;
   a.c = c;
   a.c_bf16 = c_dtype == NVFP4_BF16 ? 1 : 0;
+  a.c_accumulate = 0;
   a.ldc = ldc;
   a.seg.nseg = nseg;
   for (int j = 0; j <= nseg; ++j) a.seg.off[j] = (int32_t)seg_offsets[j];
   for (int j = nseg + 1; j <= NVFP4_MAX_SEGMENTS; ++j) a.seg.off[j] = (int32_t)N;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  switch (nvfp4::choose_gemm_path(M, K)) {
+  switch (nvfp4::choose_gemm_path(M, K, a.c_bf16 != 0)) {
     case nvfp4::GemmPath::General:
       e = nvfp4::launch_gemm_general(a, s);
       break;

@@ -60,7 +60,7 @@ template <int P, int T>
 __device__ __forceinline__ void issue_phase(const GemmArgs& p, int c0, int clast, int wave,
                                             int lane, int r, int g, uint8_t* buf0, uint8_t* buf1,
                                             uint4& aw) {
-  const int kb = p.K / 2;
+  const int kb = p.k_pitch / 2;
   // codes: slot t = wave * 64 + lane holds row t / 32, phase piece (t % 32) ^ row within 16s
   const int t = wave * 64 + lane;
   const int row = t / kPhasePieces;
@@ -163,7 +163,7 @@ gemm_skinny_kernel(GemmArgs p, int ncols) {
   // 16-byte pieces of consecutive rows); older than every phase's instructions, so each phase's
   // wait covers them
   {
-    const int ks = p.K / 16, per_row = ks / 16;
+    const int ks = p.k_pitch / 16, per_row = p.K / 256;  // row pitch; 16-byte pieces per row
 #pragma unroll
     for (int s = threadIdx.x; s < T * 16 * per_row; s += kSkinnyThreads) {
       const int row = s / per_row;
@@ -248,7 +248,12 @@ gemm_skinny_kernel(GemmArgs p, int ncols) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int m = 4 * g + e;
-    if (m < p.M) store_c(p.c, p.c_bf16, p.ldc, m, n, sum[e] * al);
+    if (m < p.M) {
+      if (p.c_accumulate)  // a later piece of a split K: f32 C, stream-ordered after the first
+        reinterpret_cast<float*>(p.c)[(int64_t)m * p.ldc + n] += sum[e] * al;
+      else
+        store_c(p.c, p.c_bf16, p.ldc, m, n, sum[e] * al);
+    }
   }
 }
 
@@ -273,12 +278,7 @@ hipError_t launch_skinny_nph(const GemmArgs& a, int cus, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
-  cus = cus > 0 ? cus : 1;
+static hipError_t launch_skinny_piece(const GemmArgs& a, int cus, hipStream_t stream) {
   switch (a.K / kPhaseK) {
     case 1: return launch_skinny_nph<1>(a, cus, stream);
     case 2: return launch_skinny_nph<2>(a, cus, stream);
@@ -290,6 +290,37 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
     case 8: return launch_skinny_nph<8>(a, cus, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+// K up to kSkinnyMaxK in one launch.  A longer K (f32 output only) is cut into the fewest pieces
+// of at most 7 phases, as equal as possible (so each keeps two tiles per workgroup and one
+// workgroup per compute unit); the first piece writes C and each later one, launched after it on
+// the same stream, adds its scaled partial product: C = fl(...fl(acc_0 a) + acc_1 a ...).
+hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  cus = cus > 0 ? cus : 1;
+  if (a.K <= kSkinnyMaxK) return launch_skinny_piece(a, cus, stream);
+  const int phases = a.K / kPhaseK;
+  const int pieces = (phases + 6) / 7;
+  int k0 = 0;
+  for (int i = 0; i < pieces; ++i) {
+    const int nph = phases / pieces + (i < phases % pieces ? 1 : 0);
+    GemmArgs b = a;
+    b.a_codes = a.a_codes + k0 / 2;
+    b.a_scales = a.a_scales + k0 / 16;
+    b.w_codes = a.w_codes + k0 / 2;
+    b.w_scales = a.w_scales + k0 / 16;
+    b.K = nph * kPhaseK;
+    b.k_pitch = a.K;
+    b.c_accumulate = i > 0 ? 1 : 0;
+    e = launch_skinny_piece(b, cus, stream);
+    if (e != hipSuccess) return e;
+    k0 += b.K;
+  }
+  return hipSuccess;
 }
 
 }  // namespace nvfp4

@@ -23,8 +23,12 @@ struct GemmArgs {
   const uint8_t* w_scales;
   const float* seg_g;
   int32_t M, N, K;
+  // elements per row of A and W (codes k_pitch / 2 bytes, scales k_pitch / 16): K, except in the
+  // pieces into which the decode-shaped product splits a long K
+  int32_t k_pitch;
   void* c;
-  int32_t c_bf16;  // 0: f32 output, 1: bf16 output
+  int32_t c_bf16;        // 0: f32 output, 1: bf16 output
+  int32_t c_accumulate;  // decode-shaped product, f32 output only: 1 adds into C instead of writing
   int64_t ldc;
   SegTable seg;
 };
@@ -74,6 +78,6 @@ constexpr int64_t kSkinnyMaxK = 8192;
 // Which kernel family serves a problem.  The choice depends on M and K only, never on N, so a
 // fused product and its per-segment products run the same kernel with the same accumulation order.
 enum class GemmPath { General, Tiled, Skinny };
-GemmPath choose_gemm_path(int64_t M, int64_t K);
+GemmPath choose_gemm_path(int64_t M, int64_t K, bool c_bf16);
 
 }  // namespace nvfp4

@@ -60,7 +60,7 @@ def test_workload1_full():
 @pytest.mark.parametrize("M,N,K", [
     (1, 1, 16), (1, 37, 64), (5, 70, 48), (33, 65, 80), (31, 129, 128), (64, 64, 64),
     (129, 130, 192), (200, 300, 1024), (257, 255, 320), (96, 160, 5120),
-    # decode-shaped (M <= 16): the skinny kernel for K a multiple of 1024 up to 8192 (ragged N),
+    # decode-shaped (M <= 16): the skinny kernel for K a multiple of 1024 (in pieces above 8192),
     # the tiled or general kernel otherwise
     (1, 100, 512), (3, 77, 1536), (16, 40, 1024), (7, 33, 512), (16, 16, 2048), (5, 3, 16384),
     (2, 300, 17408), (1, 19, 384),
@@ -70,6 +70,27 @@ def test_ragged_shapes(M, N, K):
     wt = random_matrix(N * 5 + K, N, K, std=0.02)
     enc = _encode(a, wt, [0, N])
     _check(*enc, [0, N], f"M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 48, 9216), (16, 320, 17408), (7, 130, 15360), (4, 40, 31744)])
+def test_decode_long_k_in_pieces(M, N, K):
+    # at most 16 rows and K above 8192 (f32 output): the skinny kernel in two to five pieces of K
+    # (9, 17, 15 and 31 phases of 1024), later pieces adding into C; three fused modules
+    a = random_matrix(M * 11 + K, M, K, outlier_cols=max(1, K // 200))
+    wt = random_matrix(N * 3 + K, N, K, std=0.02)
+    segs = [0, N // 3, N // 2, N]
+    _check(*_encode(a, wt, segs), segs, f"long K M={M} N={N} K={K}")
+
+
+def test_decode_long_k_bf16_output():
+    # a bf16 C would round every partial sum of a split K, so this shape takes the tiled kernel
+    a = random_matrix(71, 3, 17408, outlier_cols=40)
+    wt = random_matrix(72, 96, 17408, std=0.02)
+    ac, as_, ga, wc, ws, gw = _encode(a, wt, [0, 96])
+    C = _gpu_product(ac, as_, ga, wc, ws, gw, [0, 96], out_dtype="bf16")
+    R = oracle.gemm_exact(ac, as_, ga, wc, ws, gw, [0, 96])
+    assert np.all(np.abs(C - R) <= 2.0 ** -8 * np.abs(R) + 1e-4 * oracle.gemm_abs_bound(
+        ac, as_, ga, wc, ws, gw, [0, 96]))
 
 
 def test_bf16_output():
