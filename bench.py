@@ -9,8 +9,8 @@ tensors resident in HBM before the timed region starts.
 Printed: one JSON line with the prefill throughput (TFLOP/s = 2MNK / step time), the roofline of
 the dominant kernel (the product; its average duration from HIP events recorded on the stream it
 is launched on), the activation encode with the static and with the dynamic global scale, the
-decode-shaped GEMV throughput (GB/s of algorithmic bytes), and the CPU oracle timed on a bounded
-sample of the same workload.
+decode-shaped product throughput (GB/s of algorithmic bytes) on a 5120 x 5120 weight and on the
+MLP weights, and the CPU oracle timed on a bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -191,6 +191,59 @@ def decode(args, torch, nv, W):
                         "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
                         "bytes": nbytes}
     return res
+
+
+def decode_mlp(args, torch, nv, W):
+    """Decode-shaped products on the MLP weights, M in {1, 16}: gate+up (N = 2 x 17408, K = 5120,
+    two modules) and down (N = 5120, K = 17408, which the library runs as three K pieces).  NVFP4
+    weights encoded from seeded N(0, 0.02) draws, rotated over copies of about 300 MB in total
+    (beyond the last-level cache); kernel time per product from HIP-graph replays, as in
+    `decode`."""
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4242)
+    out = {}
+    for name, N, K, segs, R in (("gate_up", 34816, 5120, [0, 17408, 34816], 3),
+                                ("down", 5120, 17408, [0, 5120], 6)):
+        log(f"[bench] decode on the MLP {name} weights {N}x{K}")
+        wb = (torch.randn(N, K, generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+        parts = [nv.nvfp4_quantize(wb[lo:hi]) for lo, hi in zip(segs[:-1], segs[1:])]
+        wc = torch.cat([q[0] for q in parts])
+        ws = torch.cat([q[1] for q in parts])
+        gw = torch.cat([q[2] for q in parts])
+        del wb, parts
+        copies = [(wc.clone(), ws.clone()) for _ in range(R)]
+        del wc, ws
+        for M in (1, 16):
+            a = torch.randn(M, K, generator=gen, device=dev).to(torch.bfloat16)
+            ac, as_, ga = nv.nvfp4_quantize(a)
+            C = torch.empty((M, N), dtype=torch.float32, device=dev)
+            for wc, ws in copies:
+                nv.fused_nvfp4_gemm(ac, as_, ga, wc, ws, gw, segs, out=C)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for wc, ws in copies:
+                    nv.fused_nvfp4_gemm(ac, as_, ga, wc, ws, gw, segs, out=C)
+            graph.replay()
+            torch.cuda.synchronize()
+            reps = 10
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            k_ms = e0.elapsed_time(e1) / (reps * R)
+            del graph
+            nbytes = N * K * 9 // 16 + M * K * 9 // 16 + M * N * 4
+            gbs = nbytes / (k_ms * 1e-3) / 1e9
+            out[f"{name}_M{M}"] = {"N": N, "K": K, "kernel_us": round(k_ms * 1e3, 3),
+                                   "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                                   "bytes": nbytes}
+        del copies
+        torch.cuda.empty_cache()
+    return out
 
 
 def silu_quantize(args, torch, nv, W):
@@ -521,7 +574,8 @@ def main():
         copy_calibration(args, torch)
         return
     if args.only == "decode":
-        print(json.dumps({"decode": decode(args, torch, nv, W)}), flush=True)
+        print(json.dumps({"decode": decode(args, torch, nv, W),
+                          "decode_mlp": decode_mlp(args, torch, nv, W)}), flush=True)
         return
     if args.only == "silu":
         print(json.dumps({"silu_mul_quantize": silu_quantize(args, torch, nv, W)}), flush=True)
@@ -539,6 +593,7 @@ def main():
     p = prefill(args, torch, nv, W)
     run_rest = args.only == "all"
     dec = decode(args, torch, nv, W) if run_rest and not args.no_decode else None
+    dec_mlp = decode_mlp(args, torch, nv, W) if run_rest and not args.no_decode else None
     silu = silu_quantize(args, torch, nv, W) if run_rest else None
     kv = kv_store(args, torch, nv, W) if run_rest else None
     errs = error_tools(args, torch, nv, W) if run_rest else None
@@ -578,6 +633,7 @@ def main():
                                  "frac_hbm": round(qd_gbs / HBM_PEAK_GBS, 4),
                                  "bytes": int(p["qd_bytes"])}},
         "decode": dec,
+        "decode_mlp": dec_mlp,
         "silu_mul_quantize": silu,
         "kv_fp8_store": kv,
         "fake_quantize": errs and errs["fake_quantize"],
