@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libnvfp4.so")
 
-SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "gemm_skinny.hip", "kv_cache.hip",
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "gemm_skinny.hip", "gemm_stream.hip", "kv_cache.hip",
            "fake_quant.hip"]
 
 ARCH = "gfx950"

@@ -623,11 +623,11 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
 }
 
 GemmPath choose_gemm_path(int64_t M, int64_t K, bool c_bf16) {
-  // decode shapes (at most 16 activation rows) stream the weights with the skinny kernel, a K above
-  // kSkinnyMaxK in pieces that add into an f32 C (a bf16 C would round every partial sum); the
-  // tiled kernel needs whole K chunks of 64 (the host layer keeps every operand below 2 GiB, so
-  // 32-bit row offsets suffice)
-  if (M <= 16 && K % 1024 == 0 && (K <= kSkinnyMaxK || !c_bf16)) return GemmPath::Skinny;
+  // decode shapes (at most 16 activation rows) stream the weights with the skinny or the streaming
+  // kernel, a K above kStreamMaxK in pieces that add into an f32 C (a bf16 C would round every
+  // partial sum); the tiled kernel needs whole K chunks of 64 (the host layer keeps every operand
+  // below 2 GiB, so 32-bit row offsets suffice)
+  if (M <= 16 && K % 1024 == 0 && (K <= kStreamMaxK || !c_bf16)) return GemmPath::Skinny;
   return K % 64 == 0 ? GemmPath::Tiled : GemmPath::General;
 }
 

@@ -292,17 +292,22 @@ static hipError_t launch_skinny_piece(const GemmArgs& a, int cus, hipStream_t st
   }
 }
 
-// K up to kSkinnyMaxK in one launch.  A longer K (f32 output only) is cut into the fewest pieces
-// of at most 7 phases, as equal as possible (so each keeps two tiles per workgroup and one
-// workgroup per compute unit); the first piece writes C and each later one, launched after it on
-// the same stream, adds its scaled partial product: C = fl(...fl(acc_0 a) + acc_1 a ...).
+// Decode-shaped products.  Up to 32 columns per compute unit and K up to kSkinnyMaxK: this
+// kernel, in one pass.  More columns or a longer K, up to kStreamMaxK: the streaming kernel
+// (gemm_stream.hip), which walks tiles with its weight copies always in flight.  A K beyond that
+// (f32 output only) is cut into the fewest pieces of at most 7 phases, as equal as possible (so each
+// keeps two tiles per workgroup and one workgroup per compute unit); the first piece writes C and
+// each later one, launched after it on the same stream, adds its scaled partial product:
+// C = fl(...fl(acc_0 a) + acc_1 a ...).
 hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   cus = cus > 0 ? cus : 1;
-  if (a.K <= kSkinnyMaxK) return launch_skinny_piece(a, cus, stream);
+  const int per_cu = (a.N + cus - 1) / cus;
+  if (a.K <= kSkinnyMaxK && per_cu <= 32) return launch_skinny_piece(a, cus, stream);
+  if (a.K <= kStreamMaxK) return launch_gemm_stream(a, stream);
   const int phases = a.K / kPhaseK;
   const int pieces = (phases + 6) / 7;
   int k0 = 0;

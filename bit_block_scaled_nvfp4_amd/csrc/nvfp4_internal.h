@@ -74,10 +74,13 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);
 // The skinny (decode-shape) kernel keeps a workgroup's 16 weight rows over all of K in LDS
 // (9/16 byte per element), in phases of 1024: K up to this bound, a multiple of 1024.
 constexpr int64_t kSkinnyMaxK = 8192;
+// Largest K of the streaming decode kernel (its LDS holds the activation scales of all of K).
+constexpr int64_t kStreamMaxK = 32768;
 
 // Which kernel family serves a problem.  The choice depends on M and K only, never on N, so a
 // fused product and its per-segment products run the same kernel with the same accumulation order.
 enum class GemmPath { General, Tiled, Skinny };
 GemmPath choose_gemm_path(int64_t M, int64_t K, bool c_bf16);
+hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream);
 
 }  // namespace nvfp4

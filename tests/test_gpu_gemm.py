@@ -72,18 +72,30 @@ def test_ragged_shapes(M, N, K):
     _check(*enc, [0, N], f"M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 48, 9216), (16, 320, 17408), (7, 130, 15360), (4, 40, 31744)])
-def test_decode_long_k_in_pieces(M, N, K):
-    # at most 16 rows and K above 8192 (f32 output): the skinny kernel in two to five pieces of K
-    # (9, 17, 15 and 31 phases of 1024), later pieces adding into C; three fused modules
+@pytest.mark.parametrize("M,N,K", [(1, 48, 9216), (16, 320, 17408), (7, 130, 15360), (4, 40, 31744),
+                                   (2, 40, 33792), (3, 50, 65536)])
+def test_decode_long_k(M, N, K):
+    # at most 16 rows and K above 8192: the streaming kernel up to K = 32768 (9 to 31 phases of
+    # 1024), beyond that the skinny kernel in 5 and 10 pieces of K that add into C; three fused
+    # modules
     a = random_matrix(M * 11 + K, M, K, outlier_cols=max(1, K // 200))
     wt = random_matrix(N * 3 + K, N, K, std=0.02)
     segs = [0, N // 3, N // 2, N]
     _check(*_encode(a, wt, segs), segs, f"long K M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 9000, 2048), (16, 8250, 1024), (5, 12345, 3072)])
+def test_decode_many_columns(M, N, K):
+    # more than 32 columns per compute unit: the streaming kernel walks several 16-column tiles per
+    # workgroup (ragged last tile), two fused modules
+    a = random_matrix(M * 13 + N, M, K, outlier_cols=3)
+    wt = random_matrix(N + K, N, K, std=0.02)
+    segs = [0, N // 2 + 5, N]
+    _check(*_encode(a, wt, segs), segs, f"many columns M={M} N={N} K={K}")
+
+
 def test_decode_long_k_bf16_output():
-    # a bf16 C would round every partial sum of a split K, so this shape takes the tiled kernel
+    # bf16 C with a long K: the streaming kernel (one pass over K, so no partial sums are rounded)
     a = random_matrix(71, 3, 17408, outlier_cols=40)
     wt = random_matrix(72, 96, 17408, std=0.02)
     ac, as_, ga, wc, ws, gw = _encode(a, wt, [0, 96])
