@@ -8,12 +8,16 @@
 // Work split.  One persistent workgroup (8 wavefronts) per compute unit walks its tiles of 16
 // output columns, b, b + G, b + 2G, ...  A tile's weight rows are consumed in units of one
 // 1024-element K phase: 16 rows x 512 code bytes and 16 rows x 64 scale bytes.  Units stream
-// through a ring of kRing LDS slots.  The copies of unit u + kAhead are issued while unit u is
-// computed, so kAhead units (63 KB per compute unit) are always in flight and the weight stream
-// never waits for a tile boundary.  Every wavefront issues exactly three vector memory instructions
-// per unit (the code copy, the scale copy and its activation fragment), so the wait for unit u is
-// a compile-time vmcnt.  The activation block scales of all K are copied once; the activation
-// codes, which every tile reuses, are reloaded per unit from L2.
+// through LDS slots while earlier units are computed, so the weight stream never waits for a tile
+// boundary.  Two forms:
+//  * K <= 8192 (gemm_stream_cached_kernel): every wavefront decodes its activation fragments of all
+//    phases once and keeps them in registers; slots hold two tiles, unit (t + 1, q) is copied
+//    while unit (t, q) is computed, two copies per unit.
+//  * longer K (gemm_stream_kernel): a ring of kRing slots with kAhead units in flight; the
+//    activation block scales of all K are copied once and the activation codes reloaded per unit
+//    from L2 (three vector memory instructions per unit).
+// Every wavefront issues the same vector memory instructions per unit, so each wait is a
+// compile-time vmcnt.
 //
 // Per unit each wavefront takes one eighth of the phase (128 elements) with the K-slot permutation
 // and code-slot swizzle of the skinny kernel: lane (r, g) = (l % 16, l / 16) holds weight row r and
@@ -225,6 +229,163 @@ __global__ void __launch_bounds__(kThreads) gemm_stream_kernel(StreamArgs s) {
   wait_vmcnt<0>();
 }
 
+// K <= 8192 (NPH phases): the same stream with the activations decoded once.  Every tile reuses
+// the activation fragments of the NPH phases, so each wavefront decodes its fragment of every
+// phase before the stream starts and keeps it in registers (NPH x 16 VGPRs); a unit is then two
+// copies and no activation work.  Slots hold two tiles (2 NPH, statically named): unit (t + 1, q)
+// is copied into the slot of unit (t - 1, q) while unit (t, q) is computed, so NPH units are in
+// flight, and with the tile loop unrolled by two every slot and phase index is a compile-time
+// constant.
+constexpr int kVmemPerUnitCached = 2;
+
+__device__ __forceinline__ void issue_weights(const GemmArgs& p, int tile, int q, uint8_t* slot,
+                                              int wave, int lane) {
+  const int kb = p.K / 2, ks = p.K / 16;
+  const int t = wave * 64 + lane;
+  const int row = t / kPieces;
+  const int jl = t - row * kPieces;
+  const int j = (jl & ~15) | ((jl ^ row) & 15);
+  const int grow = min(tile * 16 + row, p.N - 1);
+  __builtin_amdgcn_global_load_lds(p.w_codes + (int64_t)grow * kb + q * (kUnitK / 2) + j * 16,
+                                   slot + wave * 64 * 16, 16, 0, 0);
+  const int ts = t & 255;
+  const int srow = ts >> 4, dw = ts & 15;
+  const int gsrow = min(tile * 16 + srow, p.N - 1);
+  __builtin_amdgcn_global_load_lds(p.w_scales + (int64_t)gsrow * ks + q * (kUnitK / 16) + dw * 4,
+                                   slot + kCodeBytes + (wave & 3) * 64 * 4, 4, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ void compute_weights(const uint8_t* slot, const half8_t (&av)[4],
+                                                int wave, int r, int g, floatx4_t& acc) {
+  const int j = wave * 4 + g;
+  const uint4 ww =
+      *reinterpret_cast<const uint4*>(slot + (r * kPieces + ((j & ~15) | ((j ^ r) & 15))) * 16);
+  const uint32_t ws2 = *reinterpret_cast<const uint16_t*>(slot + kCodeBytes + r * 64 + j * 2);
+  const half2_t sw = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ws2, 1.0f, false);
+  const uint32_t wq[4] = {ww.x, ww.y, ww.z, ww.w};
+#pragma unroll
+  for (int s2 = 0; s2 < 4; ++s2) {
+    const half8_t bv = decode8(wq[s2], s2 < 2 ? sw[0] : sw[1]);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[s2], bv, acc, 0, 0, 0);
+  }
+}
+
+// End of tile t: fixed-order sum of the 8 wavefronts' partial tiles, scaled, stored by wavefront 0.
+__device__ __forceinline__ void tile_epilogue(const GemmArgs& p, floatx4_t (&partial)[kWaves][64],
+                                              const float* gtab, int tile, int wave, int lane,
+                                              int r, int g, floatx4_t& acc) {
+  partial[wave][lane] = acc;
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only: copies in flight are not waited for
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  if (wave == 0) {
+    floatx4_t sum = partial[0][lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) sum += partial[w][lane];
+    const int n = tile * 16 + r;
+    if (n < p.N) {
+      const float al = 1.0f / (gtab[NVFP4_MAX_SEGMENTS] * gtab[column_segment(p.seg, n)]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 4 * g + e;
+        if (m < p.M) store_c(p.c, p.c_bf16, p.ldc, m, n, sum[e] * al);
+      }
+    }
+  }
+  acc = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+template <int NPH>
+__global__ void __launch_bounds__(kThreads) gemm_stream_cached_kernel(StreamArgs s) {
+  static_assert(NPH >= 1 && NPH <= 8, "K up to 8192");
+  constexpr int S = 2 * NPH;
+#define NVFP4_SLOT(i) \
+  __shared__ __attribute__((aligned(16))) uint8_t sl##i[(i) < S ? kSlotBytes : 16];
+  NVFP4_SLOT(0) NVFP4_SLOT(1) NVFP4_SLOT(2) NVFP4_SLOT(3) NVFP4_SLOT(4) NVFP4_SLOT(5)
+  NVFP4_SLOT(6) NVFP4_SLOT(7) NVFP4_SLOT(8) NVFP4_SLOT(9) NVFP4_SLOT(10) NVFP4_SLOT(11)
+  NVFP4_SLOT(12) NVFP4_SLOT(13) NVFP4_SLOT(14) NVFP4_SLOT(15)
+#undef NVFP4_SLOT
+  uint8_t* const slot[16] = {sl0, sl1, sl2, sl3, sl4, sl5, sl6, sl7,
+                             sl8, sl9, sl10, sl11, sl12, sl13, sl14, sl15};
+  __shared__ floatx4_t partial[kWaves][64];
+  __shared__ float gtab[NVFP4_MAX_SEGMENTS + 1];
+
+  const GemmArgs& p = s.p;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const bool arow_valid = r < p.M;
+  const int ksa = p.K / 16;
+  const int my_tiles = (s.ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int tile0 = (int)blockIdx.x, tstep = (int)gridDim.x;
+  const int last_tile = tile0 + (my_tiles - 1) * tstep;
+
+  if (threadIdx.x < p.seg.nseg) gtab[threadIdx.x] = p.seg_g[threadIdx.x];
+  if (threadIdx.x == 0) gtab[NVFP4_MAX_SEGMENTS] = *p.a_g;
+
+  // activation scales of all K staged in slot 0 (K / 16 <= 512 bytes per row, 16 rows), and this
+  // lane's activation codes of every phase
+  uint8_t* const asc = sl0;
+  {
+    const int per_row = ksa / 16;
+    for (int i = threadIdx.x; i < p.M * per_row; i += kThreads) {
+      const int row = i / per_row;
+      __builtin_amdgcn_global_load_lds(p.a_scales + (int64_t)row * ksa + (i - row * per_row) * 16,
+                                       asc + (i & ~63) * 16, 16, 0, 0);
+    }
+  }
+  uint4 aw[NPH];
+  const int arow = min(r, p.M - 1);
+#pragma unroll
+  for (int q = 0; q < NPH; ++q)
+    aw[q] = *reinterpret_cast<const uint4*>(p.a_codes + (int64_t)arow * (p.K / 2) +
+                                            q * (kUnitK / 2) + wave * 64 + g * 16);
+  wait_vmcnt<0>();
+  __syncthreads();
+  half8_t act[NPH][4];
+  const uint32_t keep = arow_valid ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+  for (int q = 0; q < NPH; ++q) {
+    const int c = q * (kUnitK / 128) + wave;
+    const uint32_t as2 = *reinterpret_cast<const uint16_t*>(asc + r * ksa + c * 8 + g * 2) & keep;
+    const half2_t sa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(as2, 1.0f, false);
+    const uint32_t aq[4] = {aw[q].x & keep, aw[q].y & keep, aw[q].z & keep, aw[q].w & keep};
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) act[q][s2] = decode8(aq[s2], s2 < 2 ? sa[0] : sa[1]);
+  }
+  __syncthreads();  // every wavefront has read the staged scales before slot 0 is reused
+
+  // tile 0's units
+#pragma unroll
+  for (int q = 0; q < NPH; ++q) issue_weights(p, tile0, q, slot[q], wave, lane);
+
+  floatx4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int i = 0; i < my_tiles; i += 2) {
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int ti = i + par;
+      const int tile = tile0 + ti * tstep;
+      // the tile whose units are copied during this one (the last tile again past the end)
+      const int tnext = ti + 1 < my_tiles ? tile + tstep : last_tile;
+#pragma unroll
+      for (int q = 0; q < NPH; ++q) {
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<(NPH - 1) * kVmemPerUnitCached>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue_weights(p, tnext, q, slot[(1 - par) * NPH + q], wave, lane);
+        if (ti < my_tiles) {  // uniform over the workgroup
+          compute_weights(slot[par * NPH + q], act[q], wave, r, g, acc);
+          if (q == NPH - 1) tile_epilogue(p, partial, gtab, tile, wave, lane, r, g, acc);
+        }
+      }
+    }
+  }
+  wait_vmcnt<0>();  // the copies issued past the last unit land before the LDS is released
+}
+
 }  // namespace
 
 hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream) {
@@ -237,7 +398,17 @@ hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream) {
   s.ntiles = (a.N + 15) / 16;
   s.nph = a.K / kUnitK;
   const int grid = s.ntiles < (cus > 0 ? cus : 1) ? s.ntiles : (cus > 0 ? cus : 1);
-  hipLaunchKernelGGL(gemm_stream_kernel, dim3(grid), dim3(kThreads), 0, stream, s);
+  switch (s.nph) {
+    case 1: hipLaunchKernelGGL(gemm_stream_cached_kernel<1>, dim3(grid), dim3(kThreads), 0, stream, s); break;
+    case 2: hipLaunchKernelGGL(gemm_stream_cached_kernel<2>, dim3(grid), dim3(kThreads), 0, stream, s); break;
+    case 3: hipLaunchKernelGGL(gemm_stream_cached_kernel<3>, dim3(grid), dim3(kThreads), 0, stream, s); break;
+    case 4: hipLaunchKernelGGL(gemm_stream_cached_kernel<4>, dim3(grid), dim3(kThreads), 0, stream, s); break;
+    case 5: hipLaunchKernelGGL(gemm_stream_cached_kernel<5>, dim3(grid), dim3(kThreads), 0, stream, s); break;
+    case 6: hipLaunchKernelGGL(gemm_stream_cached_kernel<6>, dim3(grid), dim3(kThreads), 0, stream, s); break;
+    case 7: hipLaunchKernelGGL(gemm_stream_cached_kernel<7>, dim3(grid), dim3(kThreads), 0, stream, s); break;
+    case 8: hipLaunchKernelGGL(gemm_stream_cached_kernel<8>, dim3(grid), dim3(kThreads), 0, stream, s); break;
+    default: hipLaunchKernelGGL(gemm_stream_kernel, dim3(grid), dim3(kThreads), 0, stream, s); break;
+  }
   return hipGetLastError();
 }
 
