@@ -248,12 +248,7 @@ gemm_skinny_kernel(GemmArgs p, int ncols) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int m = 4 * g + e;
-    if (m < p.M) {
-      if (p.c_accumulate)  // a later piece of a split K: f32 C, stream-ordered after the first
-        reinterpret_cast<float*>(p.c)[(int64_t)m * p.ldc + n] += sum[e] * al;
-      else
-        store_c(p.c, p.c_bf16, p.ldc, m, n, sum[e] * al);
-    }
+    if (m < p.M) store_c(p.c, p.c_bf16, p.ldc, m, n, sum[e] * al);
   }
 }
 
@@ -293,12 +288,13 @@ static hipError_t launch_skinny_piece(const GemmArgs& a, int cus, hipStream_t st
 }
 
 // Decode-shaped products.  Up to 32 columns per compute unit and K up to kSkinnyMaxK: this
-// kernel, in one pass.  More columns or a longer K, up to kStreamMaxK: the streaming kernel
-// (gemm_stream.hip), which walks tiles with its weight copies always in flight.  A K beyond that
-// (f32 output only) is cut into the fewest pieces of at most 7 phases, as equal as possible (so each
-// keeps two tiles per workgroup and one workgroup per compute unit); the first piece writes C and
-// each later one, launched after it on the same stream, adds its scaled partial product:
-// C = fl(...fl(acc_0 a) + acc_1 a ...).
+// kernel, in one pass.  More columns, or K up to kStreamMaxK: the streaming kernel
+// (gemm_stream.hip), which walks tiles with its weight copies always in flight.  K beyond that
+// (f32 output only): the streaming kernel on the fewest pieces of K of at most 8 phases, as equal
+// as possible; the first piece writes C and each later one, launched after it on the same stream,
+// adds its scaled partial product: C = fl(...fl(acc_0 a) + acc_1 a ...).  (Pieces are slower than
+// one pass at K = 17408, N = 5120: every piece meets the uneven share of 320 tiles among the
+// compute units again.)
 hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -309,7 +305,7 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
   if (a.K <= kSkinnyMaxK && per_cu <= 32) return launch_skinny_piece(a, cus, stream);
   if (a.K <= kStreamMaxK) return launch_gemm_stream(a, stream);
   const int phases = a.K / kPhaseK;
-  const int pieces = (phases + 6) / 7;
+  const int pieces = (phases + 7) / 8;
   int k0 = 0;
   for (int i = 0; i < pieces; ++i) {
     const int nph = phases / pieces + (i < phases % pieces ? 1 : 0);
@@ -321,7 +317,7 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
     b.K = nph * kPhaseK;
     b.k_pitch = a.K;
     b.c_accumulate = i > 0 ? 1 : 0;
-    e = launch_skinny_piece(b, cus, stream);
+    e = launch_gemm_stream(b, stream);
     if (e != hipSuccess) return e;
     k0 += b.K;
   }

@@ -69,7 +69,7 @@ __device__ __forceinline__ void unit_coords(const StreamArgs& s, int units, int 
 __device__ __forceinline__ void issue_unit(const StreamArgs& s, int tile, int q, uint8_t* slot,
                                            int wave, int lane, uint4& aw) {
   const GemmArgs& p = s.p;
-  const int kb = p.K / 2, ks = p.K / 16;
+  const int kb = p.k_pitch / 2, ks = p.k_pitch / 16;
   const int t = wave * 64 + lane;
   const int row = t / kPieces;                     // 0..15
   const int jl = t - row * kPieces;
@@ -155,8 +155,9 @@ __global__ void __launch_bounds__(kThreads) gemm_stream_kernel(StreamArgs s) {
     const int per_row = ksa / 16;  // 16-byte pieces per row
     for (int i = threadIdx.x; i < p.M * per_row; i += kThreads) {
       const int row = i / per_row;
-      __builtin_amdgcn_global_load_lds(p.a_scales + (int64_t)row * ksa + (i - row * per_row) * 16,
-                                       asc + (i & ~63) * 16, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          p.a_scales + (int64_t)row * (p.k_pitch / 16) + (i - row * per_row) * 16,
+          asc + (i & ~63) * 16, 16, 0, 0);
     }
   }
   // every wavefront must have issued the same number of instructions before the first unit:
@@ -240,7 +241,7 @@ constexpr int kVmemPerUnitCached = 2;
 
 __device__ __forceinline__ void issue_weights(const GemmArgs& p, int tile, int q, uint8_t* slot,
                                               int wave, int lane) {
-  const int kb = p.K / 2, ks = p.K / 16;
+  const int kb = p.k_pitch / 2, ks = p.k_pitch / 16;  // row pitches (a piece of K may be narrower)
   const int t = wave * 64 + lane;
   const int row = t / kPieces;
   const int jl = t - row * kPieces;
@@ -290,7 +291,11 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, floatx4_t (&par
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = 4 * g + e;
-        if (m < p.M) store_c(p.c, p.c_bf16, p.ldc, m, n, sum[e] * al);
+        if (m >= p.M) continue;
+        if (p.c_accumulate)  // a later piece of a split K: f32 C, stream-ordered after the first
+          reinterpret_cast<float*>(p.c)[(int64_t)m * p.ldc + n] += sum[e] * al;
+        else
+          store_c(p.c, p.c_bf16, p.ldc, m, n, sum[e] * al);
       }
     }
   }
@@ -332,15 +337,16 @@ __global__ void __launch_bounds__(kThreads) gemm_stream_cached_kernel(StreamArgs
     const int per_row = ksa / 16;
     for (int i = threadIdx.x; i < p.M * per_row; i += kThreads) {
       const int row = i / per_row;
-      __builtin_amdgcn_global_load_lds(p.a_scales + (int64_t)row * ksa + (i - row * per_row) * 16,
-                                       asc + (i & ~63) * 16, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          p.a_scales + (int64_t)row * (p.k_pitch / 16) + (i - row * per_row) * 16,
+          asc + (i & ~63) * 16, 16, 0, 0);
     }
   }
   uint4 aw[NPH];
   const int arow = min(r, p.M - 1);
 #pragma unroll
   for (int q = 0; q < NPH; ++q)
-    aw[q] = *reinterpret_cast<const uint4*>(p.a_codes + (int64_t)arow * (p.K / 2) +
+    aw[q] = *reinterpret_cast<const uint4*>(p.a_codes + (int64_t)arow * (p.k_pitch / 2) +
                                             q * (kUnitK / 2) + wave * 64 + g * 16);
   wait_vmcnt<0>();
   __syncthreads();
