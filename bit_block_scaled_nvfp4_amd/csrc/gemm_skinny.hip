@@ -288,8 +288,8 @@ static hipError_t launch_skinny_piece(const GemmArgs& a, int cus, hipStream_t st
 }
 
 // Decode-shaped products.  Up to 32 columns per compute unit and K up to kSkinnyMaxK: this
-// kernel, in one pass.  More columns, or K up to kStreamMaxK: the streaming kernel
-// (gemm_stream.hip), which walks tiles with its weight copies always in flight.  K beyond that
+// kernel, in one pass.  More columns, or K up to kStreamMaxK: the streaming kernels
+// (gemm_stream.hip), which keep their weight copies always in flight.  K beyond that
 // (f32 output only): the streaming kernel on the fewest pieces of K of at most 8 phases, as equal
 // as possible; the first piece writes C and each later one, launched after it on the same stream,
 // adds its scaled partial product: C = fl(...fl(acc_0 a) + acc_1 a ...).  (Pieces are slower than

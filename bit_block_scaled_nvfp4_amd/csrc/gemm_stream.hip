@@ -9,13 +9,16 @@
 // output columns, b, b + G, b + 2G, ...  A tile's weight rows are consumed in units of one
 // 1024-element K phase: 16 rows x 512 code bytes and 16 rows x 64 scale bytes.  Units stream
 // through LDS slots while earlier units are computed, so the weight stream never waits for a tile
-// boundary.  Two forms:
+// boundary.  Three forms:
 //  * K <= 8192 (gemm_stream_cached_kernel): every wavefront decodes its activation fragments of all
 //    phases once and keeps them in registers; slots hold two tiles, unit (t + 1, q) is copied
 //    while unit (t, q) is computed, two copies per unit.
-//  * longer K (gemm_stream_kernel): a ring of kRing slots with kAhead units in flight; the
-//    activation block scales of all K are copied once and the activation codes reloaded per unit
-//    from L2 (three vector memory instructions per unit).
+//  * longer K, at most 16 columns per compute unit (gemm_stream_kernel): a ring of
+//    kRing slots with kAhead units in flight; the activation block scales of all K are copied once
+//    and the activation codes reloaded per unit from L2 (three vector memory instructions per
+//    unit).
+//  * longer K, more than 16 columns per compute unit (gemm_stream_pair_kernel): equal column
+//    ranges instead of tiles dealt round robin, two tiles per unit; described at the kernel.
 // Every wavefront issues the same vector memory instructions per unit, so each wait is a
 // compile-time vmcnt.
 //
@@ -54,6 +57,26 @@ struct StreamArgs {
   int ntiles;  // ceil(N / 16)
   int nph;     // K / 1024
 };
+
+// The epilogue's global scales gW[0 .. nseg - 1] and gA into the LDS table, called once the first
+// weight copies are in flight.  They are scalar loads, whose waits count scalar memory operations
+// only (not the copies); the barrier before the first epilogue publishes the table.
+__device__ __forceinline__ void stage_global_scales(const GemmArgs& p, float* gtab) {
+  // read through the constant address space: the values were written by earlier launches and do not
+  // change during this one, and such uniform loads are scalar loads wherever they sit (after the
+  // copies a plain global load could not be proven unclobbered and would be a vector load)
+  typedef const __attribute__((address_space(4))) float* const_f32_ptr;
+  const const_f32_ptr sg = (const_f32_ptr)p.seg_g;
+  const const_f32_ptr ag = (const_f32_ptr)p.a_g;
+  float v[NVFP4_MAX_SEGMENTS + 1];
+#pragma unroll
+  for (int t = 0; t < NVFP4_MAX_SEGMENTS; ++t) v[t] = sg[min(t, p.seg.nseg - 1)];
+  v[NVFP4_MAX_SEGMENTS] = ag[0];
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int t = 0; t <= NVFP4_MAX_SEGMENTS; ++t) gtab[t] = v[t];
+  }
+}
 
 // Tile and phase of unit u of this workgroup; units past the last real one repeat it (their
 // copies are redundant and their compute is skipped).
@@ -145,12 +168,10 @@ __global__ void __launch_bounds__(kThreads) gemm_stream_kernel(StreamArgs s) {
   const int my_tiles = (s.ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
   const int units = my_tiles * s.nph;
 
-  // the global-scale table, read before any copy is in flight (its wait then costs nothing)
-  if (threadIdx.x < p.seg.nseg) gtab[threadIdx.x] = p.seg_g[threadIdx.x];
-  if (threadIdx.x == 0) gtab[NVFP4_MAX_SEGMENTS] = *p.a_g;
-  __syncthreads();
 
-  // the activation block scales of all K, copied once (older than every unit's copies)
+  // the activation block scales of all K, copied once.  They are older than every unit's copies,
+  // and the wait for a unit leaves only later units' instructions outstanding (the same number in
+  // every wavefront), so it covers them whatever number each wavefront issued here.
   {
     const int per_row = ksa / 16;  // 16-byte pieces per row
     for (int i = threadIdx.x; i < p.M * per_row; i += kThreads) {
@@ -160,9 +181,6 @@ __global__ void __launch_bounds__(kThreads) gemm_stream_kernel(StreamArgs s) {
           asc + (i & ~63) * 16, 16, 0, 0);
     }
   }
-  // every wavefront must have issued the same number of instructions before the first unit:
-  // wavefronts that copied fewer activation-scale pieces wait for theirs now
-  wait_vmcnt<0>();
 
   uint4 aw[kRing];
 #pragma unroll
@@ -171,6 +189,7 @@ __global__ void __launch_bounds__(kThreads) gemm_stream_kernel(StreamArgs s) {
     unit_coords(s, units, k, tile, q);
     issue_unit(s, tile, q, ring[k], wave, lane, aw[k]);
   }
+  stage_global_scales(p, gtab);
 
   floatx4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int u0 = 0; u0 < units; u0 += kRing) {
@@ -327,6 +346,9 @@ __global__ void __launch_bounds__(kThreads) gemm_stream_cached_kernel(StreamArgs
   const int tile0 = (int)blockIdx.x, tstep = (int)gridDim.x;
   const int last_tile = tile0 + (my_tiles - 1) * tstep;
 
+
+  // (here the table is read first: issuing tile 0's copies before the activation work measured
+  // slower in this form)
   if (threadIdx.x < p.seg.nseg) gtab[threadIdx.x] = p.seg_g[threadIdx.x];
   if (threadIdx.x == 0) gtab[NVFP4_MAX_SEGMENTS] = *p.a_g;
 
@@ -392,6 +414,184 @@ __global__ void __launch_bounds__(kThreads) gemm_stream_cached_kernel(StreamArgs
   wait_vmcnt<0>();  // the copies issued past the last unit land before the LDS is released
 }
 
+// Column-pair form (K beyond the cached form, more than 16 columns per compute unit when the
+// columns are shared evenly).  Workgroup b owns the `ncols` columns [b ncols, (b + 1) ncols), ncols =
+// ceil(N / compute units), so every compute unit streams the same number of weight bytes (tiles of
+// 16 dealt round robin leave some compute units two tiles and others one when N / 16 is not a
+// multiple of their count).  It walks them in groups of 32 columns (two tiles; rows past the last
+// column repeat it and are never stored), and a unit is one K phase of a group: both tiles' codes
+// and scales (18 KiB) and the activation fragment, which is decoded once for the two tiles.  Units
+// stream through a ring of kPairRing statically named slots with kPairRing - 1 in flight.
+constexpr int kPairRing = 6;
+constexpr int kPairAhead = kPairRing - 1;
+constexpr int kPairBytes = 2 * kCodeBytes + 2 * kScaleBytes;
+constexpr int kVmemPerPair = 4;
+
+struct PairArgs {
+  GemmArgs p;
+  int ncols;  // columns per workgroup
+  int nph;    // K / 1024
+};
+
+__device__ __forceinline__ void issue_pair(const PairArgs& s, int cb, int clast, int q,
+                                           uint8_t* slot, int wave, int lane, uint4& aw) {
+  const GemmArgs& p = s.p;
+  const int kb = p.k_pitch / 2, ks = p.k_pitch / 16;
+  const int t = wave * 64 + lane;
+  const int row = t / kPieces;
+  const int jl = t - row * kPieces;
+  const int j = (jl & ~15) | ((jl ^ row) & 15);
+#pragma unroll
+  for (int tile = 0; tile < 2; ++tile) {
+    const int grow = min(cb + tile * 16 + row, clast);
+    __builtin_amdgcn_global_load_lds(p.w_codes + (int64_t)grow * kb + q * (kUnitK / 2) + j * 16,
+                                     slot + tile * kCodeBytes + wave * 64 * 16, 16, 0, 0);
+  }
+  // scale bytes of the 32 rows, 64 each: thread t copies dword t % 16 of row t / 16
+  const int gsrow = min(cb + (t >> 4), clast);
+  __builtin_amdgcn_global_load_lds(p.w_scales + (int64_t)gsrow * ks + q * (kUnitK / 16) + (t & 15) * 4,
+                                   slot + 2 * kCodeBytes + wave * 64 * 4, 4, 0, 0);
+  const int r = lane & 15, g = lane >> 4;
+  const int arow = min(r, p.M - 1);
+  aw = *reinterpret_cast<const uint4*>(p.a_codes + (int64_t)arow * kb + q * (kUnitK / 2) +
+                                       wave * 64 + g * 16);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ void compute_pair(const uint8_t* slot, const uint8_t* asc, int ksa,
+                                             int q, int wave, int r, int g, bool arow_valid,
+                                             const uint4& aw_in, floatx4_t (&acc)[2]) {
+  const uint32_t keep = arow_valid ? 0xFFFFFFFFu : 0u;
+  const uint32_t aq[4] = {aw_in.x & keep, aw_in.y & keep, aw_in.z & keep, aw_in.w & keep};
+  const int c = q * (kUnitK / 128) + wave;
+  const uint32_t as2 = *reinterpret_cast<const uint16_t*>(asc + r * ksa + c * 8 + g * 2) & keep;
+  const half2_t sa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(as2, 1.0f, false);
+  const int j = wave * 4 + g;
+  const int piece = (r * kPieces + ((j & ~15) | ((j ^ r) & 15))) * 16;
+  uint4 ww[2];
+  half2_t sw[2];
+#pragma unroll
+  for (int tile = 0; tile < 2; ++tile) {
+    ww[tile] = *reinterpret_cast<const uint4*>(slot + tile * kCodeBytes + piece);
+    const uint32_t ws2 =
+        *reinterpret_cast<const uint16_t*>(slot + 2 * kCodeBytes + (tile * 16 + r) * 64 + j * 2);
+    sw[tile] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ws2, 1.0f, false);
+  }
+#pragma unroll
+  for (int s2 = 0; s2 < 4; ++s2) {
+    const half8_t av = decode8(aq[s2], s2 < 2 ? sa[0] : sa[1]);
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      const uint32_t wq = s2 == 0 ? ww[tile].x : s2 == 1 ? ww[tile].y : s2 == 2 ? ww[tile].z
+                                                                                   : ww[tile].w;
+      const half8_t bv = decode8(wq, s2 < 2 ? sw[tile][0] : sw[tile][1]);
+      acc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[tile], 0, 0, 0);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kThreads) gemm_stream_pair_kernel(PairArgs s) {
+  __shared__ __attribute__((aligned(16))) uint8_t q0[kPairBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t q1[kPairBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t q2[kPairBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t q3[kPairBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t q4[kPairBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t q5[kPairBytes];
+  uint8_t* const ring[kPairRing] = {q0, q1, q2, q3, q4, q5};
+  __shared__ __attribute__((aligned(16))) uint8_t asc[16 * (kStreamMaxK / 16)];
+  __shared__ floatx4_t partial[2][kWaves][64];
+  __shared__ float gtab[NVFP4_MAX_SEGMENTS + 1];
+
+  const GemmArgs& p = s.p;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const bool arow_valid = r < p.M;
+  const int ksa = p.K / 16;
+  const int c0 = (int)blockIdx.x * s.ncols;
+  const int cend = min(c0 + s.ncols, p.N);
+  const int clast = cend - 1;
+  const int units = ((cend - c0 + 31) / 32) * s.nph;
+
+  // activation block scales: as in gemm_stream_kernel, the unit waits cover these copies
+  {
+    const int per_row = ksa / 16;
+    for (int i = threadIdx.x; i < p.M * per_row; i += kThreads) {
+      const int row = i / per_row;
+      __builtin_amdgcn_global_load_lds(
+          p.a_scales + (int64_t)row * (p.k_pitch / 16) + (i - row * per_row) * 16,
+          asc + (i & ~63) * 16, 16, 0, 0);
+    }
+  }
+
+  // unit u: group u / nph (columns c0 + 32 (u / nph) ...), phase u % nph; units past the last
+  // repeat it (redundant copies, no compute)
+  uint4 aw[kPairRing];
+#pragma unroll
+  for (int k = 0; k < kPairAhead; ++k) {
+    const int uu = k < units ? k : units - 1;
+    const int i = uu / s.nph;
+    issue_pair(s, c0 + 32 * i, clast, uu - i * s.nph, ring[k], wave, lane, aw[k]);
+  }
+  stage_global_scales(p, gtab);
+
+  floatx4_t acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+  for (int u0 = 0; u0 < units; u0 += kPairRing) {
+#pragma unroll
+    for (int k = 0; k < kPairRing; ++k) {
+      const int u = u0 + k;
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<(kPairAhead - 1) * kVmemPerPair>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        const int un = u + kPairAhead;
+        const int uu = un < units ? un : units - 1;
+        const int i = uu / s.nph;
+        issue_pair(s, c0 + 32 * i, clast, uu - i * s.nph, ring[(k + kPairAhead) % kPairRing],
+                   wave, lane, aw[(k + kPairAhead) % kPairRing]);
+      }
+      if (u < units) {  // uniform over the workgroup
+        const int i = u / s.nph;
+        const int q = u - i * s.nph;
+        compute_pair(ring[k], asc, ksa, q, wave, r, g, arow_valid, aw[k], acc);
+        if (q == s.nph - 1) {
+          // end of a group: fixed-order sums of the 8 wavefronts' partial tiles; wavefront `tile`
+          // scales and stores tile `tile`
+          partial[0][wave][lane] = acc[0];
+          partial[1][wave][lane] = acc[1];
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+          if (wave < 2) {
+            floatx4_t sum = partial[wave][0][lane];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) sum += partial[wave][w][lane];
+            const int n = c0 + 32 * i + 16 * wave + r;
+            if (n < cend) {
+              const float al =
+                  1.0f / (gtab[NVFP4_MAX_SEGMENTS] * gtab[column_segment(p.seg, n)]);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int m = 4 * g + e;
+                if (m >= p.M) continue;
+                if (p.c_accumulate)
+                  reinterpret_cast<float*>(p.c)[(int64_t)m * p.ldc + n] += sum[e] * al;
+                else
+                  store_c(p.c, p.c_bf16, p.ldc, m, n, sum[e] * al);
+              }
+            }
+          }
+          acc[0] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+          acc[1] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+      }
+    }
+  }
+  wait_vmcnt<0>();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream) {
@@ -403,7 +603,18 @@ hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream) {
   s.p = a;
   s.ntiles = (a.N + 15) / 16;
   s.nph = a.K / kUnitK;
-  const int grid = s.ntiles < (cus > 0 ? cus : 1) ? s.ntiles : (cus > 0 ? cus : 1);
+  cus = cus > 0 ? cus : 1;
+  const int per_cu = (a.N + cus - 1) / cus;
+  if (s.nph > 8 && per_cu > 16) {
+    PairArgs pa{};
+    pa.p = a;
+    pa.ncols = per_cu;
+    pa.nph = s.nph;
+    hipLaunchKernelGGL(gemm_stream_pair_kernel, dim3((a.N + per_cu - 1) / per_cu), dim3(kThreads),
+                       0, stream, pa);
+    return hipGetLastError();
+  }
+  const int grid = s.ntiles < cus ? s.ntiles : cus;
   switch (s.nph) {
     case 1: hipLaunchKernelGGL(gemm_stream_cached_kernel<1>, dim3(grid), dim3(kThreads), 0, stream, s); break;
     case 2: hipLaunchKernelGGL(gemm_stream_cached_kernel<2>, dim3(grid), dim3(kThreads), 0, stream, s); break;

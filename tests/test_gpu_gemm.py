@@ -94,6 +94,28 @@ def test_decode_many_columns(M, N, K):
     _check(*_encode(a, wt, segs), segs, f"many columns M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(3, 4200, 9216), (16, 8250, 10240), (1, 5120, 17408)])
+def test_decode_even_column_share(M, N, K):
+    # K above 8192 and more than 16 columns per compute unit (256 of them): workgroups own equal
+    # column ranges walked in groups of 32 (17 columns and a last workgroup of one; 33 columns, two
+    # groups; 20 columns, the MLP down projection's shape), three fused modules
+    a = random_matrix(M * 17 + N, M, K, outlier_cols=max(1, K // 300))
+    wt = random_matrix(N * 5 + K, N, K, std=0.02)
+    segs = [0, N // 3 + 7, N // 2 + 1, N]
+    _check(*_encode(a, wt, segs), segs, f"even column share M={M} N={N} K={K}")
+
+
+def test_decode_even_column_share_bf16_output():
+    # the same form with bf16 C (one rounding of the FP32 result)
+    a = random_matrix(81, 5, 9216, outlier_cols=30)
+    wt = random_matrix(82, 4500, 9216, std=0.02)
+    ac, as_, ga, wc, ws, gw = _encode(a, wt, [0, 4500])
+    C = _gpu_product(ac, as_, ga, wc, ws, gw, [0, 4500], out_dtype="bf16")
+    R = oracle.gemm_exact(ac, as_, ga, wc, ws, gw, [0, 4500])
+    assert np.all(np.abs(C - R) <= 2.0 ** -8 * np.abs(R) + 1e-4 * oracle.gemm_abs_bound(
+        ac, as_, ga, wc, ws, gw, [0, 4500]))
+
+
 def test_decode_long_k_bf16_output():
     # bf16 C with a long K: the streaming kernel (one pass over K, so no partial sums are rounded)
     a = random_matrix(71, 3, 17408, outlier_cols=40)
