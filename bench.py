@@ -195,7 +195,7 @@ def decode(args, torch, nv, W):
 
 def decode_mlp(args, torch, nv, W):
     """Decode-shaped products on the MLP weights, M in {1, 16}: gate+up (N = 2 x 17408, K = 5120,
-    two modules) and down (N = 5120, K = 17408, which the library runs as three K pieces).  NVFP4
+    two modules) and down (N = 5120, K = 17408), each one launch of the streaming kernel.  NVFP4
     weights encoded from seeded N(0, 0.02) draws, rotated over copies of about 300 MB in total
     (beyond the last-level cache); kernel time per product from HIP-graph replays, as in
     `decode`."""
