@@ -3,6 +3,8 @@
 One captured sequence covers both product kernels and the encoders:
 - a dynamic activation encode;
 - a two-module fused product (tiled kernel) and a decode-shaped product (M = 4, skinny kernel);
+- a decode-shaped product with K = 9216 and 4500 columns (M = 2, streaming kernel, column-pair
+  form);
 - a dynamic SiLU-mul encode;
 - an FP8 KV store into paged slots;
 - a dynamic fake quantisation.
@@ -28,7 +30,8 @@ SLOTS = 128
 
 
 def _inputs(seed):
-    shapes = [(300, 1024, 8), (4, 1024, 0), (96, 512, 0), (96, 512, 0), (64, 256, 0), (64, 256, 0)]
+    shapes = [(300, 1024, 8), (4, 1024, 0), (96, 512, 0), (96, 512, 0), (64, 256, 0), (64, 256, 0),
+              (2, 9216, 3)]
     return [to_device(random_matrix(seed + i, r, c, outlier_cols=o, dtype="bf16"), "bf16")
             for i, (r, c, o) in enumerate(shapes)]
 
@@ -43,24 +46,28 @@ def _weights():
     wc = torch.cat([p[0] for p in parts])
     ws = torch.cat([p[1] for p in parts])
     gw = torch.cat([p[2] for p in parts])
-    return wc, ws, gw
+    long_w = nv.nvfp4_quantize(
+        to_device(random_matrix(901, 4500, 9216, std=0.02, dtype="bf16"), "bf16"))
+    return wc, ws, gw, long_w
 
 
 def _sequence(ins, wts, kv):
     """The calls under test; returns every output tensor (the caches are written in place)."""
     import bit_block_scaled_nvfp4_amd as nv
 
-    a, ad, gate, up, k, v = ins
+    a, ad, gate, up, k, v, al = ins
     ks, vs, slots, key_cache, value_cache = kv
-    wc, ws, gw = wts
+    wc, ws, gw, (lc, ls, lg) = wts
     ac, as_, ga = nv.nvfp4_quantize(a)
     c = nv.fused_nvfp4_gemm(ac, as_, ga, wc, ws, gw, SEGS)
     dc, ds, dg = nv.nvfp4_quantize(ad, ga)  # decode rows under the prefill's scale
     cd = nv.nvfp4_gemm(dc, ds, dg, wc, ws, gw[:1])
+    lac, las, lag = nv.nvfp4_quantize(al)
+    cl = nv.nvfp4_gemm(lac, las, lag, lc, ls, lg)
     sc, ss, sg = nv.nvfp4_silu_mul_quantize(gate, up)
     nv.nvfp4_kv_fp8_store(k, v, ks, vs, key_cache, value_cache, slots)
     xh, fg = nv.nvfp4_fake_quantize(a)
-    return [ac, as_, ga, c, dc, ds, cd, sc, ss, sg, xh, fg]
+    return [ac, as_, ga, c, dc, ds, cd, cl, sc, ss, sg, xh, fg]
 
 
 def test_captured_sequence_replays_bitwise():
@@ -100,7 +107,7 @@ def test_captured_sequence_replays_bitwise():
         graph.replay()
         torch.cuda.synchronize()
         names = ["a codes", "a scales", "gA", "fused product", "decode codes", "decode scales",
-                 "decode product", "silu codes", "silu scales", "silu g", "fake quant", "fake g"]
+                 "decode product", "long-K decode product", "silu codes", "silu scales", "silu g", "fake quant", "fake g"]
         for name, e, g in zip(names, outs_e, outs_g):
             assert torch.equal(e, g), f"replay {rep}: {name} differs from the eager call"
         assert torch.equal(kc_e, kc_g) and torch.equal(vc_e, vc_g), f"replay {rep}: KV caches differ"
