@@ -76,8 +76,8 @@ def test_ragged_shapes(M, N, K):
                                    (2, 40, 33792), (3, 50, 65536)])
 def test_decode_long_k(M, N, K):
     # at most 16 rows and K above 8192: the streaming kernel up to K = 32768 (9 to 31 phases of
-    # 1024), beyond that the skinny kernel in 5 and 10 pieces of K that add into C; three fused
-    # modules
+    # 1024), beyond that pieces of at most 8 phases (5 at K = 33792, 8 at K = 65536) through its
+    # cached form, each later piece adding into C; three fused modules
     a = random_matrix(M * 11 + K, M, K, outlier_cols=max(1, K // 200))
     wt = random_matrix(N * 3 + K, N, K, std=0.02)
     segs = [0, N // 3, N // 2, N]
