@@ -52,6 +52,21 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
 }
 
+// wait_vmcnt with a count that loop unrolling makes constant: the switch folds to one wait (any
+// other count waits for everything, which is always safe)
+__device__ __forceinline__ void wait_vmcnt_folded(int n) {
+  switch (n) {
+    case 2: wait_vmcnt<2>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    default: wait_vmcnt<0>(); break;
+  }
+}
+
 struct StreamArgs {
   GemmArgs p;
   int ntiles;  // ceil(N / 16)
@@ -316,6 +331,25 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& p, floatx4_t (&par
   acc = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
+// The last tile of gemm_stream_cached_kernel, held in slots PAR * NPH ...: no copies are issued, and
+// the wait at step q leaves its NPH - 1 - q later units outstanding.
+template <int NPH, int PAR>
+__device__ __forceinline__ void cached_last_tile(const GemmArgs& p, uint8_t* const (&slot)[16],
+                                                 const half8_t (&act)[NPH][4],
+                                                 floatx4_t (&partial)[kWaves][64],
+                                                 const float* gtab, int tile, int wave, int lane,
+                                                 int r, int g, floatx4_t& acc) {
+#pragma unroll
+  for (int q = 0; q < NPH; ++q) {
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt_folded((NPH - 1 - q) * kVmemPerUnitCached);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    compute_weights(slot[PAR * NPH + q], act[q], wave, r, g, acc);
+    if (q == NPH - 1) tile_epilogue(p, partial, gtab, tile, wave, lane, r, g, acc);
+  }
+}
+
 template <int NPH>
 __global__ void __launch_bounds__(kThreads) gemm_stream_cached_kernel(StreamArgs s) {
   static_assert(NPH >= 1 && NPH <= 8, "K up to 8192");
@@ -339,7 +373,6 @@ __global__ void __launch_bounds__(kThreads) gemm_stream_cached_kernel(StreamArgs
   const int ksa = p.K / 16;
   const int my_tiles = (s.ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
   const int tile0 = (int)blockIdx.x, tstep = (int)gridDim.x;
-  const int last_tile = tile0 + (my_tiles - 1) * tstep;
 
 
   // (here the table is read first: issuing tile 0's copies before the activation work measured
@@ -385,28 +418,31 @@ __global__ void __launch_bounds__(kThreads) gemm_stream_cached_kernel(StreamArgs
   for (int q = 0; q < NPH; ++q) issue_weights(p, tile0, q, slot[q], wave, lane);
 
   floatx4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int i = 0; i < my_tiles; i += 2) {
+  // every tile but the last: the next tile's units are copied during this one
+  for (int i = 0; i < my_tiles - 1; i += 2) {
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
       const int ti = i + par;
+      if (ti >= my_tiles - 1) break;  // uniform over the workgroup
       const int tile = tile0 + ti * tstep;
-      // the tile whose units are copied during this one (the last tile again past the end)
-      const int tnext = ti + 1 < my_tiles ? tile + tstep : last_tile;
 #pragma unroll
       for (int q = 0; q < NPH; ++q) {
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<(NPH - 1) * kVmemPerUnitCached>();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        issue_weights(p, tnext, q, slot[(1 - par) * NPH + q], wave, lane);
-        if (ti < my_tiles) {  // uniform over the workgroup
-          compute_weights(slot[par * NPH + q], act[q], wave, r, g, acc);
-          if (q == NPH - 1) tile_epilogue(p, partial, gtab, tile, wave, lane, r, g, acc);
-        }
+        issue_weights(p, tile + tstep, q, slot[(1 - par) * NPH + q], wave, lane);
+        compute_weights(slot[par * NPH + q], act[q], wave, r, g, acc);
+        if (q == NPH - 1) tile_epilogue(p, partial, gtab, tile, wave, lane, r, g, acc);
       }
     }
   }
-  wait_vmcnt<0>();  // the copies issued past the last unit land before the LDS is released
+  // the last tile copies nothing: at its step q only its own later units are outstanding
+  const int tl = my_tiles - 1;
+  if (tl & 1)
+    cached_last_tile<NPH, 1>(p, slot, act, partial, gtab, tile0 + tl * tstep, wave, lane, r, g, acc);
+  else
+    cached_last_tile<NPH, 0>(p, slot, act, partial, gtab, tile0 + tl * tstep, wave, lane, r, g, acc);
 }
 
 // Column-pair form (K beyond the cached form, more than 16 columns per compute unit when the
