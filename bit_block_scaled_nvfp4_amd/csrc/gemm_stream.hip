@@ -522,6 +522,77 @@ __device__ __forceinline__ void compute_pair(const uint8_t* slot, const uint8_t*
   }
 }
 
+// End of a group (columns cb ..): fixed-order sums of the 8 wavefronts' partial tiles; wavefront
+// `tile` scales and stores tile `tile`.
+__device__ __forceinline__ void pair_epilogue(const GemmArgs& p,
+                                              floatx4_t (&partial)[2][kWaves][64],
+                                              const float* gtab, int cb, int cend, int wave,
+                                              int lane, int r, int g, floatx4_t (&acc)[2]) {
+  partial[0][wave][lane] = acc[0];
+  partial[1][wave][lane] = acc[1];
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  if (wave < 2) {
+    floatx4_t sum = partial[wave][0][lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) sum += partial[wave][w][lane];
+    const int n = cb + 16 * wave + r;
+    if (n < cend) {
+      const float al = 1.0f / (gtab[NVFP4_MAX_SEGMENTS] * gtab[column_segment(p.seg, n)]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 4 * g + e;
+        if (m >= p.M) continue;
+        if (p.c_accumulate)
+          reinterpret_cast<float*>(p.c)[(int64_t)m * p.ldc + n] += sum[e] * al;
+        else
+          store_c(p.c, p.c_bf16, p.ldc, m, n, sum[e] * al);
+      }
+    }
+  }
+  acc[0] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  acc[1] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+// The last REM units of gemm_stream_pair_kernel (kPairAhead <= REM < kPairAhead + kPairRing),
+// starting at unit u0 in slot 0: step j copies unit u0 + j + kPairAhead only while that unit
+// exists, and waits for unit u0 + j with the one later unit still outstanding, or none at the last.
+template <int REM>
+__device__ __forceinline__ void pair_tail(const PairArgs& s, uint8_t* const (&ring)[kPairRing],
+                                          uint4 (&aw)[kPairRing], const uint8_t* asc,
+                                          floatx4_t (&partial)[2][kWaves][64], const float* gtab,
+                                          int u0, int c0, int clast, int cend, int wave, int lane,
+                                          floatx4_t (&acc)[2]) {
+  static_assert(kPairAhead == 2 && REM >= kPairAhead && REM < kPairAhead + kPairRing,
+                "tail length");
+  const GemmArgs& p = s.p;
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < REM; ++j) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (j + 1 < REM)
+      wait_vmcnt<(kPairAhead - 1) * kVmemPerPair>();
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (j + kPairAhead < REM) {
+      const int un = u0 + j + kPairAhead;
+      const int i = un / s.nph;
+      issue_pair(s, c0 + 32 * i, clast, un - i * s.nph, ring[(j + kPairAhead) % kPairRing], wave,
+                 lane, aw[(j + kPairAhead) % kPairRing]);
+    }
+    const int u = u0 + j;
+    const int i = u / s.nph;
+    const int q = u - i * s.nph;
+    compute_pair(ring[j % kPairRing], asc, p.K / 16, q, wave, r, g, r < p.M, aw[j % kPairRing],
+                 acc);
+    if (q == s.nph - 1) pair_epilogue(p, partial, gtab, c0 + 32 * i, cend, wave, lane, r, g, acc);
+  }
+}
+
 __global__ void __launch_bounds__(kThreads) gemm_stream_pair_kernel(PairArgs s) {
   __shared__ __attribute__((aligned(16))) uint8_t q0[kPairBytes];
   __shared__ __attribute__((aligned(16))) uint8_t q1[kPairBytes];
@@ -553,19 +624,20 @@ __global__ void __launch_bounds__(kThreads) gemm_stream_pair_kernel(PairArgs s) 
     }
   }
 
-  // unit u: group u / nph (columns c0 + 32 (u / nph) ...), phase u % nph; units past the last
-  // repeat it (redundant copies, no compute)
+  // unit u: group u / nph (columns c0 + 32 (u / nph) ...), phase u % nph, in slot u % kPairRing
+  // (units >= nph > 8 > kPairAhead)
   uint4 aw[kPairRing];
 #pragma unroll
   for (int k = 0; k < kPairAhead; ++k) {
-    const int uu = k < units ? k : units - 1;
-    const int i = uu / s.nph;
-    issue_pair(s, c0 + 32 * i, clast, uu - i * s.nph, ring[k], wave, lane, aw[k]);
+    const int i = k / s.nph;
+    issue_pair(s, c0 + 32 * i, clast, k - i * s.nph, ring[k], wave, lane, aw[k]);
   }
   stage_global_scales(p, gtab);
 
   floatx4_t acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-  for (int u0 = 0; u0 < units; u0 += kPairRing) {
+  // whole rounds of kPairRing units while every unit they copy exists
+  int u0 = 0;
+  for (; u0 + kPairRing + kPairAhead <= units; u0 += kPairRing) {
 #pragma unroll
     for (int k = 0; k < kPairRing; ++k) {
       const int u = u0 + k;
@@ -575,50 +647,23 @@ __global__ void __launch_bounds__(kThreads) gemm_stream_pair_kernel(PairArgs s) 
       __builtin_amdgcn_sched_barrier(0);
       {
         const int un = u + kPairAhead;
-        const int uu = un < units ? un : units - 1;
-        const int i = uu / s.nph;
-        issue_pair(s, c0 + 32 * i, clast, uu - i * s.nph, ring[(k + kPairAhead) % kPairRing],
+        const int i = un / s.nph;
+        issue_pair(s, c0 + 32 * i, clast, un - i * s.nph, ring[(k + kPairAhead) % kPairRing],
                    wave, lane, aw[(k + kPairAhead) % kPairRing]);
       }
-      if (u < units) {  // uniform over the workgroup
-        const int i = u / s.nph;
-        const int q = u - i * s.nph;
-        compute_pair(ring[k], asc, ksa, q, wave, r, g, arow_valid, aw[k], acc);
-        if (q == s.nph - 1) {
-          // end of a group: fixed-order sums of the 8 wavefronts' partial tiles; wavefront `tile`
-          // scales and stores tile `tile`
-          partial[0][wave][lane] = acc[0];
-          partial[1][wave][lane] = acc[1];
-          __builtin_amdgcn_sched_barrier(0);
-          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
-          __builtin_amdgcn_s_barrier();
-          __builtin_amdgcn_sched_barrier(0);
-          if (wave < 2) {
-            floatx4_t sum = partial[wave][0][lane];
-#pragma unroll
-            for (int w = 1; w < kWaves; ++w) sum += partial[wave][w][lane];
-            const int n = c0 + 32 * i + 16 * wave + r;
-            if (n < cend) {
-              const float al =
-                  1.0f / (gtab[NVFP4_MAX_SEGMENTS] * gtab[column_segment(p.seg, n)]);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int m = 4 * g + e;
-                if (m >= p.M) continue;
-                if (p.c_accumulate)
-                  reinterpret_cast<float*>(p.c)[(int64_t)m * p.ldc + n] += sum[e] * al;
-                else
-                  store_c(p.c, p.c_bf16, p.ldc, m, n, sum[e] * al);
-              }
-            }
-          }
-          acc[0] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
-          acc[1] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        }
-      }
+      const int i = u / s.nph;
+      const int q = u - i * s.nph;
+      compute_pair(ring[k], asc, ksa, q, wave, r, g, arow_valid, aw[k], acc);
+      if (q == s.nph - 1)
+        pair_epilogue(p, partial, gtab, c0 + 32 * i, cend, wave, lane, r, g, acc);
     }
   }
-  wait_vmcnt<0>();
+  // the remaining kPairAhead .. kPairAhead + kPairRing - 1 units, from slot 0
+  switch (units - u0) {
+    case 2: pair_tail<2>(s, ring, aw, asc, partial, gtab, u0, c0, clast, cend, wave, lane, acc); break;
+    case 3: pair_tail<3>(s, ring, aw, asc, partial, gtab, u0, c0, clast, cend, wave, lane, acc); break;
+    default: pair_tail<4>(s, ring, aw, asc, partial, gtab, u0, c0, clast, cend, wave, lane, acc); break;
+  }
 }
 
 }  // namespace

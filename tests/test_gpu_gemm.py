@@ -94,11 +94,13 @@ def test_decode_many_columns(M, N, K):
     _check(*_encode(a, wt, segs), segs, f"many columns M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(3, 4200, 9216), (16, 8250, 10240), (1, 5120, 17408)])
+@pytest.mark.parametrize("M,N,K", [(3, 4200, 9216), (16, 8250, 10240), (1, 5120, 17408),
+                                   (2, 4500, 10240)])
 def test_decode_even_column_share(M, N, K):
     # K above 8192 and more than 16 columns per compute unit (256 of them): workgroups own equal
     # column ranges walked in groups of 32 (17 columns and a last workgroup of one; 33 columns, two
-    # groups; 20 columns, the MLP down projection's shape), three fused modules
+    # groups; 20 columns, the MLP down projection's shape; 18 columns), three fused modules.  Their
+    # 9, 20, 17 and 10 units of one group-phase end in closing runs of 3, 2, 2 and 4 units
     a = random_matrix(M * 17 + N, M, K, outlier_cols=max(1, K // 300))
     wt = random_matrix(N * 5 + K, N, K, std=0.02)
     segs = [0, N // 3 + 7, N // 2 + 1, N]
