@@ -84,10 +84,11 @@ def test_decode_long_k(M, N, K):
     _check(*_encode(a, wt, segs), segs, f"long K M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 9000, 2048), (16, 8250, 1024), (5, 12345, 3072)])
+@pytest.mark.parametrize("M,N,K", [(1, 9000, 2048), (16, 8250, 1024), (5, 12345, 3072),
+                                   (3, 8500, 4096), (16, 8250, 8192)])
 def test_decode_many_columns(M, N, K):
     # more than 32 columns per compute unit: the streaming kernel walks several 16-column tiles per
-    # workgroup (ragged last tile), two fused modules
+    # workgroup (ragged last tile), with 1 to 8 phases of K, two fused modules
     a = random_matrix(M * 13 + N, M, K, outlier_cols=3)
     wt = random_matrix(N + K, N, K, std=0.02)
     segs = [0, N // 2 + 5, N]
