@@ -15,15 +15,31 @@ SEGS = [0, 192, 512]
 
 
 def _work(seed):
-    """Inputs of one thread's sequence: activations, a fused two-module weight, gate and up."""
+    """Inputs of one thread's sequence: activations, a fused two-module weight, gate and up, and
+    two activation rows for a long-K decode product."""
     return (to_device(random_matrix(seed, 257, 1024, outlier_cols=4, dtype="bf16"), "bf16"),
             to_device(random_matrix(seed + 1, SEGS[-1], 1024, std=0.02, dtype="bf16"), "bf16"),
             to_device(random_matrix(seed + 2, 64, 768, dtype="bf16"), "bf16"),
-            to_device(random_matrix(seed + 3, 64, 768, dtype="bf16"), "bf16"))
+            to_device(random_matrix(seed + 3, 64, 768, dtype="bf16"), "bf16"),
+            to_device(random_matrix(seed + 4, 2, 9216, outlier_cols=3, dtype="bf16"), "bf16"))
 
 
-def _sequence(a, w, gate, up, reps):
-    """Dynamic encodes, the fused product and a decode-shaped product, `reps` times over."""
+_LONG = {}
+
+
+def _long_weight():
+    """One NVFP4 weight of 4500 x 9216 shared (read only) by every thread: its decode products take
+    the streaming kernel's column-pair form."""
+    import bit_block_scaled_nvfp4_amd as nv
+
+    if "w" not in _LONG:
+        _LONG["w"] = nv.nvfp4_quantize(
+            to_device(random_matrix(3999, 4500, 9216, std=0.02, dtype="bf16"), "bf16"))
+    return _LONG["w"]
+
+
+def _sequence(a, w, gate, up, al, reps):
+    """Dynamic encodes, the fused product and two decode-shaped products, `reps` times over."""
     import torch
 
     import bit_block_scaled_nvfp4_amd as nv
@@ -39,7 +55,10 @@ def _sequence(a, w, gate, up, reps):
         dc, ds, dg = nv.nvfp4_quantize(a[:3], ga)
         cd = nv.nvfp4_gemm(dc, ds, dg, wc, ws, gw[:1])
         sc, ss, sg = nv.nvfp4_silu_mul_quantize(gate, up)
-        outs.append([wc, ws, gw, ac, as_, ga, c, cd, sc, ss, sg])
+        lc, ls, lg = _LONG["w"]
+        lac, las, lag = nv.nvfp4_quantize(al)
+        cl = nv.nvfp4_gemm(lac, las, lag, lc, ls, lg)
+        outs.append([wc, ws, gw, ac, as_, ga, c, cd, sc, ss, sg, lac, las, lag, cl])
     return outs
 
 
@@ -48,6 +67,8 @@ def test_threads_on_their_own_streams_match_sequential_calls():
 
     seeds = [3100, 3200, 3300, 3400]
     inputs = [_work(s) for s in seeds]
+    _long_weight()
+    torch.cuda.synchronize()
     ref = [_sequence(*ins, reps=1)[0] for ins in inputs]
     torch.cuda.synchronize()
 
