@@ -5,6 +5,10 @@
 * Brute force on tiny shapes: each output element summed as exact rationals straight from the packed
   bytes (``oracle.element_value_exact`` indexes the bytes by hand, a separate decoding from the
   vectorised one), divided by the two global scales, several segments with distinct scales.
+* The tolerance scale ``gemm_abs_bound`` (``sum_k |a*w| / (gA gW[seg])``, the quantity every GPU
+  parity bound is a multiple of) against the same exact rationals, on operands whose bytes cover
+  every E2M1 nibble, zero and subnormal E4M3 scales and both signs, and against a hand-built case
+  where the product cancels to zero but the bound does not.
 * Closed forms: one-hot activations select one weight row, constant activations give row sums.
 * Fused-module invariants (ai.info summary, "Main Findings"): the per-segment fused product equals the
   concatenation of one product per module; the defective fused product (largest global scale applied
@@ -60,6 +64,53 @@ def test_brute_force_exact_rationals(K):
                 acc += oracle.element_value_exact(ac, as_, m, k) * oracle.element_value_exact(wc, ws, n, k)
             ref = acc / (Fraction(float(ga)) * Fraction(float(gw[j])))
             assert abs(Fraction(C[m, n]) - ref) <= abs(ref) * Fraction(1, 2 ** 51)
+
+
+def _raw_operands(seed, M, N, K):
+    """Random code and scale bytes: every nibble 0x0..0xF (both signed zeros), scale codes drawn
+    from all 127 finite E4M3 codes 0x00..0x7E (zero, the seven subnormals, 448)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    wc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    as_ = rng.integers(0, 0x7F, (M, K // 16), dtype=np.uint8)
+    ws = rng.integers(0, 0x7F, (N, K // 16), dtype=np.uint8)
+    return ac, as_, wc, ws
+
+
+@pytest.mark.parametrize("K", [16, 48])
+def test_abs_bound_against_exact_rationals(K):
+    M, N = 3, 4
+    segs = [0, 1, 4]
+    ac, as_, wc, ws = _raw_operands(60 + K, M, N, K)
+    as_[0, 0] = 0x00  # a zero block
+    ws[1, -1] = 0x01  # the smallest subnormal scale
+    ga, gw = np.float32(3.0), np.array([0.75, 5.0], np.float32)
+    B = oracle.gemm_abs_bound(ac, as_, ga, wc, ws, gw, segs)
+    C = oracle.gemm_exact(ac, as_, ga, wc, ws, gw, segs)
+    for m in range(M):
+        for n in range(N):
+            j = 0 if n < 1 else 1
+            acc, acc_abs = Fraction(0), Fraction(0)
+            for k in range(K):
+                p = oracle.element_value_exact(ac, as_, m, k) * oracle.element_value_exact(wc, ws, n, k)
+                acc += p
+                acc_abs += abs(p)
+            den = Fraction(float(ga)) * Fraction(float(gw[j]))
+            ref_b, ref_c = acc_abs / den, acc / den
+            assert abs(Fraction(B[m, n]) - ref_b) <= ref_b * Fraction(1, 2 ** 51)
+            assert abs(Fraction(C[m, n]) - ref_c) <= ref_b * Fraction(1, 2 ** 51)
+
+
+def test_abs_bound_of_a_cancelling_product():
+    # A: one row, all elements +1.0 (code 0x2, scale 0x38 = 1.0).  W: one row whose first 8
+    # elements are +1.5 and last 8 are -1.5 (codes 0x3 / 0xB, scale 0x38).  The product cancels to
+    # exactly 0 while the bound is 16 * 1.5 / (gA gW) = 24 / (2 * 0.5) = 24.
+    K = 16
+    a_codes = np.full((1, 8), 0x22, np.uint8)
+    w_codes = np.array([[0x33] * 4 + [0xBB] * 4], np.uint8)
+    sc = np.full((1, 1), 0x38, np.uint8)
+    assert oracle.gemm_exact(a_codes, sc, 2.0, w_codes, sc, [0.5]).tolist() == [[0.0]]
+    assert oracle.gemm_abs_bound(a_codes, sc, 2.0, w_codes, sc, [0.5]).tolist() == [[24.0]]
 
 
 def test_brute_force_hand_built_operands():

@@ -46,6 +46,15 @@ MUTATIONS = {
                              "C[:, lo:hi] = S[:, lo:hi].astype(np.float64) * 2.0 ** -18 / denom"),
     "e2m1_subnormal_value": ("return m * 0.5  # subnormal", "return m * 0.75  # subnormal"),
     "block_max_uses_signed_max": ("amax_b = ax.max(axis=2)", "amax_b = xb.max(axis=2)"),
+    # the per-element tolerance scale of every GPU parity test
+    "abs_bound_loosened_64x": (
+        "B[:, lo:hi] = S[:, lo:hi].astype(np.float64) * 2.0 ** -20 / (ga * np.float64(seg_g[j]))",
+        "B[:, lo:hi] = S[:, lo:hi].astype(np.float64) * 2.0 ** -14 / (ga * np.float64(seg_g[j]))"),
+    "abs_bound_without_abs": ("A = np.abs(decode_integers(a_codes, a_scales))",
+                              "A = decode_integers(a_codes, a_scales)"),
+    "abs_bound_segment_off_by_one": (
+        "/ (ga * np.float64(seg_g[j]))\n    return B",
+        "/ (ga * np.float64(seg_g[(j + 1) % len(seg_g)]))\n    return B"),
 }
 
 
@@ -86,6 +95,8 @@ def _pins():
         T_quant.test_sign_symmetry,
         T_quant.test_error_bound_half_grid_step_times_scale,
         lambda: T_gemm.test_brute_force_exact_rationals(32),
+        lambda: T_gemm.test_abs_bound_against_exact_rationals(16),
+        T_gemm.test_abs_bound_of_a_cancelling_product,
         T_gemm.test_brute_force_hand_built_operands,
         T_gemm.test_one_hot_activation_selects_a_weight_column,
         T_gemm.test_fused_equals_concatenated_per_module_products,
