@@ -135,9 +135,76 @@ def _stream(device) -> int:
 
 
 def _require_cuda(*ts):
+    devs = set()
     for t in ts:
-        if t is not None and not t.is_cuda:
-            raise ValueError("tensors must live on the GPU")
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("tensors must live on the GPU")
+            devs.add(t.device)
+    if len(devs) > 1:
+        raise ValueError("tensors must live on one GPU")
+
+
+# Shape, dtype and layout checks, made before any tensor reaches the library: the C ABI takes bare
+# pointers, so a wrongly sized or strided tensor would otherwise be read or written out of bounds.
+
+def _packed(t, rows: int, width: int, name: str):
+    """``t`` must be uint8 ``[rows, width]`` with rows packed back to back (row pitch = width)."""
+    torch = _torch()
+    if t.dtype != torch.uint8:
+        raise ValueError(f"{name} must be uint8, got {t.dtype}")
+    if t.dim() != 2 or tuple(t.shape) != (rows, width):
+        raise ValueError(f"{name} must have shape [{rows}, {width}], got {list(t.shape)}")
+    if rows > 0 and width > 0 and (t.stride(1) != 1 or (rows > 1 and t.stride(0) != width)):
+        raise ValueError(f"{name} must be row-contiguous with row pitch {width}, "
+                         f"got strides {t.stride()}")
+
+
+def _scales_f32(t, n: int, name: str):
+    """``t`` must hold at least ``n`` contiguous float32 values."""
+    torch = _torch()
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32, got {t.dtype}")
+    if t.numel() < n or (n > 1 and (t.dim() != 1 or t.stride(0) != 1)):
+        raise ValueError(f"{name} must hold {n} contiguous float32 value(s)")
+
+
+def _matrix_out(t, rows: int, cols: int, name: str, dtypes):
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if t.dim() != 2 or tuple(t.shape) != (rows, cols):
+        raise ValueError(f"{name} must have shape [{rows}, {cols}], got {list(t.shape)}")
+    if rows > 0 and cols > 0 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have contiguous rows (stride(1) == 1)")
+
+
+def _input_matrix(x, name: str):
+    torch = _torch()
+    if x.dim() != 2 or (x.numel() > 0 and x.stride(1) != 1):
+        raise ValueError(f"{name} must be 2-D with contiguous rows")
+    if x.dtype not in (torch.float32, torch.bfloat16, torch.float16):
+        raise ValueError(f"{name} must be float32, bfloat16 or float16, got {x.dtype}")
+    if x.shape[1] % 16 != 0:
+        raise ValueError(f"{name} must have a multiple of 16 columns, got {x.shape[1]}")
+
+
+def _gemm_operands(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_gscale, nseg):
+    """Check the encoded operands of a product; returns (M, N, K)."""
+    if a_codes.dim() != 2 or w_codes.dim() != 2:
+        raise ValueError("a_codes and w_codes must be 2-D")
+    M, K = a_codes.shape[0], a_codes.shape[1] * 2
+    N = w_codes.shape[0]
+    if w_codes.shape[1] * 2 != K:
+        raise ValueError("A and W disagree on K")
+    if K % 16 != 0:
+        raise ValueError(f"K = {K} is not a multiple of 16")
+    _packed(a_codes, M, K // 2, "a_codes")
+    _packed(a_scales, M, K // 16, "a_scales")
+    _packed(w_codes, N, K // 2, "w_codes")
+    _packed(w_scales, N, K // 16, "w_scales")
+    _scales_f32(a_gscale, 1, "a_gscale")
+    _scales_f32(seg_gscale, nseg, "segment global scales")
+    return M, N, K
 
 
 def nvfp4_quantize(x, global_scale=None, codes=None, scales=None):
@@ -148,14 +215,18 @@ def nvfp4_quantize(x, global_scale=None, codes=None, scales=None):
     ``(codes uint8[rows, cols/2], scales uint8[rows, cols/16], global_scale)``."""
     torch = _torch()
     lib = load_library()
-    if x.dim() != 2 or x.stride(1) != 1:
-        raise ValueError("x must be 2-D with contiguous rows")
-    _require_cuda(x)
+    _input_matrix(x, "x")
     rows, cols = x.shape
+    if global_scale is not None:
+        _scales_f32(global_scale, 1, "global_scale")
+    if codes is not None:
+        _packed(codes, rows, cols // 2, "codes")
+    if scales is not None:
+        _packed(scales, rows, cols // 16, "scales")
+    _require_cuda(x, global_scale, codes, scales)
     dynamic = global_scale is None
     if dynamic:
         global_scale = torch.empty(1, dtype=torch.float32, device=x.device)
-    _require_cuda(global_scale)
     if codes is None:
         codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
     if scales is None:
@@ -173,16 +244,21 @@ def nvfp4_silu_mul_quantize(gate, up, global_scale=None, codes=None, scales=None
     global_scale)``."""
     torch = _torch()
     lib = load_library()
-    if gate.dim() != 2 or gate.stride(1) != 1 or up.dim() != 2 or up.stride(1) != 1:
-        raise ValueError("gate and up must be 2-D with contiguous rows")
+    _input_matrix(gate, "gate")
+    _input_matrix(up, "up")
     if gate.shape != up.shape or gate.dtype != up.dtype:
         raise ValueError("gate and up must have the same shape and dtype")
-    _require_cuda(gate, up)
     rows, cols = gate.shape
+    if global_scale is not None:
+        _scales_f32(global_scale, 1, "global_scale")
+    if codes is not None:
+        _packed(codes, rows, cols // 2, "codes")
+    if scales is not None:
+        _packed(scales, rows, cols // 16, "scales")
+    _require_cuda(gate, up, global_scale, codes, scales)
     dynamic = global_scale is None
     if dynamic:
         global_scale = torch.empty(1, dtype=torch.float32, device=gate.device)
-    _require_cuda(global_scale)
     if codes is None:
         codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=gate.device)
     if scales is None:
@@ -205,11 +281,10 @@ def nvfp4_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, out_dty
     """``C = A @ W^T / (gA * gW)`` for NVFP4 ``A[M, K]`` and ``W[N, K]``."""
     torch = _torch()
     lib = load_library()
-    _require_cuda(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale)
-    M, K = a_codes.shape[0], a_codes.shape[1] * 2
-    N = w_codes.shape[0]
-    if w_codes.shape[1] * 2 != K:
-        raise ValueError("A and W disagree on K")
+    M, N, K = _gemm_operands(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, 1)
+    if out is not None:
+        _matrix_out(out, M, N, "out", (torch.float32, torch.bfloat16))
+    _require_cuda(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, out)
     if out is None:
         out = _out(M, N, out_dtype or torch.float32, a_codes.device)
     _check(lib.nvfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(a_gscale), _ptr(w_codes),
@@ -224,13 +299,14 @@ def fused_nvfp4_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_gscale,
     ``[seg_offsets[j], seg_offsets[j+1])`` are divided by ``gA * seg_gscale[j]``."""
     torch = _torch()
     lib = load_library()
-    _require_cuda(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_gscale)
-    M, K = a_codes.shape[0], a_codes.shape[1] * 2
-    N = w_codes.shape[0]
-    if w_codes.shape[1] * 2 != K:
-        raise ValueError("A and W disagree on K")
     offs = [int(o) for o in seg_offsets]
     nseg = len(offs) - 1
+    if not 1 <= nseg <= NVFP4_MAX_SEGMENTS:
+        raise ValueError(f"between 1 and {NVFP4_MAX_SEGMENTS} segments, got {nseg}")
+    M, N, K = _gemm_operands(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_gscale, nseg)
+    if out is not None:
+        _matrix_out(out, M, N, "out", (torch.float32, torch.bfloat16))
+    _require_cuda(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_gscale, out)
     arr = (ctypes.c_int64 * len(offs))(*offs)
     if out is None:
         out = _out(M, N, out_dtype or torch.float32, a_codes.device)
@@ -246,14 +322,16 @@ def nvfp4_fake_quantize(x, global_scale=None, out_dtype=None, out=None):
     :func:`nvfp4_quantize`.  Returns ``(xh, global_scale)``."""
     torch = _torch()
     lib = load_library()
-    if x.dim() != 2 or x.stride(1) != 1:
-        raise ValueError("x must be 2-D with contiguous rows")
-    _require_cuda(x)
+    _input_matrix(x, "x")
     rows, cols = x.shape
+    if global_scale is not None:
+        _scales_f32(global_scale, 1, "global_scale")
+    if out is not None:
+        _matrix_out(out, rows, cols, "out", (torch.float32, torch.bfloat16))
+    _require_cuda(x, global_scale, out)
     dynamic = global_scale is None
     if dynamic:
         global_scale = torch.empty(1, dtype=torch.float32, device=x.device)
-    _require_cuda(global_scale)
     if out is None:
         out = _out(rows, cols, out_dtype or torch.float32, x.device)
     _check(lib.nvfp4_fake_quantize(_ptr(x), _dtype_code(x.dtype), rows, cols, x.stride(0),
@@ -267,14 +345,14 @@ def nvfp4_quant_error_stats(x, global_scale=None):
     dominated int32[rows], global_scale)``."""
     torch = _torch()
     lib = load_library()
-    if x.dim() != 2 or x.stride(1) != 1:
-        raise ValueError("x must be 2-D with contiguous rows")
-    _require_cuda(x)
+    _input_matrix(x, "x")
     rows, cols = x.shape
+    if global_scale is not None:
+        _scales_f32(global_scale, 1, "global_scale")
+    _require_cuda(x, global_scale)
     dynamic = global_scale is None
     if dynamic:
         global_scale = torch.empty(1, dtype=torch.float32, device=x.device)
-    _require_cuda(global_scale)
     err2 = torch.zeros(rows, dtype=torch.float64, device=x.device)
     norm2 = torch.zeros(rows, dtype=torch.float64, device=x.device)
     dom = torch.zeros(rows, dtype=torch.int32, device=x.device)
@@ -288,8 +366,20 @@ def nvfp4_requantize(codes, scales, g_in, g_out, codes_out=None, scales_out=None
     """Re-encode NVFP4 ``(codes [rows, cols/2], scales [rows, cols/16])`` from global scale
     ``g_in`` to ``g_out`` (1-element float32 device tensors).  The outputs may be the inputs."""
     lib = load_library()
-    _require_cuda(codes, scales, g_in, g_out)
+    if codes.dim() != 2:
+        raise ValueError("codes must be 2-D")
     rows, cols = codes.shape[0], codes.shape[1] * 2
+    if cols % 16 != 0:
+        raise ValueError(f"{cols} columns is not a multiple of 16")
+    _packed(codes, rows, cols // 2, "codes")
+    _packed(scales, rows, cols // 16, "scales")
+    _scales_f32(g_in, 1, "g_in")
+    _scales_f32(g_out, 1, "g_out")
+    if codes_out is not None:
+        _packed(codes_out, rows, cols // 2, "codes_out")
+    if scales_out is not None:
+        _packed(scales_out, rows, cols // 16, "scales_out")
+    _require_cuda(codes, scales, g_in, g_out, codes_out, scales_out)
     if codes_out is None:
         codes_out = codes.new_empty(codes.shape)
     if scales_out is None:
@@ -305,9 +395,24 @@ def nvfp4_harmonize_segments(codes, scales, seg_gscale, seg_offsets, codes_out=N
     ``(codes, scales, shared_gscale)``; the outputs may be the inputs."""
     torch = _torch()
     lib = load_library()
-    _require_cuda(codes, scales, seg_gscale)
+    if codes.dim() != 2:
+        raise ValueError("codes must be 2-D")
     N, K = codes.shape[0], codes.shape[1] * 2
+    if K % 16 != 0:
+        raise ValueError(f"K = {K} is not a multiple of 16")
     offs = [int(o) for o in seg_offsets]
+    if not 1 <= len(offs) - 1 <= NVFP4_MAX_SEGMENTS:
+        raise ValueError(f"between 1 and {NVFP4_MAX_SEGMENTS} segments, got {len(offs) - 1}")
+    _packed(codes, N, K // 2, "codes")
+    _packed(scales, N, K // 16, "scales")
+    _scales_f32(seg_gscale, len(offs) - 1, "seg_gscale")
+    if codes_out is not None:
+        _packed(codes_out, N, K // 2, "codes_out")
+    if scales_out is not None:
+        _packed(scales_out, N, K // 16, "scales_out")
+    if shared_gscale is not None:
+        _scales_f32(shared_gscale, 1, "shared_gscale")
+    _require_cuda(codes, scales, seg_gscale, codes_out, scales_out, shared_gscale)
     arr = (ctypes.c_int64 * len(offs))(*offs)
     if codes_out is None:
         codes_out = codes.new_empty(codes.shape)
@@ -328,10 +433,19 @@ def nvfp4_kv_fp8_store(key, value, key_scale, value_scale, key_cache, value_cach
     ``slot_mapping[t]`` (int64 device tensor, or None for row t) of the uint8 caches
     ``[num_slots, width]`` (``value_cache`` None with ``value``).  Slots outside the cache are
     skipped."""
+    torch = _torch()
     lib = load_library()
-    if key.dim() != 2 or key.stride(1) != 1:
-        raise ValueError("key must be 2-D with contiguous rows")
+    _input_matrix(key, "key")
     tokens, width = key.shape
+    _scales_f32(key_scale, 1, "key_scale")
+    if value is not None:
+        if value_scale is None or value_cache is None:
+            raise ValueError("value needs value_scale and value_cache")
+        _scales_f32(value_scale, 1, "value_scale")
+    elif value_scale is not None or value_cache is not None:
+        raise ValueError("value_scale and value_cache come with value")
+    if key_cache.dtype != torch.uint8:
+        raise ValueError("key_cache must be uint8")
     ts = [key, key_scale, key_cache]
     if value is not None:
         if value.shape != key.shape or value.dtype != key.dtype or value.stride(1) != 1:
@@ -360,10 +474,15 @@ def nvfp4_kv_fp8_load(cache, scale, slot_mapping=None, out_dtype=None, width=Non
     float32 or bfloat16.  Slots outside the cache give rows of zeros."""
     torch = _torch()
     lib = load_library()
-    if cache.dim() != 2 or cache.stride(1) != 1:
-        raise ValueError("cache must be 2-D with contiguous rows")
+    if cache.dim() != 2 or cache.stride(1) != 1 or cache.dtype != torch.uint8:
+        raise ValueError("cache must be 2-D uint8 with contiguous rows")
     width = cache.shape[1] if width is None else int(width)
+    if not 0 <= width <= cache.shape[1]:
+        raise ValueError(f"width {width} exceeds the cache row of {cache.shape[1]}")
+    _scales_f32(scale, 1, "scale")
     tokens = cache.shape[0] if slot_mapping is None else slot_mapping.numel()
+    if out is not None:
+        _matrix_out(out, tokens, width, "out", (torch.float32, torch.bfloat16))
     ts = [cache, scale]
     if slot_mapping is not None:
         ts.append(slot_mapping)

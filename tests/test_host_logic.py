@@ -113,3 +113,77 @@ def test_binding_checks_shapes_before_calling_the_library():
     with pytest.raises(ValueError):
         nv.nvfp4_kv_fp8_store(torch.zeros(4, 32), None, torch.ones(1), None, torch.zeros(4, 32,
                               dtype=torch.uint8), None)
+
+
+def test_binding_rejects_malformed_operands_before_the_device_check():
+    """Every shape, dtype and layout check of the binding fires on CPU tensors, before the device
+    check: a wrongly sized or strided operand never reaches the library, which takes bare pointers
+    and would read or write out of bounds."""
+    torch = pytest.importorskip("torch")
+    import bit_block_scaled_nvfp4_amd as nv
+
+    if not os.path.exists(nv.LIB_PATH):
+        pytest.skip("libnvfp4.so not built")
+    u8, f32 = torch.uint8, torch.float32
+    M, N, K = 4, 24, 64
+    ac, as_ = torch.zeros(M, K // 2, dtype=u8), torch.zeros(M, K // 16, dtype=u8)
+    wc, ws = torch.zeros(N, K // 2, dtype=u8), torch.zeros(N, K // 16, dtype=u8)
+    g1, g2 = torch.ones(1), torch.ones(2)
+
+    def gemm_raises(match, **kw):
+        a = dict(a_codes=ac, a_scales=as_, a_gscale=g1, w_codes=wc, w_scales=ws, w_gscale=g1)
+        a.update(kw)
+        with pytest.raises(ValueError, match=match):
+            nv.nvfp4_gemm(**a)
+
+    gemm_raises("a_scales must have shape", a_scales=torch.zeros(M, K // 16 + 1, dtype=u8))
+    gemm_raises("w_scales must have shape", w_scales=torch.zeros(N - 1, K // 16, dtype=u8))
+    gemm_raises("w_codes must be uint8", w_codes=torch.zeros(N, K // 2, dtype=torch.int8))
+    gemm_raises("a_codes must be row-contiguous",
+                a_codes=torch.zeros(M, K, dtype=u8)[:, : K // 2])
+    gemm_raises("disagree on K", w_codes=torch.zeros(N, K // 2 + 8, dtype=u8))
+    gemm_raises("multiple of 16", a_codes=torch.zeros(M, 36, dtype=u8),
+                w_codes=torch.zeros(N, 36, dtype=u8))
+    gemm_raises("a_gscale must be float32", a_gscale=torch.ones(1, dtype=torch.float64))
+    gemm_raises("out must have shape", out=torch.zeros(M, N + 1))
+    gemm_raises("out must have dtype", out=torch.zeros(M, N, dtype=torch.float16))
+    gemm_raises("out must have contiguous rows", out=torch.zeros(N, M).t())
+    gemm_raises("tensors must live on the GPU")  # well formed, but on the host
+
+    def fused_raises(match, segs=(0, 8, N), seg_g=g2, **kw):
+        with pytest.raises(ValueError, match=match):
+            nv.fused_nvfp4_gemm(ac, as_, g1, wc, ws, seg_g, list(segs), **kw)
+
+    fused_raises("segment global scales must hold 3", segs=(0, 8, 16, N))
+    fused_raises("segment global scales must hold 2", seg_g=torch.ones(4)[::2])
+    fused_raises("between 1 and 16 segments", segs=tuple(range(0, 18)) + (N,), seg_g=torch.ones(18))
+    fused_raises("tensors must live on the GPU")
+
+    x = torch.zeros(M, K)
+    with pytest.raises(ValueError, match="codes must have shape"):
+        nv.nvfp4_quantize(x, g1, torch.zeros(M, K // 2 - 1, dtype=u8))
+    with pytest.raises(ValueError, match="scales must be row-contiguous"):
+        nv.nvfp4_quantize(x, g1, torch.zeros(M, K // 2, dtype=u8),
+                          torch.zeros(M, K // 8, dtype=u8)[:, ::2])
+    with pytest.raises(ValueError, match="multiple of 16 columns"):
+        nv.nvfp4_quantize(torch.zeros(M, 40))
+    with pytest.raises(ValueError, match="x must be float32, bfloat16 or float16"):
+        nv.nvfp4_quantize(torch.zeros(M, K, dtype=torch.float64))
+    with pytest.raises(ValueError, match="global_scale must be float32"):
+        nv.nvfp4_quantize(x, torch.ones(1, dtype=torch.float16))
+    with pytest.raises(ValueError, match="codes must have shape"):
+        nv.nvfp4_silu_mul_quantize(x, x, g1, torch.zeros(M + 1, K // 2, dtype=u8))
+    with pytest.raises(ValueError, match="out must have shape"):
+        nv.nvfp4_fake_quantize(x, g1, out=torch.zeros(M, K - 16))
+    with pytest.raises(ValueError, match="scales must have shape"):
+        nv.nvfp4_requantize(ac, torch.zeros(M, K // 32, dtype=u8), g1, g1)
+    with pytest.raises(ValueError, match="codes_out must have shape"):
+        nv.nvfp4_requantize(ac, as_, g1, g1, codes_out=torch.zeros(M, K // 4, dtype=u8))
+    with pytest.raises(ValueError, match="seg_gscale must hold 2"):
+        nv.nvfp4_harmonize_segments(wc, ws, g1, [0, 8, N])
+    with pytest.raises(ValueError, match="cache must be 2-D uint8"):
+        nv.nvfp4_kv_fp8_load(torch.zeros(8, 32), g1)
+    with pytest.raises(ValueError, match="exceeds the cache row"):
+        nv.nvfp4_kv_fp8_load(torch.zeros(8, 32, dtype=u8), g1, width=48)
+    with pytest.raises(ValueError, match="value needs value_scale"):
+        nv.nvfp4_kv_fp8_store(x, x, g1, None, torch.zeros(8, K, dtype=u8), None)
