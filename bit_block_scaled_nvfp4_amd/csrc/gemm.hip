@@ -567,6 +567,10 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
     v += gridDim.x;
     const bool more = v < ntiles;
     if (more) {
+      // With an odd number of chunks the last one was read from s0 after the last barrier; every
+      // wavefront must be past those reads before any copies of the next tile land in s0.  (With
+      // an even number, the last chunk's own barrier already orders them.)
+      if (nchunks & 1) __builtin_amdgcn_s_barrier();
       tile_coords(v, tiles_m, tiles_n, tmi, tni);
       m0 = (int)tmi * Cfg::BM;
       n0 = (int)tni * Cfg::BN;

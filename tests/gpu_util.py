@@ -82,3 +82,23 @@ def check_gemm(C_gpu: np.ndarray, C_ref: np.ndarray, B_ref: np.ndarray, what: st
     else:
         assert np.all(C_gpu == 0)
     return float(np.max(err / np.maximum(B_ref, 1e-300))) if err.size else 0.0
+
+
+def oracle_product(ac, as_, ga, wc, ws, seg_g, segs, threads: int = 16):
+    """The oracle's exact product and its tolerance scale, ``(gemm_exact, gemm_abs_bound)``, formed
+    over blocks of rows in a thread pool (NumPy's int64 matmul runs on one core but releases the
+    interpreter lock); each block is exactly the oracle's own call on those rows."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    M = ac.shape[0]
+    step = max(1, -(-M // threads))
+    blocks = [(r, min(M, r + step)) for r in range(0, M, step)]
+
+    def run(b):
+        lo, hi = b
+        return (oracle.gemm_exact(ac[lo:hi], as_[lo:hi], ga, wc, ws, seg_g, segs),
+                oracle.gemm_abs_bound(ac[lo:hi], as_[lo:hi], ga, wc, ws, seg_g, segs))
+
+    with ThreadPoolExecutor(max_workers=min(threads, len(blocks))) as ex:
+        parts = list(ex.map(run, blocks))
+    return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])

@@ -12,7 +12,7 @@ import pytest
 import oracle
 from workloads import WORKLOADS, activations, gate_up, random_matrix, weights
 
-from .gpu_util import DEV, check_gemm, log, scalar
+from .gpu_util import DEV, check_gemm, log, oracle_product, scalar
 
 pytestmark = pytest.mark.gpu
 
@@ -319,14 +319,24 @@ def _sampled_full_size(wid, M=None):
     C = nv.fused_nvfp4_gemm(ac_d, as_d, scalar(ga), wc_d, ws_d, _up(gw), segs)
     torch.cuda.synchronize()
 
+    # stratified sample: one random row in every band of 256 rows and one random column in every
+    # band of 256 columns (so every 256 x 256 output tile holds a checked element), the first and
+    # last row and column of the matrix and of every segment, and 30 rows / 40 columns per segment
+    # more at random
     rng = np.random.Generator(np.random.PCG64(100 + wid))
-    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(30, M), replace=False)]))
-    cols = [0, w.N - 1]
+
+    def bands(n):
+        return [int(rng.integers(lo, min(n, lo + 256))) for lo in range(0, n, 256)]
+
+    rows = np.unique(np.concatenate([[0, M - 1], bands(M),
+                                     rng.choice(M, min(30, M), replace=False)]))
+    cols = [0, w.N - 1] + bands(w.N)
     for j in range(len(segs) - 1):
         cols += [segs[j], segs[j + 1] - 1]
         cols += list(rng.choice(np.arange(segs[j], segs[j + 1]), min(40, segs[j + 1] - segs[j]),
                                 replace=False))
     cols = np.unique(np.array(cols))
+    assert len(np.unique(rows // 256)) == -(-M // 256) and len(np.unique(cols // 256)) == -(-w.N // 256)
     log(f"workload {wid}: oracle on {len(rows)} rows x {len(cols)} cols")
     ac, as_ = encode_rows(rows)
     assert np.array_equal(ac, ac_d[rows].cpu().numpy()) and np.array_equal(as_, as_d[rows].cpu().numpy())
@@ -339,8 +349,7 @@ def _sampled_full_size(wid, M=None):
     assert np.array_equal(wc, wc_d[cols].cpu().numpy()) and np.array_equal(ws, ws_d[cols].cpu().numpy())
     # per-column global scales: treat each sampled column as its own one-column segment
     one = list(range(len(cols) + 1))
-    R = oracle.gemm_exact(ac, as_, ga, wc, ws, gw[seg_of], one)
-    B = oracle.gemm_abs_bound(ac, as_, ga, wc, ws, gw[seg_of], one)
+    R, B = oracle_product(ac, as_, ga, wc, ws, gw[seg_of], one)
     got = C[torch.from_numpy(rows).to(DEV)][:, torch.from_numpy(cols).to(DEV)].cpu().numpy()
     worst = check_gemm(got, R, B, f"workload {wid}")
     log(f"workload {wid}: worst err / sum|ab| = {worst:.2e}")

@@ -1,0 +1,149 @@
+"""GPU parity of the W4A4 product on operand bytes no encoder would produce for smooth data, on
+every kernel the dispatch can choose, and on mid-size problems compared in full.
+
+* Raw bytes (``workloads.random_nvfp4_bytes``): every E2M1 nibble including the signed zero 0x8,
+  block scales drawn from all 127 finite E4M3 codes (zero, the seven subnormals 0x01..0x07, every
+  normal up to 0x7E = 448), all-zero blocks made by zero codes and by a zero scale.  Each product
+  kernel decodes block scales its own way (a hardware fp8 conversion in the tiled, one-pass decode
+  and streaming kernels, a bit-level decode in the general one), so each is driven over the whole
+  scale range: general (K % 64 != 0), tiled (odd and even numbers of 64-element K chunks), the
+  one-pass decode kernel with one and two 16-column tiles per workgroup, the streaming kernel's
+  cached, ring and column-pair forms, and K split into pieces that add into C.
+* Mid-size problems compared element by element over the whole output: more tiles than compute
+  units with a tile count that is not a multiple of 8 (the persistent kernel's plain tile order),
+  partial edge tiles, and an odd number of K chunks (the last chunk of a tile read from the first
+  LDS stage while the next tile's first copies are issued).
+
+Tolerance as everywhere (stated for FP32 accumulation of exact products): per element
+``|C_gpu - C_ref| <= 1e-4 * sum_k |a*w| / (gA gW[seg])``, relative Frobenius error <= 1e-5.  The
+reference is the oracle's exact int64 product of the same bytes (ai.info summary, "Methodology in
+Plain English": an E4M3 scale per 16-element block of E2M1 values)."""
+
+import numpy as np
+import pytest
+
+from workloads import random_matrix, random_nvfp4_bytes
+
+import oracle
+
+from .gpu_util import DEV, check_gemm, log, oracle_product, scalar
+
+pytestmark = pytest.mark.gpu
+
+
+def _up(arr):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(DEV)
+
+
+def _run(ac, as_, ga, wc, ws, gw, segs, what):
+    import torch
+
+    import bit_block_scaled_nvfp4_amd as nv
+
+    log(f"{what}: M={ac.shape[0]} N={wc.shape[0]} K={ac.shape[1] * 2}")
+    C = nv.fused_nvfp4_gemm(_up(ac), _up(as_), scalar(ga), _up(wc), _up(ws),
+                            _up(np.asarray(gw, np.float32)), segs)
+    torch.cuda.synchronize()
+    C = C.cpu().numpy()
+    R, B = oracle_product(ac, as_, ga, wc, ws, gw, segs)
+    worst = check_gemm(C, R, B, what)
+    log(f"{what}: worst err / sum|ab| = {worst:.2e}")
+    return C, R
+
+
+# (M, N, K, kernel the dispatch picks)
+RAW_SHAPES = [
+    (40, 300, 2064, "general"),
+    (33, 65, 48, "general, K = 48"),
+    (300, 260, 256, "tiled, 4 K chunks"),
+    (257, 513, 320, "tiled, 5 K chunks (odd)"),
+    (17, 1000, 2048, "tiled, 17 rows"),
+    (1, 3000, 2048, "one-pass decode, one tile per workgroup"),
+    (16, 6000, 2048, "one-pass decode, two tiles per workgroup"),
+    (3, 8100, 8192, "one-pass decode, K = 8192"),
+    (4, 9000, 2048, "streaming, cached form"),
+    (2, 1000, 9216, "streaming, ring form"),
+    (3, 4500, 10240, "streaming, column-pair form"),
+    (2, 40, 33792, "K pieces adding into C"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,path", RAW_SHAPES)
+def test_raw_bytes_every_scale_code(M, N, K, path):
+    ac, as_ = random_nvfp4_bytes(1000 + M + K, M, K)
+    wc, ws = random_nvfp4_bytes(2000 + N + K, N, K)
+    # every nibble appears in both operands, and every scale code too (the smallest shape, with
+    # three blocks per row, holds only some of them)
+    for c, s in ((ac, as_), (wc, ws)):
+        assert len(np.unique(np.concatenate([c & 15, c >> 4]))) == 16
+        assert K == 48 or len(np.unique(s)) == 0x7F
+    segs = [0, N // 3, N] if N >= 3 else [0, N]
+    gw = np.array([1.7, 0.03125][: len(segs) - 1], np.float32)
+    _run(ac, as_, np.float32(2.5), wc, ws, gw, segs, f"raw bytes, {path}")
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 260, 256), (1, 3000, 1024), (4, 9000, 2048),
+                                   (3, 4500, 10240), (40, 70, 80)])
+def test_zero_operands_give_zero(M, N, K):
+    """All-zero activations (zero scales) against random weights, and the signed-zero code 0x8
+    everywhere under the largest scale: every output is exactly +0 or -0 equal to 0."""
+    import torch
+
+    import bit_block_scaled_nvfp4_amd as nv
+
+    wc, ws = random_nvfp4_bytes(3000 + N, N, K)
+    for codes, scale in ((0x00, 0x00), (0x88, 0x7E)):
+        ac = np.full((M, K // 2), codes, np.uint8)
+        as_ = np.full((M, K // 16), scale, np.uint8)
+        C = nv.nvfp4_gemm(_up(ac), _up(as_), scalar(1.0), _up(wc), _up(ws), scalar(3.0))
+        torch.cuda.synchronize()
+        assert np.all(C.cpu().numpy() == 0.0)
+
+
+def test_small_scales_under_a_static_activation_scale():
+    """Activations with quiet tokens: rows scaled by 1e-2, 2e-3, 5e-4 and 1e-6, and exact zero rows,
+    encoded by the oracle under a static scale calibrated on the loud rows, so low and subnormal
+    E4M3 block scales (codes 0x01..0x07) and underflowed (zero) blocks appear, as in zero-padded or
+    quiet tokens of real prefill batches."""
+    M, N, K = 96, 384, 1024
+    a = random_matrix(77, M, K, outlier_cols=4, outlier_gain=100.0)
+    for i, f in enumerate((1e-2, 2e-3, 5e-4, 1e-6)):
+        a[1 + i::5] *= np.float32(f)
+    a[2::11] = 0.0
+    a[5, :16] = -0.0
+    ga = oracle.dynamic_global_scale(a[0::5])
+    ac, as_, _ = oracle.quantize(a, ga)
+    assert (as_ == 0).mean() > 0.1 and ((as_ > 0) & (as_ < 8)).mean() > 0.1
+    assert set(range(8)) <= set(np.unique(as_).tolist())
+    wt = random_matrix(78, N, K, std=0.02)
+    wc, ws, gw = oracle.quantize_segments(wt, [0, N])
+    _run(ac, as_, ga, wc, ws, gw, [0, N], "quiet tokens, tiled")
+    for m in (1, 16):  # the same rows through the decode-shaped kernels
+        _run(ac[:m], as_[:m], ga, wc, ws, gw, [0, N], f"quiet tokens, {m} rows")
+
+
+@pytest.mark.parametrize("M,N,K,what", [
+    (2304, 8485, 128, "306 tiles (not a multiple of 8), partial last tile column"),
+    (2304, 7936, 192, "279 tiles, 3 K chunks per tile (odd)"),
+    (1100, 16400, 320, "325 tiles, 5 K chunks, partial last tile row"),
+])
+def test_mid_size_full_output(M, N, K, what):
+    """Every output element of problems with more tiles than compute units, so each persistent
+    workgroup runs several tiles back to back (plain tile order, since the tile count is not a
+    multiple of 8), compared with the oracle."""
+    a = random_matrix(90 + K, M, K, outlier_cols=3)
+    wt = random_matrix(91 + K, N, K, std=0.02)
+    segs = [0, N // 2 + 3, N]
+    ac, as_, ga = oracle.quantize(a)
+    wc, ws, gw = oracle.quantize_segments(wt, segs)
+    _run(ac, as_, ga, wc, ws, gw, segs, f"full output, {what}")
+
+
+def test_mid_size_raw_bytes_full_output():
+    M, N, K = 2304, 7936, 192
+    ac, as_ = random_nvfp4_bytes(5, M, K)
+    wc, ws = random_nvfp4_bytes(6, N, K)
+    _run(ac, as_, np.float32(0.75), wc, ws, np.array([3.0], np.float32), [0, N],
+         "raw bytes, full output, 279 tiles, odd K chunks")

@@ -71,22 +71,20 @@ def test_bf16_inputs_are_exact_bf16_values():
 def test_traffic_summary_is_used_only_while_the_kernel_sources_match(tmp_path, monkeypatch):
     import bench
 
-    val = bench.traffic_from_profile(bench.TILED_SOURCES, bench.TILED_TRAFFIC)
-    assert val is not None and val > 1e9
-    # a summary whose hash does not match the sources is ignored
-    fake = tmp_path / "profiles"
-    fake.mkdir()
-    with open(os.path.join(ROOT, "profiles", bench.TILED_TRAFFIC)) as fh:
-        text = fh.read()
     h = hashlib.sha256()
     for f in bench.TILED_SOURCES:
         with open(os.path.join(ROOT, "bit_block_scaled_nvfp4_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
-    assert h.hexdigest() in text
-    (fake / bench.TILED_TRAFFIC).write_text(text.replace(h.hexdigest(), "0" * 64))
-    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    fake = tmp_path / "profiles"
+    fake.mkdir()
     # sources are read relative to ROOT: link them in so only the summary differs
     (tmp_path / "bit_block_scaled_nvfp4_amd").symlink_to(os.path.join(ROOT, "bit_block_scaled_nvfp4_amd"))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    body = "# summary\ncommand: x\ntraffic_bytes_per_launch: 2446000000\nkernel_source_sha256: {}\n"
+    (fake / bench.TILED_TRAFFIC).write_text(body.format(h.hexdigest()))
+    assert bench.traffic_from_profile(bench.TILED_SOURCES, bench.TILED_TRAFFIC) == 2446000000.0
+    # a summary whose hash does not match the sources is ignored
+    (fake / bench.TILED_TRAFFIC).write_text(body.format("0" * 64))
     assert bench.traffic_from_profile(bench.TILED_SOURCES, bench.TILED_TRAFFIC) is None
     assert bench.traffic_from_profile(bench.TILED_SOURCES, "missing.txt") is None
 

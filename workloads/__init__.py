@@ -12,6 +12,7 @@ from .synthetic import (  # noqa: F401
     kv_tokens,
     outlier_channels,
     random_matrix,
+    random_nvfp4_bytes,
     round_bf16,
     weights,
 )

@@ -266,3 +266,29 @@ def kv_slot_mapping(w: KvWorkload, tokens: int | None = None) -> np.ndarray:
     table = _rng(w.wid, 2).permutation(w.num_blocks)[:nblk].astype(np.int64)
     t = np.arange(tokens, dtype=np.int64)
     return table[t // w.block_size] * w.block_size + t % w.block_size
+
+
+def random_nvfp4_bytes(seed: int, rows: int, cols: int, zero_block_frac: float = 0.05):
+    """Random encoded operand bytes, not produced by any encoder: ``codes [rows, cols/2]`` uint8
+    with every nibble 0x0..0xF equally likely (0x8 is the signed zero), and ``scales
+    [rows, cols/16]`` uint8 drawn uniformly from the 127 finite non-negative E4M3 codes 0x00..0x7E
+    (zero, the seven subnormals and every normal value up to 448).  A ``zero_block_frac`` share of
+    blocks is then made all zero: half of them by zero codes under a random scale (mixing 0x0 and
+    0x8), half by a zero scale under random codes.  The first row holds every scale code in turn
+    (none of its blocks is zeroed)."""
+    if cols % 16 != 0:
+        raise ValueError("cols must be a multiple of 16")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    codes = rng.integers(0, 256, (rows, cols // 2), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, (rows, cols // 16), dtype=np.uint8)
+    nb = cols // 16
+    if rows > 0:
+        scales[0] = np.arange(nb) % 0x7F
+    pick = rng.random((rows, nb)) < zero_block_frac
+    pick[:1] = False
+    by_codes = pick & (rng.random((rows, nb)) < 0.5)
+    by_scale = pick & ~by_codes
+    zc = rng.choice(np.array([0x00, 0x08, 0x80, 0x88], np.uint8), size=(rows, cols // 2))
+    codes = np.where(np.repeat(by_codes, 8, axis=1), zc, codes)
+    scales = np.where(by_scale, np.uint8(0), scales)
+    return np.ascontiguousarray(codes, np.uint8), np.ascontiguousarray(scales, np.uint8)
