@@ -34,97 +34,124 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def prefill(args, torch, nv, W):
-    import numpy as np
-
-    w = W.WORKLOADS[3]
-    dev = "cuda:0"
-    log(f"[bench] generating {w.name}")
-    a = W.activations(w)
-    g_a = np.float32(2688.0 / np.abs(a).max())  # calibration stand-in: static scale from amax
-    ad = torch.from_numpy(a).to(torch.bfloat16).to(dev)
-    del a
+def _encode_weights(torch, nv, W, w, dev):
+    """Offline step: encode each calibrated module of the weight with its own dynamic scale."""
     segs = w.seg_offsets
     wc = torch.empty((w.N, w.K // 2), dtype=torch.uint8, device=dev)
     ws = torch.empty((w.N, w.K // 16), dtype=torch.uint8, device=dev)
     gw = torch.empty(len(segs) - 1, dtype=torch.float32, device=dev)
     for j in range(len(segs) - 1):
-        wj = W.weights(w, slice(segs[j], segs[j + 1]))
-        wd = torch.from_numpy(wj).to(torch.bfloat16).to(dev)
+        wd = W.device_weights(w, dev, slice(segs[j], segs[j + 1]))
         _, _, g = nv.nvfp4_quantize(wd, None, wc[segs[j]:segs[j + 1]], ws[segs[j]:segs[j + 1]])
         gw[j:j + 1].copy_(g)
-        del wd, wj
-    ga = torch.tensor([g_a], dtype=torch.float32, device=dev)
+        del wd
+    return wc, ws, gw
+
+
+def prefill(args, torch, nv, W, wid=3):
+    """One prefill-shaped linear layer: the activation encode (or, for the down projection, the
+    fused SiLU(g) * u encode) with the static calibrated scale, then the fused product with the
+    per-module epilogue, f32 output.  Times: the whole step (`steps` steps between events), the
+    product alone (events around each launch, on its stream), and for the headline shape the encode
+    alone over rotating inputs and the vendor bf16 GEMM of the same shape."""
+    w = W.WORKLOADS[wid]
+    dev = "cuda:0"
+    log(f"[bench] prefill {w.name}: drawing inputs on the device")
+    wc, ws, gw = _encode_weights(torch, nv, W, w, dev)
+    segs = w.seg_offsets
     ac = torch.empty((w.M, w.K // 2), dtype=torch.uint8, device=dev)
     as_ = torch.empty((w.M, w.K // 16), dtype=torch.uint8, device=dev)
     C = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+    if w.silu_mul:
+        gd, ud = W.device_gate_up(w, dev)
+        _, _, ga = nv.nvfp4_silu_mul_quantize(gd, ud, None, ac, as_)  # calibration stand-in
+
+        def encode():
+            nv.nvfp4_silu_mul_quantize(gd, ud, ga, ac, as_)
+    else:
+        ad = W.device_activations(w, dev)
+        # calibration stand-in: the static scale 2688 / amax of this batch
+        ga = torch.tensor([2688.0], device=dev) / ad.float().abs().max().reshape(1)
+
+        def encode():
+            nv.nvfp4_quantize(ad, ga, ac, as_)
     torch.cuda.synchronize()
 
-    def step():
-        nv.nvfp4_quantize(ad, ga, ac, as_)
+    def product():
         nv.fused_nvfp4_gemm(ac, as_, ga, wc, ws, gw, segs, out=C)
+
+    def step():
+        encode()
+        product()
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
-        step()
-    end.record()
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / args.steps
-
-    # per-kernel durations, events on the launch stream: the product around each launch (it runs
-    # for milliseconds); the encode around `steps` launches back to back (it runs for tens of
-    # microseconds, so single-launch events would mostly time the launch)
+    ms_step = _timed(torch, args.steps, lambda i: step())
+    # the product alone: events around each launch (it runs for milliseconds)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
     for i in range(args.steps):
-        nv.nvfp4_quantize(ad, ga, ac, as_)
+        encode()
         evs[2 * i].record()
-        nv.fused_nvfp4_gemm(ac, as_, ga, wc, ws, gw, segs, out=C)
+        product()
         evs[2 * i + 1].record()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(args.steps):
-        nv.nvfp4_quantize(ad, ga, ac, as_)
-    e1.record()
     torch.cuda.synchronize()
     g_ms = sum(evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(args.steps)) / args.steps
-    q_ms = e0.elapsed_time(e1) / args.steps
-    # the same encode with the dynamic scale: clearing the max cell, the max pass over A, the encode
-    # and the scale's finalisation (A is read twice), `steps` calls back to back between events
-    e0.record()
-    for i in range(args.steps):
-        nv.nvfp4_quantize(ad, None, ac, as_)
-    e1.record()
+    res = dict(w=w, ms_step=ms_step, gemm_ms=g_ms, flops=w.flops)
+    if wid != 3:
+        return res
+
+    # the encode alone, `steps` launches back to back over 4 rotating input/output sets (430 MB,
+    # beyond the 256 MB last-level cache), static and dynamic scale
+    R = 4
+    sets = [(W.device_activations(w, dev) if i else ad, torch.empty_like(ac), torch.empty_like(as_))
+            for i in range(R)]
+    for i in range(R):
+        nv.nvfp4_quantize(sets[i][0], ga, sets[i][1], sets[i][2])
     torch.cuda.synchronize()
-    qd_ms = e0.elapsed_time(e1) / args.steps
-    nv.nvfp4_quantize(ad, ga, ac, as_)  # back to the static-scale codes the product is timed on
-    flops = w.flops
-    q_bytes = w.M * w.K * (2 + 9 / 16)
-    qd_bytes = w.M * w.K * (2 + 2 + 9 / 16)
+    q_ms = _timed(torch, args.steps, lambda i: nv.nvfp4_quantize(sets[i % R][0], ga, sets[i % R][1],
+                                                                 sets[i % R][2]))
+    # the dynamic scale: clearing the max cell, the max pass over A, the encode and the scale's
+    # finalisation (A is read twice)
+    qd_ms = _timed(torch, args.steps, lambda i: nv.nvfp4_quantize(sets[i % R][0], None, sets[i % R][1],
+                                                                  sets[i % R][2]))
+    del sets
+    res.update(quant_ms=q_ms, q_bytes=w.M * w.K * (2 + 9 / 16), quant_dyn_ms=qd_ms,
+               qd_bytes=w.M * w.K * (2 + 2 + 9 / 16), quant_sets=R)
     # the vendor dense bf16 GEMM of the same shape (torch.matmul -> hipBLASLt), timed in turns with
     # the NVFP4 product so both see the same clock and temperature
+    nv.nvfp4_quantize(ad, ga, ac, as_)
     wb = torch.randn(w.N, w.K, device=dev, dtype=torch.bfloat16)
     for _ in range(2):
         ad @ wb.t()
     torch.cuda.synchronize()
     ours, vend = [], []
     for _ in range(3):
-        ours.append(_timed(torch, args.steps,
-                           lambda i: nv.fused_nvfp4_gemm(ac, as_, ga, wc, ws, gw, segs, out=C)))
+        ours.append(_timed(torch, args.steps, lambda i: product()))
         vend.append(_timed(torch, args.steps, lambda i: ad @ wb.t()))
     del wb
     torch.cuda.empty_cache()
-    vendor = {"ms": round(min(vend), 4), "TFLOP/s": round(flops / min(vend) / 1e9, 1),
-              "frac_of_peak": round(flops / min(vend) / 1e9 / MFMA_F16_PEAK_TFLOPS, 4),
-              "nvfp4_product_ms_same_turns": round(min(ours), 4),
-              "nvfp4_product_over_vendor": round(min(vend) / min(ours), 4)}
-    return dict(w=w, ms_step=ms_step, gemm_ms=g_ms, quant_ms=q_ms, flops=flops, q_bytes=q_bytes,
-                quant_dyn_ms=qd_ms, qd_bytes=qd_bytes, vendor=vendor)
+    flops = w.flops
+    res["vendor"] = {"ms": round(min(vend), 4), "TFLOP/s": round(flops / min(vend) / 1e9, 1),
+                     "frac_of_peak": round(flops / min(vend) / 1e9 / MFMA_F16_PEAK_TFLOPS, 4),
+                     "nvfp4_product_ms_same_turns": round(min(ours), 4),
+                     "nvfp4_product_over_vendor": round(min(vend) / min(ours), 4)}
+    return res
+
+
+def prefill_summary(p):
+    """Sub-object of the JSON line for one prefill shape."""
+    w = p["w"]
+    prod = p["flops"] / (p["gemm_ms"] * 1e-3) / 1e12
+    stp = p["flops"] / (p["ms_step"] * 1e-3) / 1e12
+    return {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "segments": list(w.seg_sizes),
+            "encode": "fused SiLU(g)*u -> NVFP4" if w.silu_mul else "NVFP4 (static scale)",
+            "step_ms": round(p["ms_step"], 4), "step_TFLOP/s": round(stp, 1),
+            "product_ms": round(p["gemm_ms"], 4), "product_TFLOP/s": round(prod, 1),
+            "frac": round(prod / MFMA_F16_PEAK_TFLOPS, 4), "bound": "mfma",
+            "peak": MFMA_F16_PEAK_TFLOPS}
 
 
 def decode(args, torch, nv, W):
@@ -190,7 +217,41 @@ def decode(args, torch, nv, W):
         res[f"M{M}"] = {"kernel_us": round(k_ms * 1e3, 3), "call_us": round(call_ms * 1e3, 3),
                         "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
                         "bytes": nbytes}
+    res["copy_ceiling"] = _copy_ceiling(torch, copies, R)
     return res
+
+
+def _copy_ceiling(torch, copies, R):
+    """The measured ceiling for streaming one decode weight: the vendor device copy of the same
+    14.75 MB (codes and scales of one 5120 x 5120 weight) from each of the R rotated copies into one
+    destination, replayed back to back from a HIP graph, total / R.  A copy reads and writes the
+    bytes; the decode product reads them once."""
+    dst_c = torch.empty_like(copies[0][0])
+    dst_s = torch.empty_like(copies[0][1])
+    for wc, ws in copies:
+        dst_c.copy_(wc)
+        dst_s.copy_(ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for wc, ws in copies:
+            dst_c.copy_(wc)
+            dst_s.copy_(ws)
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * R)
+    del graph
+    nbytes = copies[0][0].numel() + copies[0][1].numel()
+    return {"us_per_weight": round(ms * 1e3, 3), "bytes_read": nbytes,
+            "read_GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "note": "vendor device copy of one weight's codes and scales (two copies per weight)"}
 
 
 def decode_mlp(args, torch, nv, W):
@@ -254,11 +315,8 @@ def silu_quantize(args, torch, nv, W):
 
     w = W.WORKLOADS[5]
     dev = "cuda:0"
-    log(f"[bench] generating gate/up {w.M}x{w.K}")
-    g, u = W.gate_up(w)
-    gd = torch.from_numpy(g).to(torch.bfloat16).to(dev)
-    ud = torch.from_numpy(u).to(torch.bfloat16).to(dev)
-    del g, u
+    log(f"[bench] drawing gate/up {w.M}x{w.K} on the device")
+    gd, ud = W.device_gate_up(w, dev)
     codes = torch.empty((w.M, w.K // 2), dtype=torch.uint8, device=dev)
     scales = torch.empty((w.M, w.K // 16), dtype=torch.uint8, device=dev)
     _, _, ga = nv.nvfp4_silu_mul_quantize(gd, ud, None, codes, scales)  # calibration stand-in
@@ -531,9 +589,26 @@ def cpu_baseline(rows: int = 112):
     oracle.gemm_exact(ac, as_, g_a, wc, ws, gw, segs)
     dt = time.perf_counter() - t0
     flops = 2.0 * rows * w.N * w.K
+    # the decode shape: one activation row encoded and multiplied by the 5120 x 5120 weight (the
+    # weight encoded beforehand, untimed), as GB/s of the same algorithmic bytes as the GPU figure
+    w4 = W.WORKLOADS[4]
+    a4 = W.activations(w4, 1)
+    wc4, ws4, gw4 = oracle.quantize(W.weights(w4))
+    g4 = np.float32(2688.0 / np.abs(a4).max())
+    reps = 3
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        c4, s4, _ = oracle.quantize(a4, g4)
+        oracle.gemm_exact(c4, s4, g4, wc4, ws4, [gw4])
+    dt4 = (time.perf_counter() - t0) / reps
+    nbytes4 = w4.N * w4.K * 9 // 16 + w4.K * 9 // 16 + w4.N * 4
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "host_cpu_count": os.cpu_count(), "host_cpus_usable": len(os.sched_getaffinity(0)),
             "sample": f"{rows} of {w.M} activation rows x all {w.N} columns, K={w.K} "
-                      f"(encode + exact int64 product), {dt:.1f} s"}
+                      f"(encode + exact int64 product), {dt:.1f} s, one thread",
+            "decode": {"value": round(nbytes4 / dt4 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                       "sample": f"M=1 x {w4.K} x {w4.N}: encode + exact int64 product, "
+                                 f"{dt4 * 1e3:.1f} ms per call, mean of {reps}"}}
 
 
 # Sources of the tiled product kernel: its committed HBM counter summary is valid while they are
@@ -549,8 +624,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--only", choices=("all", "prefill", "decode", "silu", "kv", "errors",
-                                      "vendor", "copy"),
+    ap.add_argument("--only", choices=("all", "prefill", "prefill_gdn", "prefill_down", "decode",
+                                      "silu", "kv", "errors", "vendor", "copy"),
                     default="all",
                     help="run one part (for profiler runs); 'copy' is the counter calibration copy")
     args = ap.parse_args()
@@ -590,8 +665,17 @@ def main():
         print(json.dumps({"vendor_bf16_gemm": vendor_bf16_gemm(args, torch, W)}), flush=True)
         return
 
-    p = prefill(args, torch, nv, W)
+    if args.only == "prefill_gdn":
+        print(json.dumps({"prefill_gdn": prefill_summary(prefill(args, torch, nv, W, 2))}), flush=True)
+        return
+    if args.only == "prefill_down":
+        print(json.dumps({"prefill_down": prefill_summary(prefill(args, torch, nv, W, 5))}), flush=True)
+        return
+
+    p = prefill(args, torch, nv, W, 3)
     run_rest = args.only == "all"
+    gdn = prefill_summary(prefill(args, torch, nv, W, 2)) if run_rest else None
+    down = prefill_summary(prefill(args, torch, nv, W, 5)) if run_rest else None
     dec = decode(args, torch, nv, W) if run_rest and not args.no_decode else None
     dec_mlp = decode_mlp(args, torch, nv, W) if run_rest and not args.no_decode else None
     silu = silu_quantize(args, torch, nv, W) if run_rest else None
@@ -616,8 +700,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "nvfp4 (e2m1 + e4m3/16) operands decoded exactly to f16, f16 MFMA, f32 accumulate",
-        "data": "synthetic (seeded; bf16 N(0,1) activations with 1% Student-t(3)x50 channels, "
-                "N(0,0.02) weights)",
+        "data": "synthetic (seeded, drawn on the device; bf16 N(0,1) activations with 1% "
+                "Student-t(3)x50 channels, N(0,0.02) weights)",
         "config": {"workload": w.name, "M": w.M, "K": w.K, "N": w.N,
                    "segments": list(w.seg_sizes), "act_scale": "static", "output": "f32"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
@@ -627,8 +711,11 @@ def main():
                      "kernel": "gemm_tiled_kernel (fused_nvfp4_gemm)",
                      "kernel_ms": round(p["gemm_ms"], 4),
                      "frac_of_mxfp4_peak": round(achieved / MFMA_FP4_PEAK_TFLOPS, 4)},
+        "prefill_gdn": gdn,
+        "prefill_down": down,
         "quantize": {"bound": "hbm", "ms": round(p["quant_ms"], 4), "GB/s": round(q_gbs, 1),
                      "frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4), "bytes": int(p["q_bytes"]),
+                     "rotating_sets": p["quant_sets"],
                      "dynamic": {"ms": round(p["quant_dyn_ms"], 4), "GB/s": round(qd_gbs, 1),
                                  "frac_hbm": round(qd_gbs / HBM_PEAK_GBS, 4),
                                  "bytes": int(p["qd_bytes"])}},

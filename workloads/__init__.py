@@ -6,6 +6,9 @@ from .synthetic import (  # noqa: F401
     KvWorkload,
     Workload,
     activations,
+    device_activations,
+    device_gate_up,
+    device_weights,
     gate_up,
     kv_key_channels,
     kv_slot_mapping,

@@ -292,3 +292,64 @@ def random_nvfp4_bytes(seed: int, rows: int, cols: int, zero_block_frac: float =
     codes = np.where(np.repeat(by_codes, 8, axis=1), zc, codes)
     scales = np.where(by_scale, np.uint8(0), scales)
     return np.ascontiguousarray(codes, np.uint8), np.ascontiguousarray(scales, np.uint8)
+
+
+# ---- the same recipes drawn on the device ----------------------------------------------------
+#
+# The benchmark draws its large inputs directly on the GPU with torch's seeded generator, so that a
+# run does not spend most of its time generating gigabytes on the host.  The distributions are the
+# ones above (same outlier channels, gains, segment spreads, bf16 rounding by torch's
+# nearest-even cast); the random streams differ from the host draws, which the parity tests use.
+
+
+def _device_gen(device, seed: int):
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def device_activations(w: Workload, device, M: int | None = None):
+    """Activations ``[M, K]`` bf16 (or f32) on ``device``: N(0,1), the workload's outlier channels
+    scaled by its gain (``scale``) or replaced by gain * Student-t(3) draws (``t3``)."""
+    import torch
+
+    if w.silu_mul:
+        raise ValueError("this workload's activation is SiLU(g) * u: draw gate and up instead")
+    M = w.M if M is None else M
+    gen = _device_gen(device, 1000 * w.wid + 11)
+    x = torch.randn((M, w.K), generator=gen, device=device, dtype=torch.float32)
+    ch = torch.from_numpy(outlier_channels(w)).to(device)
+    if len(ch):
+        if w.outlier_kind == "scale":
+            x[:, ch] *= w.outlier_gain
+        elif w.outlier_kind == "t3":
+            z = torch.randn((M, len(ch)), generator=gen, device=device)
+            chi2 = (torch.randn((M, len(ch), 3), generator=gen, device=device) ** 2).sum(-1)
+            x[:, ch] = w.outlier_gain * z / torch.sqrt(chi2 / 3.0)
+    return x.to(torch.bfloat16) if w.act_dtype == "bf16" else x
+
+
+def device_gate_up(w: Workload, device, M: int | None = None):
+    """Gate and up inputs ``[M, K]`` of a SiLU(g) * u workload on ``device``, bf16 N(0,1)."""
+    import torch
+
+    M = w.M if M is None else M
+    gen = _device_gen(device, 1000 * w.wid + 14)
+    g = torch.randn((M, w.K), generator=gen, device=device).to(torch.bfloat16)
+    u = torch.randn((M, w.K), generator=gen, device=device).to(torch.bfloat16)
+    return g, u
+
+
+def device_weights(w: Workload, device, rows: slice | None = None):
+    """Weight rows ``[N, K]`` on ``device``: N(0, 0.02) times the segment spread, bf16 (or f32)."""
+    import torch
+
+    rows = slice(0, w.N) if rows is None else rows
+    r0, r1 = rows.start or 0, w.N if rows.stop is None else rows.stop
+    gen = _device_gen(device, 1000 * w.wid + 12 + 7919 * r0)
+    x = torch.randn((r1 - r0, w.K), generator=gen, device=device, dtype=torch.float32)
+    mult = torch.from_numpy(_row_std_mult(w)[r0:r1] * WEIGHT_STD).to(device)
+    x *= mult[:, None]
+    return x.to(torch.bfloat16) if w.w_dtype == "bf16" else x
