@@ -10,10 +10,11 @@
 // Two kernels:
 //  * gemm_general_kernel: any K that is a multiple of 16.  One wavefront per 32x32 output tile,
 //    operands read straight from global memory 4 bytes (8 codes) per lane per K step.
-//  * gemm_tiled_kernel: K a multiple of 64.  A workgroup owns a BM x BN output tile; each K chunk of
-//    64 is staged in LDS as raw 4-bit codes plus E4M3 bytes (9/16 byte per element instead of 2 for
-//    f16, so staging costs a quarter of the LDS space and bandwidth of an f16 GEMM), then every
-//    wavefront decodes its own fragments in registers right before the MFMAs.
+//  * gemm_tiled_kernel: K a multiple of 64.  A workgroup owns a BM x BN output tile (256 x 256 or
+//    256 x 192, chosen per problem); each K chunk of 64 is staged in LDS as raw 4-bit codes plus
+//    E4M3 bytes (9/16 byte per element instead of 2 for f16, so staging costs a quarter of the LDS
+//    space and bandwidth of an f16 GEMM), then every wavefront decodes its own fragments in
+//    registers right before the MFMAs.
 //
 // K-slot permutation.  In a 32x32x16 MFMA, lane l supplies row (l % 32) and 8 of the 16 k-slots
 // (half h = l / 32).  Within a K chunk of 64, lane half h reads the 16 contiguous bytes holding
@@ -76,20 +77,24 @@ struct TileCfg {
   static constexpr int kThreads = WAVES_M * WAVES_N * 64;
   static constexpr int BM = WAVES_M * FM * 32;
   static constexpr int BN = WAVES_N * FN * 32;
-  // one LDS stage: the codes of BM + BN rows (32 bytes each per K chunk of 64), then their 4 scale
-  // bytes per row
+  // scale words per lane group in LDS: a lane reads the words of its F fragments from one group
+  // of 4 (16 bytes) or 8 (32 bytes) slots
+  static constexpr int GA = FM <= 4 ? 4 : 8;
+  static constexpr int GB = FN <= 4 ? 4 : 8;
+  // one LDS stage: the codes of BM + BN rows (32 bytes each per K chunk of 64), then the scale
+  // slots of each operand (4 bytes per slot: one row's 4 scale bytes)
   static constexpr int kCodesA = BM * 32;
   static constexpr int kCodesB = BN * 32;
-  static constexpr int kScalesA = BM * 4;
-  static constexpr int kScalesB = BN * 4;
+  static constexpr int kScalesA = WAVES_M * 32 * GA * 4;
+  static constexpr int kScalesB = WAVES_N * 32 * GB * 4;
   static constexpr int kStage = kCodesA + kCodesB + kScalesA + kScalesB;
-  static constexpr int kPiecesA = BM * 2 / kThreads;  // 16-byte copies per thread per chunk
-  static constexpr int kPiecesB = BN * 2 / kThreads;
-  static constexpr int kWordsA = BM / kThreads;  // 4-byte scale copies per thread per chunk
-  static constexpr int kWordsB = BN / kThreads;
-  static_assert(BM * 2 % kThreads == 0 && BN * 2 % kThreads == 0, "piece split");
-  static_assert(BM % kThreads == 0 && BN % kThreads == 0, "scale split");
-  static_assert(FM == 4 && FN == 4, "one 16-byte scale read per operand assumes 4 fragments");
+  // 16-byte code copies and 4-byte scale copies per thread per chunk (the last may be partial)
+  static constexpr int kPiecesA = (BM * 2 + kThreads - 1) / kThreads;
+  static constexpr int kPiecesB = (BN * 2 + kThreads - 1) / kThreads;
+  static constexpr int kWordsA = (kScalesA / 4 + kThreads - 1) / kThreads;
+  static constexpr int kWordsB = (kScalesB / 4 + kThreads - 1) / kThreads;
+  static_assert(FM >= 1 && FM <= 8 && FN >= 1 && FN <= 8, "fragments per wavefront");
+  static_assert((BM * 2) % 64 == 0 && (BN * 2) % 64 == 0, "whole wavefronts of code copies");
 };
 
 // Per-thread byte offsets of the global rows this thread copies (rows beyond the matrix are
@@ -109,11 +114,14 @@ struct RowOffsets {
 //  * codes: slot d holds row (d / 64) * 32 + (d % 32), bytes [16 * ((d % 64) / 32), +16) of the
 //    chunk.  Each 32-row group is 1 KiB laid out [half][row][16 B] -- exactly the order in which
 //    the 64 lanes of a fragment read it (lane l at 16 l): reads are contiguous, conflict-free.
-//  * scales: slot d holds the 4 scale bytes of row (d / (32F)) * 32F + (d % F) * 32 + (d / F) % 32
-//    (F fragments per wavefront): the F scale words one lane needs sit in one 16-byte slot group.
-template <int F>
+//  * scales: with F fragments per wavefront and lane groups of G >= F slots, slot
+//    d = (g * 32 + r) * G + i holds the 4 scale bytes of row g * 32 F + i * 32 + r (the lane of
+//    row r in wavefront group g, fragment i): the F words one lane needs sit in one group of 16 or
+//    32 bytes.  Padding slots (i >= F) repeat fragment F - 1's row and are never read.
+template <int F, int G>
 __device__ __forceinline__ int scale_slot_row(int d) {
-  return (d / (32 * F)) * (32 * F) + (d % F) * 32 + (d / F) % 32;
+  const int g = d / (32 * G), r = (d / G) % 32, i = min(d % G, F - 1);
+  return g * 32 * F + i * 32 + r;
 }
 
 template <class Cfg, int FM, int FN>
@@ -134,38 +142,46 @@ __device__ __forceinline__ void row_offsets(const GemmArgs& p, int m0, int n0, i
   }
 #pragma unroll
   for (int i = 0; i < Cfg::kWordsA; ++i)
-    o.sa[i] = (uint32_t)min(m0 + scale_slot_row<FM>(tid + i * Cfg::kThreads), p.M - 1) * ks;
+    o.sa[i] = (uint32_t)min(m0 + scale_slot_row<FM, Cfg::GA>(tid + i * Cfg::kThreads), p.M - 1) * ks;
 #pragma unroll
   for (int i = 0; i < Cfg::kWordsB; ++i)
-    o.sb[i] = (uint32_t)min(n0 + scale_slot_row<FN>(tid + i * Cfg::kThreads), p.N - 1) * ks;
+    o.sb[i] = (uint32_t)min(n0 + scale_slot_row<FN, Cfg::GB>(tid + i * Cfg::kThreads), p.N - 1) * ks;
 }
 
-// Issue the direct global->LDS copies of K chunk `kc` into `stage`.
+// Issue the direct global->LDS copies of K chunk `kc` into `stage`.  A wavefront whose copy
+// slots of the last, partial round lie past the area skips that copy (the test is uniform across
+// the wavefront).
 template <class Cfg>
 __device__ __forceinline__ void issue_chunk(const GemmArgs& p, const RowOffsets<Cfg>& o, int kc,
                                             uint8_t* stage) {
   const int wave_slot = (threadIdx.x >> 6) * 64;
 #pragma unroll
   for (int i = 0; i < Cfg::kPiecesA; ++i)
-    __builtin_amdgcn_global_load_lds(p.a_codes + o.a[i] + kc * 32,
-                                     stage + (i * Cfg::kThreads + wave_slot) * 16, 16, 0, 0);
+    if ((i + 1) * Cfg::kThreads <= Cfg::BM * 2 || i * Cfg::kThreads + wave_slot < Cfg::BM * 2)
+      __builtin_amdgcn_global_load_lds(p.a_codes + o.a[i] + kc * 32,
+                                       stage + (i * Cfg::kThreads + wave_slot) * 16, 16, 0, 0);
 #pragma unroll
   for (int i = 0; i < Cfg::kPiecesB; ++i)
-    __builtin_amdgcn_global_load_lds(p.w_codes + o.b[i] + kc * 32,
-                                     stage + Cfg::kCodesA + (i * Cfg::kThreads + wave_slot) * 16,
-                                     16, 0, 0);
+    if ((i + 1) * Cfg::kThreads <= Cfg::BN * 2 || i * Cfg::kThreads + wave_slot < Cfg::BN * 2)
+      __builtin_amdgcn_global_load_lds(p.w_codes + o.b[i] + kc * 32,
+                                       stage + Cfg::kCodesA + (i * Cfg::kThreads + wave_slot) * 16,
+                                       16, 0, 0);
 #pragma unroll
   for (int i = 0; i < Cfg::kWordsA; ++i)
-    __builtin_amdgcn_global_load_lds(p.a_scales + o.sa[i] + kc * 4,
-                                     stage + Cfg::kCodesA + Cfg::kCodesB +
-                                         (i * Cfg::kThreads + wave_slot) * 4,
-                                     4, 0, 0);
+    if ((i + 1) * Cfg::kThreads * 4 <= Cfg::kScalesA ||
+        (i * Cfg::kThreads + wave_slot) * 4 < Cfg::kScalesA)
+      __builtin_amdgcn_global_load_lds(p.a_scales + o.sa[i] + kc * 4,
+                                       stage + Cfg::kCodesA + Cfg::kCodesB +
+                                           (i * Cfg::kThreads + wave_slot) * 4,
+                                       4, 0, 0);
 #pragma unroll
   for (int i = 0; i < Cfg::kWordsB; ++i)
-    __builtin_amdgcn_global_load_lds(p.w_scales + o.sb[i] + kc * 4,
-                                     stage + Cfg::kCodesA + Cfg::kCodesB + Cfg::kScalesA +
-                                         (i * Cfg::kThreads + wave_slot) * 4,
-                                     4, 0, 0);
+    if ((i + 1) * Cfg::kThreads * 4 <= Cfg::kScalesB ||
+        (i * Cfg::kThreads + wave_slot) * 4 < Cfg::kScalesB)
+      __builtin_amdgcn_global_load_lds(p.w_scales + o.sb[i] + kc * 4,
+                                       stage + Cfg::kCodesA + Cfg::kCodesB + Cfg::kScalesA +
+                                           (i * Cfg::kThreads + wave_slot) * 4,
+                                       4, 0, 0);
 }
 
 // Tile order: hardware hands workgroup ids to the 8 XCDs round-robin, so id b runs on XCD b % 8.
@@ -189,14 +205,29 @@ __device__ __forceinline__ void tile_coords(uint32_t bid, uint32_t tiles_m, uint
 }
 
 // One K chunk of a wavefront's fragments, read from LDS: FM + FN code words of 16 bytes (32
-// codes) and one 16-byte scale group per operand.
+// codes) and the scale words of each fragment row (one 16-byte read per operand, a second 4-byte
+// read for a fifth fragment).
 template <int FM, int FN>
 struct Frags {
   uint4 qa[FM];
   uint4 qb[FN];
-  uint4 sa;
-  uint4 sb;
+  uint32_t sa[FM];
+  uint32_t sb[FN];
 };
+
+template <int F>
+__device__ __forceinline__ void read_scale_words(const uint8_t* p, uint32_t (&w)[F]) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < (F < 4 ? F : 4); ++i) w[i] = x[i];
+  if constexpr (F > 4) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p + 16);
+    const uint32_t y[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 4; i < F; ++i) w[i] = y[i - 4];
+  }
+}
 
 template <int FM, int FN>
 __device__ __forceinline__ void read_frags(const uint8_t* stage, int a_frag, int b_frag, int a_scl,
@@ -205,8 +236,8 @@ __device__ __forceinline__ void read_frags(const uint8_t* stage, int a_frag, int
   for (int i = 0; i < FM; ++i) f.qa[i] = *reinterpret_cast<const uint4*>(stage + a_frag + i * 1024);
 #pragma unroll
   for (int j = 0; j < FN; ++j) f.qb[j] = *reinterpret_cast<const uint4*>(stage + b_frag + j * 1024);
-  f.sa = *reinterpret_cast<const uint4*>(stage + a_scl);
-  f.sb = *reinterpret_cast<const uint4*>(stage + b_scl);
+  read_scale_words<FM>(stage + a_scl, f.sa);
+  read_scale_words<FN>(stage + b_scl, f.sb);
 }
 
 template <int STEP>
@@ -252,14 +283,12 @@ __device__ __forceinline__ void interleave_mfma_valu() {
 template <int FM, int FN>
 __device__ __forceinline__ void decode_scales(const Frags<FM, FN>& f, uint32_t sh,
                                               half2_t (&sa)[FM], half2_t (&sb)[FN]) {
-  const uint32_t swa[4] = {f.sa.x, f.sa.y, f.sa.z, f.sa.w};
-  const uint32_t swb[4] = {f.sb.x, f.sb.y, f.sb.z, f.sb.w};
 #pragma unroll
   for (int i = 0; i < FM; ++i)
-    sa[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(swa[i] >> sh, 1.0f, false);
+    sa[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.sa[i] >> sh, 1.0f, false);
 #pragma unroll
   for (int j = 0; j < FN; ++j)
-    sb[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(swb[j] >> sh, 1.0f, false);
+    sb[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.sb[j] >> sh, 1.0f, false);
 }
 
 // Wait until this wavefront's copies of the chunk in `stage` have landed, meet the other
@@ -361,98 +390,93 @@ __device__ __forceinline__ int opaque_tid() {
 }
 
 // Epilogue of one tile: C = acc * alpha[column], through LDS one fragment row (32 rows of the
-// wavefront's sub-tile) at a time.  Each lane writes its four-column pieces into the wavefront's
-// own staging rows, then reads back four consecutive columns of one row, so that a wavefront store
-// covers two rows x 512 bytes -- whole cache lines, not 32 rows x 32 bytes.  The staging area
-// belongs to one wavefront and LDS instructions of a wavefront execute in order, so no barrier is
-// needed.  Rows and columns past the matrix are masked at the store; a lane stores its four
-// columns as one vector when they are all inside and rows of C start 16-byte aligned (`vec`).
-template <int FN>
-constexpr int kEpiStride = FN * 32 + 4;  // floats per staged row; the pad spreads rows over banks
+// wavefront's sub-tile) and up to four fragment columns (128 columns) at a time.  Each lane writes
+// its four-column pieces into the wavefront's own staging rows, then reads back four consecutive
+// columns of one row, so that a wavefront store covers whole rows of up to 512 contiguous bytes
+// instead of 32 rows x 32 bytes.  The staging area belongs to one wavefront and LDS instructions
+// of a wavefront execute in order, so no barrier is needed.  Rows and columns past the matrix are
+// masked at the store; a lane stores its four columns as one vector when they are all inside and
+// rows of C start 16-byte aligned (`vec`).
+constexpr int kEpiStride = 4 * 32 + 4;  // floats per staged row; the pad spreads rows over banks
+
+template <bool BF16, int G, int J0, int FM, int FN>
+__device__ __forceinline__ void store_group(const GemmArgs& p, const floatx16 (&acc)[FM][FN],
+                                            const float* alpha, float* epi, int m0, int n0, int wm,
+                                            int wn, int lane, bool vec, bool interior, int i) {
+  using OutT = typename std::conditional<BF16, uint16_t, float>::type;
+  OutT* const c = reinterpret_cast<OutT*>(p.c);
+  constexpr int S = kEpiStride;
+  constexpr int LPR = G * 8;    // lanes per staged row (four columns each)
+  constexpr int RPI = 64 / LPR;  // rows per read-back instruction
+  constexpr int NT = 32 / RPI;   // read-backs per fragment row
+  const int r = lane & 31, h = lane >> 5;
+  const int rr = lane / LPR;
+  const int cc = (lane % LPR) * 4;  // read-back columns of this lane within the group
+  const int col = wn * FN * 32 + J0 * 32 + cc;
+  const int n = n0 + col;
+  const floatx4 al = *reinterpret_cast<const floatx4*>(alpha + col);
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<floatx4*>(epi + r * S + j * 32 + 8 * q + 4 * h) =
+          floatx4{acc[i][J0 + j][4 * q], acc[i][J0 + j][4 * q + 1], acc[i][J0 + j][4 * q + 2],
+                  acc[i][J0 + j][4 * q + 3]};
+  floatx4 x[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) x[t] = *reinterpret_cast<const floatx4*>(epi + (RPI * t + rr) * S + cc);
+  const int mb = m0 + wm * FM * 32 + i * 32 + rr;
+  const bool full = vec && n + 3 < p.N;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const floatx4 v = {x[t][0] * al[0], x[t][1] * al[1], x[t][2] * al[2], x[t][3] * al[3]};
+    const int m = mb + RPI * t;
+    if (!interior && m >= p.M) continue;
+    OutT* const dst = c + (int64_t)m * p.ldc + n;
+    if (interior || full) {
+      if constexpr (BF16) {
+        const uint32_t lo = f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+        const uint32_t hi = f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+        *reinterpret_cast<uint2*>(dst) = uint2{lo, hi};
+      } else {
+        *reinterpret_cast<floatx4*>(dst) = v;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (n + e < p.N) {
+          if constexpr (BF16)
+            dst[e] = f32_to_bf16_rne(v[e]);
+          else
+            dst[e] = v[e];
+        }
+      }
+    }
+  }
+  // one staged block at a time: its accumulators are read into registers only here
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Column groups of 4, 2 and 1 fragments (a group's rows must fill whole wavefront reads).
+template <bool BF16, int J0, int FM, int FN>
+__device__ __forceinline__ void store_groups(const GemmArgs& p, const floatx16 (&acc)[FM][FN],
+                                             const float* alpha, float* epi, int m0, int n0,
+                                             int wm, int wn, int lane, bool vec, bool interior,
+                                             int i) {
+  if constexpr (J0 < FN) {
+    constexpr int G = FN - J0 >= 4 ? 4 : FN - J0 >= 2 ? 2 : 1;
+    store_group<BF16, G, J0>(p, acc, alpha, epi, m0, n0, wm, wn, lane, vec, interior, i);
+    store_groups<BF16, J0 + G>(p, acc, alpha, epi, m0, n0, wm, wn, lane, vec, interior, i);
+  }
+}
 
 template <bool BF16, int FM, int FN>
 __device__ __forceinline__ void store_tile(const GemmArgs& p, const floatx16 (&acc)[FM][FN],
                                            const float* alpha, float* epi, int m0, int n0, int wm,
                                            int wn, int lane, bool vec, bool interior) {
-  using OutT = typename std::conditional<BF16, uint16_t, float>::type;
-  OutT* const c = reinterpret_cast<OutT*>(p.c);
-  constexpr int S = kEpiStride<FN>;
-  const int r = lane & 31, h = lane >> 5;
-  const int cc = (lane & 31) * 4;  // read-back columns of this lane within the wavefront's 128
-  const int n = n0 + wn * FN * 32 + cc;
-  const floatx4 al = *reinterpret_cast<const floatx4*>(alpha + wn * FN * 32 + cc);
-  if (interior) {
-    // the tile lies inside C and rows are 16-byte aligned: no masks, and the 16 read-backs of a
-    // fragment row are all issued before the first store, so their LDS latency overlaps
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<floatx4*>(epi + r * S + j * 32 + 8 * q + 4 * h) =
-              floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                      acc[i][j][4 * q + 3]};
-      floatx4 x[16];
-#pragma unroll
-      for (int t = 0; t < 16; ++t) x[t] = *reinterpret_cast<const floatx4*>(epi + (2 * t + h) * S + cc);
-      OutT* const dst = c + (int64_t)(m0 + wm * FM * 32 + i * 32 + h) * p.ldc + n;
-#pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const floatx4 v = {x[t][0] * al[0], x[t][1] * al[1], x[t][2] * al[2], x[t][3] * al[3]};
-        if constexpr (BF16) {
-          const uint32_t lo = f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-          const uint32_t hi = f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
-          *reinterpret_cast<uint2*>(dst + (int64_t)(2 * t) * p.ldc) = uint2{lo, hi};
-        } else {
-          *reinterpret_cast<floatx4*>(dst + (int64_t)(2 * t) * p.ldc) = v;
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    return;
-  }
-  const bool full = vec && n + 3 < p.N;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<floatx4*>(epi + r * S + j * 32 + 8 * q + 4 * h) =
-            floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                    acc[i][j][4 * q + 3]};
-    const int mb = m0 + wm * FM * 32 + i * 32 + h;
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const floatx4 x = *reinterpret_cast<const floatx4*>(epi + (2 * t + h) * S + cc);
-      const floatx4 v = {x[0] * al[0], x[1] * al[1], x[2] * al[2], x[3] * al[3]};
-      const int m = mb + 2 * t;
-      if (m >= p.M) continue;
-      OutT* const dst = c + (int64_t)m * p.ldc + n;
-      if (full) {
-        if constexpr (BF16) {
-          const uint32_t lo = f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-          const uint32_t hi = f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
-          *reinterpret_cast<uint2*>(dst) = uint2{lo, hi};
-        } else {
-          *reinterpret_cast<floatx4*>(dst) = v;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (n + e < p.N) {
-            if constexpr (BF16)
-              dst[e] = f32_to_bf16_rne(v[e]);
-            else
-              dst[e] = v[e];
-          }
-        }
-      }
-    }
-    // one fragment row at a time: its accumulators are read into registers only here
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  for (int i = 0; i < FM; ++i)
+    store_groups<BF16, 0>(p, acc, alpha, epi, m0, n0, wm, wn, lane, vec, interior, i);
 }
 
 // Main kernel, persistent: workgroup b runs tiles b, b + G, b + 2G, ... (G = grid size, at most
@@ -478,7 +502,7 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
   // per-column epilogue factors of the current tile, double-buffered by tile parity
   __shared__ __attribute__((aligned(16))) float alpha_s[2][Cfg::BN];
   // epilogue staging, one area of 32 rows per wavefront
-  __shared__ __attribute__((aligned(16))) float epi_s[WAVES_M * WAVES_N][32 * kEpiStride<FN>];
+  __shared__ __attribute__((aligned(16))) float epi_s[WAVES_M * WAVES_N][32 * kEpiStride];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -496,8 +520,8 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
   // LDS read offsets of this lane's fragments and scale groups (within a stage)
   const int a_frag = (wm * FM) * 1024 + lane * 16;
   const int b_frag = Cfg::kCodesA + (wn * FN) * 1024 + lane * 16;
-  const int a_scl = Cfg::kCodesA + Cfg::kCodesB + (wm * 32 + r) * FM * 4;
-  const int b_scl = Cfg::kCodesA + Cfg::kCodesB + Cfg::kScalesA + (wn * 32 + r) * FN * 4;
+  const int a_scl = Cfg::kCodesA + Cfg::kCodesB + (wm * 32 + r) * Cfg::GA * 4;
+  const int b_scl = Cfg::kCodesA + Cfg::kCodesB + Cfg::kScalesA + (wn * 32 + r) * Cfg::GB * 4;
 
   uint32_t v = blockIdx.x;
   uint32_t tmi, tni;
@@ -590,21 +614,13 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
   }
 }
 
-#ifndef NVFP4_TILED_CFG
-#define NVFP4_TILED_CFG 2, 2, 4, 4
-#endif
-
 template <int WAVES_M, int WAVES_N, int FM, int FN>
-hipError_t launch_tiled_cfg(const GemmArgs& a, hipStream_t stream) {
+hipError_t launch_tiled_cfg(const GemmArgs& a, int cus, hipStream_t stream) {
   using Cfg = TileCfg<WAVES_M, WAVES_N, FM, FN>;
   const uint32_t tiles_m = (a.M + Cfg::BM - 1) / Cfg::BM;
   const uint32_t tiles_n = (a.N + Cfg::BN - 1) / Cfg::BN;
   // one workgroup per compute unit (the kernel's registers allow one per compute unit), each
   // walking its share of the tiles
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
   const uint32_t ntiles = tiles_m * tiles_n;
   const uint32_t grid = min(ntiles, (uint32_t)max(cus, 1));
   hipLaunchKernelGGL((gemm_tiled_kernel<WAVES_M, WAVES_N, FM, FN>), dim3(grid),
@@ -612,7 +628,33 @@ hipError_t launch_tiled_cfg(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Tile shapes of the persistent kernel: 256 x 256 (4 x 4 fragments per wavefront) and 256 x 192
+// (4 x 3).  The narrower tile decodes more per MFMA (7 fragment words per 12 MFMAs instead of 8 per
+// 16) and measured about 0.89 of the wider one's rate per tile FLOP, but it can save a whole round
+// of tiles: the GDN in_proj (4096 x 8288) is 528 tiles of 256 x 256 on 256 compute units, three
+// rounds of which the last is 1/16 full, and 704 of 256 x 192, three rounds of 3/4 the work.
+// The shape is chosen by the estimated time, rounds x tile FLOPs / relative rate.  Every output
+// element is accumulated the same way in either shape (same K chunks, steps and MFMA), so the
+// choice never changes a result.
+constexpr float kNarrowTileRate = 0.89f;
+
 }  // namespace
+
+hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  cus = max(cus, 1);
+  auto rounds = [&](int bm, int bn) {
+    const int64_t t = (int64_t)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
+    return (t + cus - 1) / cus;
+  };
+  const float wide = (float)rounds(256, 256) * 256.0f * 256.0f;
+  const float narrow = (float)rounds(256, 192) * 256.0f * 192.0f / kNarrowTileRate;
+  if (narrow < wide) return launch_tiled_cfg<2, 2, 4, 3>(a, cus, stream);
+  return launch_tiled_cfg<2, 2, 4, 4>(a, cus, stream);
+}
 
 hipError_t launch_gemm_general(const GemmArgs& a, hipStream_t stream) {
   const uint32_t tiles_m = (a.M + 63) / 64;
@@ -620,10 +662,6 @@ hipError_t launch_gemm_general(const GemmArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(gemm_general_kernel, dim3(tiles_m * tiles_n), dim3(256), 0, stream, a,
                      tiles_n);
   return hipGetLastError();
-}
-
-hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
-  return launch_tiled_cfg<NVFP4_TILED_CFG>(a, stream);
 }
 
 GemmPath choose_gemm_path(int64_t M, int64_t K, bool c_bf16) {

@@ -365,3 +365,29 @@ def test_full_size_sampled(wid):
 @pytest.mark.parametrize("M", [1, 4, 16])
 def test_decode_shapes(M):
     _sampled_full_size(4, M)
+
+
+def test_fused_equals_per_segment_calls_across_tile_shapes():
+    """The GDN in_proj's shape (M = 4096, modules of 2048, 2048, 4096, 48 and 48 columns): the fused
+    product runs 256 x 192 tiles (three rounds of 704 tiles instead of 528 tiles of 256 x 256 whose
+    third round is 1/16 full), the 4096-column module alone runs 256 x 256 tiles and the others
+    256 x 192.  Every element is accumulated the same way in either shape, so the fused result
+    equals the per-module results bit for bit; sampled rows are checked against the oracle."""
+    from workloads import random_nvfp4_bytes
+
+    from .gpu_util import oracle_product
+
+    M, K = 4096, 128
+    sizes = [2048, 2048, 4096, 48, 48]
+    segs = list(np.cumsum([0] + sizes))
+    ac, as_ = random_nvfp4_bytes(71, M, K)
+    wc, ws = random_nvfp4_bytes(72, segs[-1], K)
+    gw = np.array([0.5, 2.0, 1.25, 3.0, 0.75], np.float32)
+    ga = np.float32(1.5)
+    fused = _gpu_product(ac, as_, ga, wc, ws, gw, segs)
+    parts = [_gpu_product(ac, as_, ga, wc[segs[j]:segs[j + 1]], ws[segs[j]:segs[j + 1]], [gw[j]],
+                          [0, sizes[j]]) for j in range(len(sizes))]
+    assert np.array_equal(fused, np.concatenate(parts, axis=1))
+    rows = np.arange(0, M, 64)
+    R, B = oracle_product(ac[rows], as_[rows], ga, wc, ws, gw, segs)
+    check_gemm(fused[rows], R, B, "fused GDN in_proj shape, sampled rows")

@@ -57,9 +57,10 @@ def _run(ac, as_, ga, wc, ws, gw, segs, what):
 RAW_SHAPES = [
     (40, 300, 2064, "general"),
     (33, 65, 48, "general, K = 48"),
-    (300, 260, 256, "tiled, 4 K chunks"),
-    (257, 513, 320, "tiled, 5 K chunks (odd)"),
-    (17, 1000, 2048, "tiled, 17 rows"),
+    (300, 260, 256, "tiled 256 x 192, 4 K chunks"),
+    (257, 513, 320, "tiled 256 x 192, 5 K chunks (odd)"),
+    (17, 1000, 2048, "tiled 256 x 192, 17 rows"),
+    (4096, 4096, 128, "tiled 256 x 256, one full round"),
     (1, 3000, 2048, "one-pass decode, one tile per workgroup"),
     (16, 6000, 2048, "one-pass decode, two tiles per workgroup"),
     (3, 8100, 8192, "one-pass decode, K = 8192"),
@@ -125,14 +126,15 @@ def test_small_scales_under_a_static_activation_scale():
 
 
 @pytest.mark.parametrize("M,N,K,what", [
-    (2304, 8485, 128, "306 tiles (not a multiple of 8), partial last tile column"),
-    (2304, 7936, 192, "279 tiles, 3 K chunks per tile (odd)"),
-    (1100, 16400, 320, "325 tiles, 5 K chunks, partial last tile row"),
+    (2304, 8485, 128, "405 tiles of 256 x 192 (not a multiple of 8), partial last tile column"),
+    (2304, 7936, 192, "378 tiles of 256 x 192, 3 K chunks per tile (odd)"),
+    (1100, 16400, 320, "430 tiles of 256 x 192, 5 K chunks, partial last tile row"),
+    (1100, 19653, 192, "385 tiles of 256 x 256, 3 K chunks, partial last tile row and column"),
 ])
 def test_mid_size_full_output(M, N, K, what):
     """Every output element of problems with more tiles than compute units, so each persistent
     workgroup runs several tiles back to back (plain tile order, since the tile count is not a
-    multiple of 8), compared with the oracle."""
+    multiple of 8), in both tile shapes the dispatch picks between, compared with the oracle."""
     a = random_matrix(90 + K, M, K, outlier_cols=3)
     wt = random_matrix(91 + K, N, K, std=0.02)
     segs = [0, N // 2 + 3, N]
@@ -146,4 +148,4 @@ def test_mid_size_raw_bytes_full_output():
     ac, as_ = random_nvfp4_bytes(5, M, K)
     wc, ws = random_nvfp4_bytes(6, N, K)
     _run(ac, as_, np.float32(0.75), wc, ws, np.array([3.0], np.float32), [0, N],
-         "raw bytes, full output, 279 tiles, odd K chunks")
+         "raw bytes, full output, 378 tiles, odd K chunks")
