@@ -162,7 +162,9 @@ def decode(args, torch, nv, W):
     Two timings per M: ``call_us``, the median over single calls (encode + product) between HIP
     events, launch latency included; ``kernel_us``, the product kernels alone, 24 of them (one per
     weight copy) replayed back to back from a HIP graph, total / 24.  The algorithmic bytes of the
-    product are the NVFP4 weights (codes + scales), the encoded activations and the f32 output."""
+    product are the NVFP4 weights (codes + scales), the encoded activations and the f32 output.
+    ``linear``: the same step through nvfp4_linear, encode and product in one launch (call and
+    graph-replay timings as above)."""
     import numpy as np
 
     w = W.WORKLOADS[4]
@@ -214,9 +216,40 @@ def decode(args, torch, nv, W):
         del graph
         nbytes = w.N * w.K * 9 // 16 + M * w.K * 9 // 16 + M * w.N * 4
         gbs = nbytes / (k_ms * 1e-3) / 1e9
+        # the same step through nvfp4_linear: the activation encode and the product in one launch
+        # (one call per step; bytes: the bf16 activation read instead of its codes)
+        for i in range(2 * R):
+            wc, ws = copies[i % R]
+            nv.nvfp4_linear(ad, ga, wc, ws, gw, out=C, a_codes=ac, a_scales=as_)
+        torch.cuda.synchronize()
+        for i in range(n):
+            wc, ws = copies[i % R]
+            evs[2 * i].record()
+            nv.nvfp4_linear(ad, ga, wc, ws, gw, out=C, a_codes=ac, a_scales=as_)
+            evs[2 * i + 1].record()
+        torch.cuda.synchronize()
+        lcall_ms = sorted(evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(n))[n // 2]
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for wc, ws in copies:
+                nv.nvfp4_linear(ad, ga, wc, ws, gw, out=C, a_codes=ac, a_scales=as_)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        lk_ms = e0.elapsed_time(e1) / (reps * R)
+        del graph
+        lbytes = w.N * w.K * 9 // 16 + M * w.K * 2 + M * w.K * 9 // 16 + M * w.N * 4
         res[f"M{M}"] = {"kernel_us": round(k_ms * 1e3, 3), "call_us": round(call_ms * 1e3, 3),
                         "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-                        "bytes": nbytes}
+                        "bytes": nbytes,
+                        "linear": {"kernel_us": round(lk_ms * 1e3, 3),
+                                   "call_us": round(lcall_ms * 1e3, 3),
+                                   "GB/s": round(lbytes / (lk_ms * 1e-3) / 1e9, 1),
+                                   "bytes": lbytes, "launches": 1}}
     res["copy_ceiling"] = _copy_ceiling(torch, copies, R)
     return res
 

@@ -12,6 +12,8 @@ Entry points (same names as the C ABI):
 * ``nvfp4_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, out_dtype)`` -> ``C``
 * ``fused_nvfp4_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_gscale, seg_offsets,
   out_dtype)`` -> ``C``
+* ``nvfp4_linear(x, a_gscale, w_codes, w_scales, seg_gscale, seg_offsets, out_dtype)`` ->
+  ``(C, a_codes, a_scales)``
 * ``nvfp4_fake_quantize(x, global_scale=None, out_dtype=None)`` -> ``(xh, global_scale)``
 * ``nvfp4_quant_error_stats(x, global_scale=None)`` -> ``(err2, norm2, dominated, global_scale)``
 * ``nvfp4_requantize(codes, scales, g_in, g_out)`` -> ``(codes, scales)``
@@ -34,7 +36,7 @@ NVFP4_MAX_SEGMENTS = 16
 
 #: every symbol include/nvfp4.h declares
 EXPORTED_SYMBOLS = ("nvfp4_quantize", "nvfp4_silu_mul_quantize", "nvfp4_gemm", "fused_nvfp4_gemm",
-                    "nvfp4_fake_quantize", "nvfp4_quant_error_stats", "nvfp4_requantize",
+                    "nvfp4_linear", "nvfp4_fake_quantize", "nvfp4_quant_error_stats", "nvfp4_requantize",
                     "nvfp4_harmonize_segments", "nvfp4_kv_fp8_store", "nvfp4_kv_fp8_load",
                     "nvfp4_status_string", "nvfp4_version")
 
@@ -87,6 +89,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.fused_nvfp4_gemm.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.POINTER(c_i64),
                                      c_int, c_i64, c_i64, c_i64, c_vp, c_int, c_i64, c_vp]
     lib.fused_nvfp4_gemm.restype = c_int
+    lib.nvfp4_linear.argtypes = [c_vp, c_int, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                 ctypes.POINTER(c_i64), c_int, c_i64, c_i64, c_i64, c_vp, c_int,
+                                 c_i64, c_vp]
+    lib.nvfp4_linear.restype = c_int
     lib.nvfp4_status_string.argtypes = [c_int]
     lib.nvfp4_status_string.restype = ctypes.c_char_p
     lib.nvfp4_version.argtypes = []
@@ -314,6 +320,50 @@ def fused_nvfp4_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_gscale,
                                 _ptr(w_scales), _ptr(seg_gscale), arr, nseg, M, N, K, _ptr(out),
                                 _dtype_code(out.dtype), out.stride(0), _stream(a_codes.device)))
     return out
+
+
+def nvfp4_linear(x, a_gscale, w_codes, w_scales, seg_gscale, seg_offsets=None, out_dtype=None,
+                 out=None, a_codes=None, a_scales=None):
+    """The linear layer on a raw activation ``x[M, K]`` (f32/bf16/f16, contiguous rows): encode it
+    with the static scale ``a_gscale`` (bit-identical to :func:`nvfp4_quantize`) and form the fused
+    product with the weight's modules (``seg_offsets``; None: one module), in one launch for decode
+    shapes.  Returns ``(C, a_codes, a_scales)``."""
+    torch = _torch()
+    lib = load_library()
+    _input_matrix(x, "x")
+    M, K = x.shape
+    if w_codes.dim() != 2:
+        raise ValueError("w_codes must be 2-D")
+    N = w_codes.shape[0]
+    offs = [0, N] if seg_offsets is None else [int(o) for o in seg_offsets]
+    nseg = len(offs) - 1
+    if not 1 <= nseg <= NVFP4_MAX_SEGMENTS:
+        raise ValueError(f"between 1 and {NVFP4_MAX_SEGMENTS} segments, got {nseg}")
+    if w_codes.shape[1] * 2 != K:
+        raise ValueError("x and W disagree on K")
+    _packed(w_codes, N, K // 2, "w_codes")
+    _packed(w_scales, N, K // 16, "w_scales")
+    _scales_f32(a_gscale, 1, "a_gscale")
+    _scales_f32(seg_gscale, nseg, "segment global scales")
+    if a_codes is not None:
+        _packed(a_codes, M, K // 2, "a_codes")
+    if a_scales is not None:
+        _packed(a_scales, M, K // 16, "a_scales")
+    if out is not None:
+        _matrix_out(out, M, N, "out", (torch.float32, torch.bfloat16))
+    _require_cuda(x, a_gscale, w_codes, w_scales, seg_gscale, out, a_codes, a_scales)
+    if a_codes is None:
+        a_codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    if a_scales is None:
+        a_scales = torch.empty((M, K // 16), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = _out(M, N, out_dtype or torch.float32, x.device)
+    arr = (ctypes.c_int64 * len(offs))(*offs)
+    _check(lib.nvfp4_linear(_ptr(x), _dtype_code(x.dtype), x.stride(0), _ptr(a_gscale),
+                            _ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales),
+                            _ptr(seg_gscale), arr, nseg, M, N, K, _ptr(out), _dtype_code(out.dtype),
+                            out.stride(0), _stream(x.device)))
+    return out, a_codes, a_scales
 
 
 def nvfp4_fake_quantize(x, global_scale=None, out_dtype=None, out=None):

@@ -52,10 +52,10 @@ nvfp4_status check_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const f
   return NVFP4_OK;
 }
 
-nvfp4_status run_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
-                      const uint8_t* w_codes, const uint8_t* w_scales, const float* seg_gscale,
-                      const int64_t* seg_offsets, int nseg, int64_t M, int64_t N, int64_t K,
-                      void* c, nvfp4_dtype c_dtype, int64_t ldc, void* stream) {
+nvfp4::GemmArgs gemm_args(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                          const uint8_t* w_codes, const uint8_t* w_scales, const float* seg_gscale,
+                          const int64_t* seg_offsets, int nseg, int64_t M, int64_t N, int64_t K,
+                          void* c, nvfp4_dtype c_dtype, int64_t ldc) {
   nvfp4::GemmArgs a{};
   a.a_codes = a_codes;
   a.a_scales = a_scales;
@@ -74,6 +74,15 @@ nvfp4_status run_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const flo
   a.seg.nseg = nseg;
   for (int j = 0; j <= nseg; ++j) a.seg.off[j] = (int32_t)seg_offsets[j];
   for (int j = nseg + 1; j <= NVFP4_MAX_SEGMENTS; ++j) a.seg.off[j] = (int32_t)N;
+  return a;
+}
+
+nvfp4_status run_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                      const uint8_t* w_codes, const uint8_t* w_scales, const float* seg_gscale,
+                      const int64_t* seg_offsets, int nseg, int64_t M, int64_t N, int64_t K,
+                      void* c, nvfp4_dtype c_dtype, int64_t ldc, void* stream) {
+  const nvfp4::GemmArgs a = gemm_args(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_gscale,
+                                      seg_offsets, nseg, M, N, K, c, c_dtype, ldc);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   switch (nvfp4::choose_gemm_path(M, K, a.c_bf16 != 0)) {
@@ -319,6 +328,36 @@ nvfp4_status fused_nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                                seg_offsets, nseg, M, N, K, c, c_dtype, ldc);
   if (st != NVFP4_OK) return st;
   if (M == 0 || N == 0) return NVFP4_OK;
+  return run_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_gscale, seg_offsets, nseg, M,
+                  N, K, c, c_dtype, ldc, stream);
+}
+
+nvfp4_status nvfp4_linear(const void* x, nvfp4_dtype x_dtype, int64_t ldx, const float* a_gscale,
+                          uint8_t* a_codes, uint8_t* a_scales, const uint8_t* w_codes,
+                          const uint8_t* w_scales, const float* seg_gscale,
+                          const int64_t* seg_offsets, int nseg, int64_t M, int64_t N, int64_t K,
+                          void* c, nvfp4_dtype c_dtype, int64_t ldc, void* stream) {
+  nvfp4_status st = check_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_gscale,
+                               seg_offsets, nseg, M, N, K, c, c_dtype, ldc);
+  if (st != NVFP4_OK) return st;
+  if (M != 0 && !x) return NVFP4_EINVAL;
+  if (!valid_in_dtype(x_dtype)) return NVFP4_EINVAL;
+  if (ldx < K || ldx < 1) return NVFP4_ESHAPE;
+  if (M > 0 && (M - 1) * ldx + K > kMaxSpan) return NVFP4_ESHAPE;
+  if (!aligned(x, 16) || (ldx * dtype_bytes(x_dtype)) % 16 != 0) return NVFP4_EALIGN;
+  if (M == 0) return NVFP4_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (N > 0 && nvfp4::choose_gemm_path(M, K, c_dtype == NVFP4_BF16) == nvfp4::GemmPath::Skinny &&
+      nvfp4::skinny_one_pass(M, N, K)) {
+    nvfp4::GemmArgs a = gemm_args(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_gscale,
+                                  seg_offsets, nseg, M, N, K, c, c_dtype, ldc);
+    return device_status(
+        nvfp4::launch_gemm_skinny_encode(a, x, x_dtype, ldx, a_codes, a_scales, s));
+  }
+  hipError_t e = nvfp4::launch_quantize(x, x_dtype, M, K, ldx, const_cast<float*>(a_gscale), 0,
+                                        a_codes, a_scales, s);
+  if (e != hipSuccess) return NVFP4_EDEVICE;
+  if (N == 0) return NVFP4_OK;
   return run_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_gscale, seg_offsets, nseg, M,
                   N, K, c, c_dtype, ldc, stream);
 }

@@ -7,27 +7,31 @@
 // Work split.  One workgroup per compute unit: workgroup b owns the `ncols` output columns
 // [b * ncols, (b + 1) * ncols) -- ncols = ceil(N / compute units), so every compute unit streams the
 // same number of weight bytes -- as T = 1 or 2 MFMA tiles of 16 columns (the second tile may be
-// partly empty), plus all M <= 16 activation rows.  Its 8 wavefronts first copy the tiles' weight
-// rows (codes and scales) into LDS with direct global->LDS copies in which each wavefront
-// instruction moves 1 KiB of contiguous memory, so the weight stream is fully coalesced.  Each
-// wavefront then takes one eighth of every K phase: it reads the weight fragments from LDS and the
-// activation fragments from global memory (L2-resident: every workgroup reads the same few rows),
-// decodes the activation fragment once and the weight fragments of each tile exactly to f16, and
-// contracts with v_mfma_f32_16x16x32_f16 (A = activations padded to 16 rows with zeros, B =
-// weights).  The 8 partial 16x16 tiles of each tile are summed through LDS in a fixed order
-// (deterministic), scaled per column by 1 / (gA * gW[seg(n)]) and stored.  Every output element
-// is accumulated the same way whichever workgroup and tile slot its column falls in.
+// partly empty), plus all M <= 16 activation rows.  K is cut into phases of 1024 and each phase
+// into 8 chunks of 128; wavefront w of the 8 owns chunk w of every phase.
 //
-// K-slot permutation: in a 16x16x32 MFMA, lane l supplies row/column (l % 16) and 8 of the 32
-// k-slots (group g = l / 16).  Within a chunk of 128, lane group g uses the 16 bytes holding
-// elements [32g, 32g + 32) of its row, 32-bit word j of them in MFMA step j (j = 0..3); word j
-// covers elements 32g + 8j .. +7, inside 16-block 2g + j/2.  Both operands use this map.
+// Every lane loads exactly the bytes it feeds to the MFMA: in a 16x16x32 MFMA, lane l supplies
+// row/column r = l % 16 and 8 of the 32 k-slots (group g = l / 16); within a chunk of 128, lane
+// group g uses the 16 bytes holding elements [32g, 32g + 32) of its row, 32-bit word j of them in
+// MFMA step j (j = 0..3), inside 16-blocks 2g and 2g + 1 (two scale bytes).  Both operands use this
+// map.  So a wavefront's weight load of one tile and phase reads 16 rows x 64 contiguous bytes, the
+// eight wavefronts together 16 rows x 512 bytes, straight into registers: no LDS staging and no
+// workgroup barrier while the weights stream.  All loads of the launch are issued up front, the
+// activation's first (small, and the same for every workgroup, so served from L2), then the weight
+// scales, then the weight codes phase by phase.  The activation fragments of all phases are decoded
+// to f16 while the weights are in flight, so once phase q's weights land only their decode and the
+// MFMAs remain.  Rows of the activation at or past M are zero.
 //
-// LDS layout of the codes: row r, 16-byte piece j (bytes [16j, 16j+16) of the row) sits at slot
-// r * P + ((j & ~15) | ((j ^ r) & 15)), P = K/32 pieces per row.  The XOR swizzle spreads the 16
-// rows a fragment read touches over all LDS banks; the copy realises it by choosing, for each
-// destination slot, which global piece to fetch (a permutation inside 256-byte groups, so each
-// copy instruction still reads 1 KiB of contiguous memory).
+// Activation input.  Either its NVFP4 codes and scales (the product alone), or the raw activation
+// (f32, bf16 or f16) with its static global scale: then every workgroup first encodes the M x K
+// activation into LDS with the encoder's block routine (bit-identical codes and scales), workgroup
+// 0 also writes them out for the caller, and the lanes read their fragments from LDS.  That makes
+// a decode step's activation encode and product one launch.
+//
+// Reduction: the 8 wavefronts' partial 16x16 tiles of each tile are summed through LDS in a fixed
+// order (deterministic), scaled per column by 1 / (gA * gW[seg(n)]) and stored.  Every output
+// element is accumulated the same way whichever workgroup and tile slot its column falls in.
+#include "codec.h"
 #include "gemm_common.h"
 
 namespace nvfp4 {
@@ -35,120 +39,61 @@ namespace {
 
 constexpr int kSkinnyWaves = 8;
 constexpr int kSkinnyThreads = kSkinnyWaves * 64;
-constexpr int kPhaseK = 1024;                    // K elements per phase (8 chunks of 128)
-constexpr int kPhasePieces = kPhaseK / 32;       // 16-byte code pieces per row per phase (32)
-constexpr int kPhaseCodes = 16 * kPhasePieces;   // code slots per phase (512 = one per thread)
-constexpr int kPhaseScaleBytes = kPhaseK / 16;   // scale bytes per row per phase (64)
-constexpr int kPhaseBytes = kPhaseCodes * 16;   // 8 KiB of codes per phase
-// per wavefront and phase: one weight-code copy per tile and the activation-code load
-template <int T>
-constexpr int kVmemPerPhase = T + 1;
+constexpr int kPhaseK = 1024;  // K elements per phase (8 chunks of 128, one per wavefront)
 
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
+// Raw activation input of the encoding form (null `x`: the activation comes encoded in GemmArgs).
+struct DecodeEncode {
+  const void* x;
+  int64_t ldx;      // elements per row of x
+  uint8_t* codes;   // the activation's codes and scales, written by workgroup 0 (row pitch K/2, K/16)
+  uint8_t* scales;
+};
+
+// 16-byte and 2-byte loads of one lane's fragment bytes.
+__device__ __forceinline__ uint4 load16(const uint8_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ uint32_t load2(const uint8_t* p) {
+  return *reinterpret_cast<const uint16_t*>(p);
 }
 
-// Issue phase P's copies (weight codes of each tile's 16 rows into its buffer) and this lane's
-// activation-code load for its chunk of the phase.  Every wavefront issues exactly
-// kVmemPerPhase<T> vector memory instructions per phase, so the wait for phase P is a compile-time
-// vmcnt.  Rows past the workgroup's columns load its last column instead (never stored).
-template <int P, int T>
-__device__ __forceinline__ void issue_phase(const GemmArgs& p, int c0, int clast, int wave,
-                                            int lane, int r, int g, uint8_t* buf0, uint8_t* buf1,
-                                            uint4& aw) {
-  const int kb = p.k_pitch / 2;
-  // codes: slot t = wave * 64 + lane holds row t / 32, phase piece (t % 32) ^ row within 16s
-  const int t = wave * 64 + lane;
-  const int row = t / kPhasePieces;
-  const int jl = t - row * kPhasePieces;
-  const int j = (jl & ~15) | ((jl ^ row) & 15);
-#pragma unroll
-  for (int tile = 0; tile < T; ++tile) {
-    const int grow = min(c0 + tile * 16 + row, clast);
-    __builtin_amdgcn_global_load_lds(p.w_codes + (int64_t)grow * kb + P * (kPhaseK / 2) + j * 16,
-                                     (tile == 0 ? buf0 : buf1) + wave * 64 * 16, 16, 0, 0);
-  }
-  // this lane's activation fragment for chunk `wave` of the phase; rows >= M load the last row
-  // (unconditionally, so no register merge forces an early wait) and are zeroed at use
-  {
-    const int c = P * (kPhaseK / 128) + wave;
-    const int arow = min(r, p.M - 1);
-    aw = *reinterpret_cast<const uint4*>(p.a_codes + (int64_t)arow * kb + c * 64 + g * 16);
-  }
-  // keep the phases' memory instructions in phase order (the waits count on it)
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// Contract this wavefront's chunk of phase data (chunk `wave` of the phase) for each tile: the
-// activation fragment is decoded once per MFMA step and used by every tile.
-template <int T>
-__device__ __forceinline__ void compute_phase(const uint8_t* buf0, const uint8_t* buf1,
-                                              const uint8_t* wsc, const uint8_t* asc, int ks,
-                                              int c, int wave, int r, int g, bool arow_valid,
-                                              const uint4& aw_in, floatx4_t (&acc)[T]) {
-  const uint32_t keep = arow_valid ? 0xFFFFFFFFu : 0u;  // padded rows contribute zeros
-  const uint4 aw = {aw_in.x & keep, aw_in.y & keep, aw_in.z & keep, aw_in.w & keep};
-  const uint32_t as2 = *reinterpret_cast<const uint16_t*>(asc + r * ks + c * 8 + g * 2) & keep;
-  const half2_t sa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(as2, 1.0f, false);
-  const int j = wave * 4 + g;
-  const int slot = (r * kPhasePieces + ((j & ~15) | ((j ^ r) & 15))) * 16;
-  uint4 ww[T];
-  half2_t sw[T];
-#pragma unroll
-  for (int tile = 0; tile < T; ++tile) {
-    ww[tile] = *reinterpret_cast<const uint4*>((tile == 0 ? buf0 : buf1) + slot);
-    const uint32_t ws2 =
-        *reinterpret_cast<const uint16_t*>(wsc + (tile * 16 + r) * ks + c * 8 + g * 2);
-    sw[tile] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ws2, 1.0f, false);
-  }
-  const uint32_t aq[4] = {aw.x, aw.y, aw.z, aw.w};
-#pragma unroll
-  for (int s2 = 0; s2 < 4; ++s2) {
-    const half8_t av = decode8(aq[s2], s2 < 2 ? sa[0] : sa[1]);
-#pragma unroll
-    for (int tile = 0; tile < T; ++tile) {
-      const uint32_t wq = s2 == 0 ? ww[tile].x : s2 == 1 ? ww[tile].y : s2 == 2 ? ww[tile].z
-                                                                                   : ww[tile].w;
-      const half8_t bv = decode8(wq, s2 < 2 ? sw[tile][0] : sw[tile][1]);
-      acc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[tile], 0, 0, 0);
+// Encode activation rows [0, M) x [0, K) with the static scale *a_g into LDS (codes [M][K/2], scales
+// [M][K/16]), one 16-element block per thread and step; workgroup 0 also writes them to `e`.
+template <nvfp4_dtype XDT>
+__device__ __forceinline__ void encode_activation(const GemmArgs& p, const DecodeEncode& e,
+                                                  uint8_t* lcodes, uint8_t* lscales) {
+  const float g = __builtin_nontemporal_load(p.a_g);
+  const float gs6 = g / 6.0f;
+  const int bpr = p.K / 16;  // blocks per row
+  const bool out = blockIdx.x == 0 && e.codes != nullptr;
+  for (int b = threadIdx.x; b < p.M * bpr; b += kSkinnyThreads) {
+    const int row = b / bpr, blk = b - row * bpr;
+    float v[16];
+    codec::load_block<XDT>(reinterpret_cast<const uint8_t*>(e.x) +
+                               ((int64_t)row * e.ldx + (int64_t)blk * 16) * codec::elem_bytes<XDT>(),
+                           v);
+    uint32_t word[2];
+    const uint32_t sc = codec::encode_codes(v, g, gs6, word);
+    *reinterpret_cast<uint2*>(lcodes + b * 8) = uint2{word[0], word[1]};
+    lscales[b] = (uint8_t)sc;
+    if (out) {
+      *reinterpret_cast<uint2*>(e.codes + (int64_t)b * 8) = uint2{word[0], word[1]};
+      e.scales[b] = (uint8_t)sc;
     }
   }
 }
 
-// K = NPH * 1024.  Every phase of every tile has its own statically named LDS buffer, and all
-// copies are issued before any phase is computed: the compiler sees which buffer each read depends
-// on, so phase P is computed as soon as its own copies (and activation loads) have landed while
-// later phases are still streaming in.
-template <int NPH, int T>
+// K = NPH * 1024, T tiles of 16 columns, XDT = the raw activation's type in the encoding form
+// (NVFP4_F32 / BF16 / F16) or -1 when the activation comes encoded.
+template <int NPH, int T, int XDT>
 __global__ void __launch_bounds__(kSkinnyThreads)
-gemm_skinny_kernel(GemmArgs p, int ncols) {
-  __shared__ floatx4_t partial[T > 1 ? 2 : 1][kSkinnyWaves][64];
-  // block scales of the (up to) 32 weight rows and of up to 16 activation rows, [rows][K/16]
-  // (sized for the largest K: a template-dependent size here is miscompiled by the host pass)
-  __shared__ __attribute__((aligned(16))) uint8_t wsc[32 * (kSkinnyMaxK / 16)];
-  __shared__ __attribute__((aligned(16))) uint8_t asc[16 * (kSkinnyMaxK / 16)];
-  __shared__ __attribute__((aligned(16))) uint8_t b0[kPhaseBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t b1[NPH > 1 ? kPhaseBytes : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t b2[NPH > 2 ? kPhaseBytes : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t b3[NPH > 3 ? kPhaseBytes : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t b4[NPH > 4 ? kPhaseBytes : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t b5[NPH > 5 ? kPhaseBytes : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t b6[NPH > 6 ? kPhaseBytes : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t b7[NPH > 7 ? kPhaseBytes : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t c0b[T > 1 ? kPhaseBytes : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t c1b[(T > 1 && NPH > 1) ? kPhaseBytes : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t c2b[(T > 1 && NPH > 2) ? kPhaseBytes : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t c3b[(T > 1 && NPH > 3) ? kPhaseBytes : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t c4b[(T > 1 && NPH > 4) ? kPhaseBytes : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t c5b[(T > 1 && NPH > 5) ? kPhaseBytes : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t c6b[(T > 1 && NPH > 6) ? kPhaseBytes : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t c7b[(T > 1 && NPH > 7) ? kPhaseBytes : 16];
-  uint8_t* const bufs0[8] = {b0, b1, b2, b3, b4, b5, b6, b7};
-  uint8_t* const bufs1[8] = {c0b, c1b, c2b, c3b, c4b, c5b, c6b, c7b};
+gemm_skinny_kernel(GemmArgs p, DecodeEncode e, int ncols) {
+  constexpr bool kEncode = XDT >= 0;
+  __shared__ floatx4_t partial[T][kSkinnyWaves][64];
+  // the encoded activation (encoding form only): codes [M][K/2], scales [M][K/16]
+  __shared__ __attribute__((aligned(16))) uint8_t act[kEncode ? 16 * (kSkinnyMaxK / 2 + kSkinnyMaxK / 16) : 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -158,83 +103,95 @@ gemm_skinny_kernel(GemmArgs p, int ncols) {
   const int cend = min(c0 + ncols, p.N);
   const int clast = cend - 1;
   const bool arow_valid = r < p.M;
+  const int64_t kb = p.k_pitch / 2, ks = p.k_pitch / 16;
+  // byte offsets of this lane's 16 code bytes and 2 scale bytes within a row, for phase q:
+  // chunk c = q * 8 + wave, codes at c * 64 + g * 16, scales at c * 8 + g * 2
+  const int cofs = wave * 64 + g * 16, sofs = wave * 8 + g * 2;
 
-  // all block scales of the weight rows and of the M activation rows, copied once (coalesced:
-  // 16-byte pieces of consecutive rows); older than every phase's instructions, so each phase's
-  // wait covers them
-  {
-    const int ks = p.k_pitch / 16, per_row = p.K / 256;  // row pitch; 16-byte pieces per row
+  // activation fragments (encoded form: straight from global memory, L2-resident after the first
+  // workgroup); rows >= M load the last row and are zeroed at decode
+  const int arow = min(r, p.M - 1);
+  uint4 aq[NPH];
+  uint32_t as2[NPH];
+  if constexpr (!kEncode) {
 #pragma unroll
-    for (int s = threadIdx.x; s < T * 16 * per_row; s += kSkinnyThreads) {
-      const int row = s / per_row;
-      const int grow = min(c0 + row, clast);
-      __builtin_amdgcn_global_load_lds(p.w_scales + (int64_t)grow * ks + (s - row * per_row) * 16,
-                                       wsc + (s & ~63) * 16, 16, 0, 0);
-    }
-    const int s = threadIdx.x;
-    if (s < p.M * per_row) {
-      const int row = s / per_row;
-      __builtin_amdgcn_global_load_lds(p.a_scales + (int64_t)row * ks + (s - row * per_row) * 16,
-                                       asc + (s & ~63) * 16, 16, 0, 0);
+    for (int q = 0; q < NPH; ++q) {
+      aq[q] = load16(p.a_codes + arow * kb + q * 512 + cofs);
+      as2[q] = load2(p.a_scales + arow * ks + q * 64 + sofs);
     }
   }
-  // global scales for the epilogue factors 1 / (gA * gW[seg(n)]) of this lane's columns: issued
-  // here as vector loads, older than every phase's copies (so the phase waits cover them), and
-  // used only at the end -- nothing waits on them before the weight stream is under way
-  int zero = 0;
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("" : "+v"(zero));  // a lane-varying index keeps the gA load a vector load
-#endif
-  const float ga = p.a_g[zero];
-  float gw[T];
-#pragma unroll
-  for (int tile = 0; tile < T; ++tile)
-    gw[tile] = p.seg_g[column_segment(p.seg, min(c0 + tile * 16 + r, clast))];
   __builtin_amdgcn_sched_barrier(0);
-
-  uint4 aw[8];  // entries >= NPH are never touched
+  // weight scales of every phase, then the weight codes phase by phase (rows past the workgroup's
+  // columns load its last column, never stored)
+  int wrow[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) wrow[t] = min(c0 + t * 16 + r, clast);
+  uint32_t ws2[NPH][T];
+#pragma unroll
+  for (int q = 0; q < NPH; ++q)
+#pragma unroll
+    for (int t = 0; t < T; ++t) ws2[q][t] = load2(p.w_scales + wrow[t] * ks + q * 64 + sofs);
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 wq[NPH][T];
 #pragma unroll
   for (int q = 0; q < NPH; ++q) {
-    switch (q) {  // compile-time after unrolling
-      case 0: issue_phase<0, T>(p, c0, clast, wave, lane, r, g, bufs0[0], bufs1[0], aw[0]); break;
-      case 1: issue_phase<1, T>(p, c0, clast, wave, lane, r, g, bufs0[1], bufs1[1], aw[1]); break;
-      case 2: issue_phase<2, T>(p, c0, clast, wave, lane, r, g, bufs0[2], bufs1[2], aw[2]); break;
-      case 3: issue_phase<3, T>(p, c0, clast, wave, lane, r, g, bufs0[3], bufs1[3], aw[3]); break;
-      case 4: issue_phase<4, T>(p, c0, clast, wave, lane, r, g, bufs0[4], bufs1[4], aw[4]); break;
-      case 5: issue_phase<5, T>(p, c0, clast, wave, lane, r, g, bufs0[5], bufs1[5], aw[5]); break;
-      case 6: issue_phase<6, T>(p, c0, clast, wave, lane, r, g, bufs0[6], bufs1[6], aw[6]); break;
-      default: issue_phase<7, T>(p, c0, clast, wave, lane, r, g, bufs0[7], bufs1[7], aw[7]); break;
+#pragma unroll
+    for (int t = 0; t < T; ++t) wq[q][t] = load16(p.w_codes + wrow[t] * kb + q * 512 + cofs);
+    __builtin_amdgcn_sched_barrier(0);  // keep the phases' loads in phase order
+  }
+  // global scales for the epilogue factors 1 / (gA * gW[seg(n)]), used only at the end
+  const float ga = p.a_g[0];
+  float gw[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) gw[t] = p.seg_g[column_segment(p.seg, wrow[t])];
+  __builtin_amdgcn_sched_barrier(0);
+
+  if constexpr (kEncode) {
+    uint8_t* const lcodes = act;
+    uint8_t* const lscales = act + 16 * (p.K / 2);
+    encode_activation<(nvfp4_dtype)XDT>(p, e, lcodes, lscales);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NPH; ++q) {
+      aq[q] = *reinterpret_cast<const uint4*>(lcodes + arow * (p.K / 2) + q * 512 + cofs);
+      as2[q] = *reinterpret_cast<const uint16_t*>(lscales + arow * (p.K / 16) + q * 64 + sofs);
     }
+  }
+
+  // decode every phase's activation fragment (the weights are still streaming in)
+  const uint32_t keep = arow_valid ? 0xFFFFFFFFu : 0u;  // padded rows contribute zeros
+  half8_t av[NPH][4];
+#pragma unroll
+  for (int q = 0; q < NPH; ++q) {
+    const half2_t sa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(as2[q] & keep, 1.0f, false);
+    const uint32_t w4[4] = {aq[q].x & keep, aq[q].y & keep, aq[q].z & keep, aq[q].w & keep};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) av[q][j] = decode8(w4[j], j < 2 ? sa[0] : sa[1]);
   }
 
   floatx4_t acc[T];
 #pragma unroll
-  for (int tile = 0; tile < T; ++tile) acc[tile] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  constexpr int V = kVmemPerPhase<T>;
+  for (int t = 0; t < T; ++t) acc[t] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int q = 0; q < NPH; ++q) {
-    // phase q has landed once only the later phases' instructions are outstanding
+    // phase q's weights: decode and contract (the compiler waits for exactly these loads)
     __builtin_amdgcn_sched_barrier(0);
-    switch (NPH - 1 - q) {
-      case 0: wait_vmcnt<0>(); break;
-      case 1: wait_vmcnt<1 * V>(); break;
-      case 2: wait_vmcnt<2 * V>(); break;
-      case 3: wait_vmcnt<3 * V>(); break;
-      case 4: wait_vmcnt<4 * V>(); break;
-      case 5: wait_vmcnt<5 * V>(); break;
-      case 6: wait_vmcnt<6 * V>(); break;
-      default: wait_vmcnt<7 * V>(); break;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const half2_t sw = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ws2[q][t], 1.0f, false);
+      const uint32_t w4[4] = {wq[q][t].x, wq[q][t].y, wq[q][t].z, wq[q][t].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const half8_t bv = decode8(w4[j], j < 2 ? sw[0] : sw[1]);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[q][j], bv, acc[t], 0, 0, 0);
+      }
     }
-    __builtin_amdgcn_s_barrier();  // every wavefront's copies of phase q have landed
-    __builtin_amdgcn_sched_barrier(0);
-    compute_phase<T>(bufs0[q], bufs1[q], wsc, asc, p.K / 16, q * (kPhaseK / 128) + wave, wave, r,
-                     g, arow_valid, aw[q], acc);
   }
 
   // deterministic reduction of the 8 partial tiles of each tile: wavefront `tile` adds the 8 in
   // order
 #pragma unroll
-  for (int tile = 0; tile < T; ++tile) partial[tile][wave][lane] = acc[tile];
+  for (int t = 0; t < T; ++t) partial[t][wave][lane] = acc[t];
   __syncthreads();
   if (wave >= T) return;
   floatx4_t sum = partial[wave][0][lane];
@@ -246,45 +203,78 @@ gemm_skinny_kernel(GemmArgs p, int ncols) {
   if (n >= cend) return;
   const float al = 1.0f / (ga * (wave == 0 ? gw[0] : gw[T - 1]));
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int m = 4 * g + e;
-    if (m < p.M) store_c(p.c, p.c_bf16, p.ldc, m, n, sum[e] * al);
+  for (int e4 = 0; e4 < 4; ++e4) {
+    const int m = 4 * g + e4;
+    if (m < p.M) store_c(p.c, p.c_bf16, p.ldc, m, n, sum[e4] * al);
   }
 }
 
 }  // namespace
 
-// One workgroup per compute unit when two tiles per workgroup suffice and fit in LDS (K up to
-// 7168): ncols = ceil(N / compute units) columns each, so every compute unit streams the same
-// number of weight bytes.  Otherwise tiles of 16 columns, one per workgroup.
-template <int NPH>
-hipError_t launch_skinny_nph(const GemmArgs& a, int cus, hipStream_t stream) {
+namespace {
+
+// One workgroup per compute unit: ncols = ceil(N / compute units) columns each (two tiles when
+// that is more than 16), so every compute unit streams the same number of weight bytes.
+template <int NPH, int XDT>
+hipError_t launch_skinny_nph(const GemmArgs& a, const DecodeEncode& e, int cus, hipStream_t stream) {
   const dim3 block(kSkinnyThreads);
   const int per_cu = (a.N + cus - 1) / cus;
-  if (NPH <= 7 && per_cu > 16) {
+  if (per_cu > 16) {
     const int ncols = per_cu <= 32 ? per_cu : 32;
     const dim3 grid((a.N + ncols - 1) / ncols);
-    hipLaunchKernelGGL((gemm_skinny_kernel<NPH, (NPH <= 7 ? 2 : 1)>), grid, block, 0, stream, a,
-                       ncols);
+    hipLaunchKernelGGL((gemm_skinny_kernel<NPH, 2, XDT>), grid, block, 0, stream, a, e, ncols);
   } else {
     const dim3 grid((a.N + 15) / 16);
-    hipLaunchKernelGGL((gemm_skinny_kernel<NPH, 1>), grid, block, 0, stream, a, 16);
+    hipLaunchKernelGGL((gemm_skinny_kernel<NPH, 1, XDT>), grid, block, 0, stream, a, e, 16);
   }
   return hipGetLastError();
 }
 
-static hipError_t launch_skinny_piece(const GemmArgs& a, int cus, hipStream_t stream) {
+template <int XDT>
+hipError_t launch_skinny_piece(const GemmArgs& a, const DecodeEncode& e, int cus, hipStream_t stream) {
   switch (a.K / kPhaseK) {
-    case 1: return launch_skinny_nph<1>(a, cus, stream);
-    case 2: return launch_skinny_nph<2>(a, cus, stream);
-    case 3: return launch_skinny_nph<3>(a, cus, stream);
-    case 4: return launch_skinny_nph<4>(a, cus, stream);
-    case 5: return launch_skinny_nph<5>(a, cus, stream);
-    case 6: return launch_skinny_nph<6>(a, cus, stream);
-    case 7: return launch_skinny_nph<7>(a, cus, stream);
-    case 8: return launch_skinny_nph<8>(a, cus, stream);
+    case 1: return launch_skinny_nph<1, XDT>(a, e, cus, stream);
+    case 2: return launch_skinny_nph<2, XDT>(a, e, cus, stream);
+    case 3: return launch_skinny_nph<3, XDT>(a, e, cus, stream);
+    case 4: return launch_skinny_nph<4, XDT>(a, e, cus, stream);
+    case 5: return launch_skinny_nph<5, XDT>(a, e, cus, stream);
+    case 6: return launch_skinny_nph<6, XDT>(a, e, cus, stream);
+    case 7: return launch_skinny_nph<7, XDT>(a, e, cus, stream);
+    case 8: return launch_skinny_nph<8, XDT>(a, e, cus, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t compute_units(int& cus) {
+  int dev = 0;
+  cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  cus = cus > 0 ? cus : 1;
+  return e;
+}
+
+}  // namespace
+
+bool skinny_one_pass(int64_t M, int64_t N, int64_t K) {
+  int cus = 0;
+  if (compute_units(cus) != hipSuccess) return false;
+  return M >= 1 && M <= 16 && K % kPhaseK == 0 && K <= kSkinnyMaxK && (N + cus - 1) / cus <= 32;
+}
+
+hipError_t launch_gemm_skinny_encode(const GemmArgs& a, const void* x, nvfp4_dtype x_dtype,
+                                     int64_t ldx, uint8_t* codes, uint8_t* scales,
+                                     hipStream_t stream) {
+  int cus = 0;
+  hipError_t e = compute_units(cus);
+  if (e != hipSuccess) return e;
+  const DecodeEncode de{x, ldx, codes, scales};
+  switch (x_dtype) {
+    case NVFP4_F32: return launch_skinny_piece<NVFP4_F32>(a, de, cus, stream);
+    case NVFP4_BF16: return launch_skinny_piece<NVFP4_BF16>(a, de, cus, stream);
+    case NVFP4_F16: return launch_skinny_piece<NVFP4_F16>(a, de, cus, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 // Decode-shaped products.  Up to 32 columns per compute unit and K up to kSkinnyMaxK: this
@@ -296,13 +286,12 @@ static hipError_t launch_skinny_piece(const GemmArgs& a, int cus, hipStream_t st
 // one pass at K = 17408, N = 5120: every piece meets the uneven share of 320 tiles among the
 // compute units again.)
 hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  int cus = 0;
+  hipError_t e = compute_units(cus);
   if (e != hipSuccess) return e;
-  cus = cus > 0 ? cus : 1;
   const int per_cu = (a.N + cus - 1) / cus;
-  if (a.K <= kSkinnyMaxK && per_cu <= 32) return launch_skinny_piece(a, cus, stream);
+  if (a.K <= kSkinnyMaxK && per_cu <= 32)
+    return launch_skinny_piece<-1>(a, DecodeEncode{nullptr, 0, nullptr, nullptr}, cus, stream);
   if (a.K <= kStreamMaxK) return launch_gemm_stream(a, stream);
   const int phases = a.K / kPhaseK;
   const int pieces = (phases + 7) / 8;

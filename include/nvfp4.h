@@ -171,6 +171,34 @@ nvfp4_status fused_nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                               int64_t K, void* c, nvfp4_dtype c_dtype, int64_t ldc, void* stream);
 
 /*
+ * nvfp4_linear -- the whole linear layer on a raw activation: encode x [M, K] to NVFP4 with the
+ * static (calibrated) global scale *a_gscale, exactly as nvfp4_quantize(..., dynamic = 0) does,
+ * writing its codes and scales to a_codes / a_scales, then form the fused product of those codes
+ * with the fused weight, exactly as fused_nvfp4_gemm does.
+ *
+ * Source: ai.info summary, "Methodology in Plain English" (activations quantized on the fly with
+ * calibrated scales; W4A4 on every linear layer) and "Main Findings" (decode is weight-bandwidth-
+ * bound; fused modules keep their own global scales).  For decode shapes (M <= 16, K a multiple of
+ * 1024 up to 8192, at most 32 output columns per compute unit) both steps run in one launch: every
+ * workgroup encodes the few activation rows itself while its weight bytes stream in, and one of
+ * them writes the codes out.  Other shapes run the encoder and the product as two launches.
+ *
+ *   x, x_dtype, ldx      device activation [M, K] (F32, BF16 or F16), as nvfp4_quantize's x.
+ *   a_gscale             device, one float: the static activation scale gA (read only).
+ *   a_codes, a_scales    device, [M, K/2] and [M, K/16] (pitches K/2, K/16): receive the codes and
+ *                        scales nvfp4_quantize would write; 16-byte aligned.
+ *   w_codes .. stream    as fused_nvfp4_gemm.
+ * Results: a_codes / a_scales bit-identical to nvfp4_quantize's; C bit-identical to
+ * fused_nvfp4_gemm on those codes.  Errors as nvfp4_quantize and fused_nvfp4_gemm; the checks of
+ * both run before any launch.
+ */
+nvfp4_status nvfp4_linear(const void* x, nvfp4_dtype x_dtype, int64_t ldx, const float* a_gscale,
+                          uint8_t* a_codes, uint8_t* a_scales, const uint8_t* w_codes,
+                          const uint8_t* w_scales, const float* seg_gscale,
+                          const int64_t* seg_offsets, int nseg, int64_t M, int64_t N, int64_t K,
+                          void* c, nvfp4_dtype c_dtype, int64_t ldc, void* stream);
+
+/*
  * nvfp4_fake_quantize -- out = dequantize(quantize(x)): the NVFP4 rounding error injected into a
  * high-precision tensor, without storing codes.
  *

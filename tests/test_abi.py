@@ -159,6 +159,35 @@ def test_gemm_validation(fused):
     assert _g(fused, M=0, ga=None) == E.NVFP4_EINVAL  # global scales are always required
 
 
+def _lin(**kw):
+    a = dict(x=P, xdt=nv.NVFP4_BF16, ldx=512, ga=P, ac=P, as_=P, wc=P, ws=P, gw=P, offs=None,
+             nseg=None, M=4, N=96, K=512, c=P, cdt=nv.NVFP4_F32, ldc=96, s=None)
+    a.update(kw)
+    offs = a["offs"] if a["offs"] is not None else [0, a["N"]]
+    nseg = a["nseg"] if a["nseg"] is not None else len(offs) - 1
+    arr = (ctypes.c_int64 * max(len(offs), 1))(*offs)
+    return nv.load_library().nvfp4_linear(a["x"], a["xdt"], a["ldx"], a["ga"], a["ac"], a["as_"],
+                                          a["wc"], a["ws"], a["gw"], arr, nseg, a["M"], a["N"],
+                                          a["K"], a["c"], a["cdt"], a["ldc"], a["s"])
+
+
+def test_linear_validation():
+    """nvfp4_linear checks the activation as nvfp4_quantize does and the product as
+    fused_nvfp4_gemm does, before any launch."""
+    E = nv
+    for k in ("x", "ga", "ac", "as_", "wc", "ws", "gw", "c"):
+        assert _lin(**{k: None}) == E.NVFP4_EINVAL, k
+    assert _lin(xdt=7) == E.NVFP4_EINVAL
+    assert _lin(cdt=E.NVFP4_F16) == E.NVFP4_EINVAL
+    assert _lin(ldx=500) == E.NVFP4_ESHAPE  # row pitch below K
+    assert _lin(K=40, ldx=40) == E.NVFP4_ESHAPE
+    assert _lin(offs=[0, 32, 95]) == E.NVFP4_ESHAPE
+    assert _lin(x=P + 8) == E.NVFP4_EALIGN
+    assert _lin(ldx=516) == E.NVFP4_EALIGN  # 1032-byte bf16 rows are not 16-byte multiples
+    assert _lin(ac=P + 8) == E.NVFP4_EALIGN
+    assert _lin(M=0, x=None, ac=None, as_=None, c=None) == E.NVFP4_OK  # empty: nothing enqueued
+
+
 def test_fused_segment_validation():
     E = nv
     assert _g(True, offs=[0, 32, 96], nseg=0) == E.NVFP4_EINVAL
