@@ -348,7 +348,7 @@ nvfp4_status nvfp4_linear(const void* x, nvfp4_dtype x_dtype, int64_t ldx, const
   if (M == 0) return NVFP4_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (N > 0 && nvfp4::choose_gemm_path(M, K, c_dtype == NVFP4_BF16) == nvfp4::GemmPath::Skinny &&
-      nvfp4::skinny_one_pass(M, N, K)) {
+      nvfp4::skinny_one_pass(M, N, K, x_dtype)) {
     nvfp4::GemmArgs a = gemm_args(a_codes, a_scales, a_gscale, w_codes, w_scales, seg_gscale,
                                   seg_offsets, nseg, M, N, K, c, c_dtype, ldc);
     return device_status(

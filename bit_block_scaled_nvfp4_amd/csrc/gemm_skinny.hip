@@ -60,28 +60,70 @@ __device__ __forceinline__ uint32_t load2(const uint8_t* p) {
 }
 
 // Encode activation rows [0, M) x [0, K) with the static scale *a_g into LDS (codes [M][K/2], scales
-// [M][K/16]), one 16-element block per thread and step; workgroup 0 also writes them to `e`.
+// [M][K/16]) with the encoder's block routine, blocks spread over the workgroup's threads; workgroup
+// 0 also writes them to `e`.  Each thread keeps the loads of its next batch of blocks in flight
+// while it encodes the current one, so the activation's load latency is paid once, not per block.
 template <nvfp4_dtype XDT>
 __device__ __forceinline__ void encode_activation(const GemmArgs& p, const DecodeEncode& e,
                                                   uint8_t* lcodes, uint8_t* lscales) {
+  constexpr int B = 4;                                     // blocks per thread and batch
+  constexpr int W = 4 * codec::elem_bytes<XDT>();          // 32-bit words per block
   const float g = __builtin_nontemporal_load(p.a_g);
   const float gs6 = g / 6.0f;
   const int bpr = p.K / 16;  // blocks per row
+  const int nblk = p.M * bpr;
   const bool out = blockIdx.x == 0 && e.codes != nullptr;
-  for (int b = threadIdx.x; b < p.M * bpr; b += kSkinnyThreads) {
-    const int row = b / bpr, blk = b - row * bpr;
-    float v[16];
-    codec::load_block<XDT>(reinterpret_cast<const uint8_t*>(e.x) +
-                               ((int64_t)row * e.ldx + (int64_t)blk * 16) * codec::elem_bytes<XDT>(),
-                           v);
-    uint32_t word[2];
-    const uint32_t sc = codec::encode_codes(v, g, gs6, word);
-    *reinterpret_cast<uint2*>(lcodes + b * 8) = uint2{word[0], word[1]};
-    lscales[b] = (uint8_t)sc;
-    if (out) {
-      *reinterpret_cast<uint2*>(e.codes + (int64_t)b * 8) = uint2{word[0], word[1]};
-      e.scales[b] = (uint8_t)sc;
+  const uint8_t* const xb = reinterpret_cast<const uint8_t*>(e.x);
+  auto load = [&](int base, uint32_t (&raw)[B][W]) {
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int b = min(base + j * kSkinnyThreads + (int)threadIdx.x, nblk - 1);
+      const int row = b / bpr, blk = b - row * bpr;
+      const uint8_t* src = xb + ((int64_t)row * e.ldx + (int64_t)blk * 16) * codec::elem_bytes<XDT>();
+#pragma unroll
+      for (int i = 0; i < W / 4; ++i) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src + 16 * i);
+        raw[j][4 * i] = v.x;
+        raw[j][4 * i + 1] = v.y;
+        raw[j][4 * i + 2] = v.z;
+        raw[j][4 * i + 3] = v.w;
+      }
     }
+  };
+  uint32_t cur[B][W], nxt[B][W];
+  load(0, cur);
+  for (int base = 0; base < nblk; base += B * kSkinnyThreads) {
+    if (base + B * kSkinnyThreads < nblk) load(base + B * kSkinnyThreads, nxt);
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int b = base + j * kSkinnyThreads + (int)threadIdx.x;
+      if (b >= nblk) continue;
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if constexpr (XDT == NVFP4_F32) {
+          v[i] = __uint_as_float(cur[j][i]);
+        } else if constexpr (XDT == NVFP4_BF16) {
+          const uint32_t w2 = cur[j][i / 2];
+          v[i] = __uint_as_float((i & 1) ? (w2 & 0xFFFF0000u) : (w2 << 16));
+        } else {
+          const uint32_t w2 = cur[j][i / 2];
+          v[i] = (float)__builtin_bit_cast(_Float16, (uint16_t)((i & 1) ? (w2 >> 16) : (w2 & 0xFFFFu)));
+        }
+      }
+      uint32_t word[2];
+      const uint32_t sc = codec::encode_codes(v, g, gs6, word);
+      *reinterpret_cast<uint2*>(lcodes + b * 8) = uint2{word[0], word[1]};
+      lscales[b] = (uint8_t)sc;
+      if (out) {
+        *reinterpret_cast<uint2*>(e.codes + (int64_t)b * 8) = uint2{word[0], word[1]};
+        e.scales[b] = (uint8_t)sc;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+#pragma unroll
+      for (int i = 0; i < W; ++i) cur[j][i] = nxt[j][i];
   }
 }
 
@@ -230,17 +272,22 @@ hipError_t launch_skinny_nph(const GemmArgs& a, const DecodeEncode& e, int cus, 
   return hipGetLastError();
 }
 
+// Phases of K the one-launch encoding form takes for an f32 activation (its encode batches hold
+// twice the registers of a 16-bit one's): at most 5.
+constexpr int kEncodeF32MaxPhases = 5;
+
 template <int XDT>
 hipError_t launch_skinny_piece(const GemmArgs& a, const DecodeEncode& e, int cus, hipStream_t stream) {
+  constexpr bool f32enc = XDT == NVFP4_F32;
   switch (a.K / kPhaseK) {
     case 1: return launch_skinny_nph<1, XDT>(a, e, cus, stream);
     case 2: return launch_skinny_nph<2, XDT>(a, e, cus, stream);
     case 3: return launch_skinny_nph<3, XDT>(a, e, cus, stream);
     case 4: return launch_skinny_nph<4, XDT>(a, e, cus, stream);
     case 5: return launch_skinny_nph<5, XDT>(a, e, cus, stream);
-    case 6: return launch_skinny_nph<6, XDT>(a, e, cus, stream);
-    case 7: return launch_skinny_nph<7, XDT>(a, e, cus, stream);
-    case 8: return launch_skinny_nph<8, XDT>(a, e, cus, stream);
+    case 6: return f32enc ? hipErrorInvalidValue : launch_skinny_nph<(f32enc ? 1 : 6), XDT>(a, e, cus, stream);
+    case 7: return f32enc ? hipErrorInvalidValue : launch_skinny_nph<(f32enc ? 1 : 7), XDT>(a, e, cus, stream);
+    case 8: return f32enc ? hipErrorInvalidValue : launch_skinny_nph<(f32enc ? 1 : 8), XDT>(a, e, cus, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -256,9 +303,10 @@ hipError_t compute_units(int& cus) {
 
 }  // namespace
 
-bool skinny_one_pass(int64_t M, int64_t N, int64_t K) {
+bool skinny_one_pass(int64_t M, int64_t N, int64_t K, int x_dtype) {
   int cus = 0;
   if (compute_units(cus) != hipSuccess) return false;
+  if (x_dtype == NVFP4_F32 && K > kEncodeF32MaxPhases * kPhaseK) return false;
   return M >= 1 && M <= 16 && K % kPhaseK == 0 && K <= kSkinnyMaxK && (N + cus - 1) / cus <= 32;
 }
 

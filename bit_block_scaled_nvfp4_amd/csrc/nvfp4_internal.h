@@ -70,11 +70,12 @@ hipError_t launch_kv_load(const uint8_t* cache, int64_t num_slots, int64_t cache
 hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_general(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);
-// Whether the one-pass decode kernel serves an M x N x K product (M <= 16, K a multiple of 1024 up
-// to kSkinnyMaxK, at most 32 columns per compute unit), and that kernel in its encoding form: the
-// raw activation x [M, K] (row pitch ldx elements) is encoded with the static scale *a.a_g inside
-// the launch; the codes and scales go to `codes` / `scales` (row pitch K/2, K/16).
-bool skinny_one_pass(int64_t M, int64_t N, int64_t K);
+// Whether the one-pass decode kernel's encoding form serves an M x N x K product on an activation
+// of type x_dtype (M <= 16, K a multiple of 1024 up to kSkinnyMaxK -- 5120 for f32 --, at most 32
+// columns per compute unit), and that kernel: the raw activation x [M, K] (row pitch ldx elements)
+// is encoded with the static scale *a.a_g inside the launch; the codes and scales go to `codes` /
+// `scales` (row pitch K/2, K/16).
+bool skinny_one_pass(int64_t M, int64_t N, int64_t K, int x_dtype);
 hipError_t launch_gemm_skinny_encode(const GemmArgs& a, const void* x, nvfp4_dtype x_dtype,
                                      int64_t ldx, uint8_t* codes, uint8_t* scales,
                                      hipStream_t stream);

@@ -48,7 +48,7 @@ hipError_t launch_gemm_tiled(const GemmArgs&, hipStream_t) { return hipSuccess; 
 hipError_t launch_gemm_general(const GemmArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_gemm_skinny(const GemmArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_gemm_stream(const GemmArgs&, hipStream_t) { return hipSuccess; }
-bool skinny_one_pass(int64_t M, int64_t N, int64_t K) {
+bool skinny_one_pass(int64_t M, int64_t N, int64_t K, int) {
   return M >= 1 && M <= 16 && K % 1024 == 0 && K <= kSkinnyMaxK && N <= 32 * 256;
 }
 hipError_t launch_gemm_skinny_encode(const GemmArgs&, const void*, nvfp4_dtype, int64_t, uint8_t*,
