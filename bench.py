@@ -251,7 +251,41 @@ def decode(args, torch, nv, W):
                                    "GB/s": round(lbytes / (lk_ms * 1e-3) / 1e9, 1),
                                    "bytes": lbytes, "launches": 1}}
     res["copy_ceiling"] = _copy_ceiling(torch, copies, R)
+    res["read_ceiling"] = _read_ceiling(torch, copies, R)
     return res
+
+
+def _read_ceiling(torch, copies, R):
+    """A vendor read of one decode weight's bytes: torch's row-wise max over the codes and the scales
+    viewed as int64 (one output per row, so nothing is written but 5120 values per tensor and no
+    reduction spans workgroups), the R rotated copies replayed back to back from a HIP graph, total
+    / R.  It reads what the decode product reads, with no decode or product."""
+    rows = copies[0][0].shape[0]
+    outs = []
+    for wc, ws in copies:
+        torch.amax(wc.view(torch.int64), dim=1)
+        torch.amax(ws.view(torch.int64), dim=1)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for wc, ws in copies:
+            outs.append(torch.amax(wc.view(torch.int64), dim=1))
+            outs.append(torch.amax(ws.view(torch.int64), dim=1))
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * R)
+    del graph, outs
+    nbytes = copies[0][0].numel() + copies[0][1].numel()
+    return {"us_per_weight": round(ms * 1e3, 3), "bytes_read": nbytes, "rows": rows,
+            "read_GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "note": "vendor row-wise max over the codes and the scales (two kernels per weight)"}
 
 
 def _copy_ceiling(torch, copies, R):

@@ -154,23 +154,29 @@ __device__ __forceinline__ void row_offsets(const GemmArgs& p, int m0, int n0, i
 template <class Cfg>
 __device__ __forceinline__ void issue_chunk(const GemmArgs& p, const RowOffsets<Cfg>& o, int kc,
                                             uint8_t* stage) {
-  const int wave_slot = (threadIdx.x >> 6) * 64;
+  // the wavefront's first copy slot and the chunk's global base are uniform: scalar registers, so
+  // each copy is a scalar base plus this lane's 32-bit row offset
+  const int wave_slot = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * 64;
+  const uint8_t* const ac = p.a_codes + kc * 32;
+  const uint8_t* const wc = p.w_codes + kc * 32;
+  const uint8_t* const as = p.a_scales + kc * 4;
+  const uint8_t* const ws = p.w_scales + kc * 4;
 #pragma unroll
   for (int i = 0; i < Cfg::kPiecesA; ++i)
     if ((i + 1) * Cfg::kThreads <= Cfg::BM * 2 || i * Cfg::kThreads + wave_slot < Cfg::BM * 2)
-      __builtin_amdgcn_global_load_lds(p.a_codes + o.a[i] + kc * 32,
-                                       stage + (i * Cfg::kThreads + wave_slot) * 16, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(ac + o.a[i], stage + (i * Cfg::kThreads + wave_slot) * 16,
+                                       16, 0, 0);
 #pragma unroll
   for (int i = 0; i < Cfg::kPiecesB; ++i)
     if ((i + 1) * Cfg::kThreads <= Cfg::BN * 2 || i * Cfg::kThreads + wave_slot < Cfg::BN * 2)
-      __builtin_amdgcn_global_load_lds(p.w_codes + o.b[i] + kc * 32,
+      __builtin_amdgcn_global_load_lds(wc + o.b[i],
                                        stage + Cfg::kCodesA + (i * Cfg::kThreads + wave_slot) * 16,
                                        16, 0, 0);
 #pragma unroll
   for (int i = 0; i < Cfg::kWordsA; ++i)
     if ((i + 1) * Cfg::kThreads * 4 <= Cfg::kScalesA ||
         (i * Cfg::kThreads + wave_slot) * 4 < Cfg::kScalesA)
-      __builtin_amdgcn_global_load_lds(p.a_scales + o.sa[i] + kc * 4,
+      __builtin_amdgcn_global_load_lds(as + o.sa[i],
                                        stage + Cfg::kCodesA + Cfg::kCodesB +
                                            (i * Cfg::kThreads + wave_slot) * 4,
                                        4, 0, 0);
@@ -178,7 +184,7 @@ __device__ __forceinline__ void issue_chunk(const GemmArgs& p, const RowOffsets<
   for (int i = 0; i < Cfg::kWordsB; ++i)
     if ((i + 1) * Cfg::kThreads * 4 <= Cfg::kScalesB ||
         (i * Cfg::kThreads + wave_slot) * 4 < Cfg::kScalesB)
-      __builtin_amdgcn_global_load_lds(p.w_scales + o.sb[i] + kc * 4,
+      __builtin_amdgcn_global_load_lds(ws + o.sb[i],
                                        stage + Cfg::kCodesA + Cfg::kCodesB + Cfg::kScalesA +
                                            (i * Cfg::kThreads + wave_slot) * 4,
                                        4, 0, 0);
