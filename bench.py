@@ -250,75 +250,90 @@ def decode(args, torch, nv, W):
                                    "call_us": round(lcall_ms * 1e3, 3),
                                    "GB/s": round(lbytes / (lk_ms * 1e-3) / 1e9, 1),
                                    "bytes": lbytes, "launches": 1}}
-    res["copy_ceiling"] = _copy_ceiling(torch, copies, R)
-    res["read_ceiling"] = _read_ceiling(torch, copies, R)
+    res["ceilings"] = _decode_ceilings(torch, copies, R)
     return res
 
 
-def _read_ceiling(torch, copies, R):
-    """A vendor read of one decode weight's bytes: torch's row-wise max over the codes and the scales
-    viewed as int64 (one output per row, so nothing is written but 5120 values per tensor and no
-    reduction spans workgroups), the R rotated copies replayed back to back from a HIP graph, total
-    / R.  It reads what the decode product reads, with no decode or product."""
-    rows = copies[0][0].shape[0]
-    outs = []
-    for wc, ws in copies:
-        torch.amax(wc.view(torch.int64), dim=1)
-        torch.amax(ws.view(torch.int64), dim=1)
+def _graph_us(torch, launch, R, reps=20):
+    """`launch(i)` for i = 0..R-1 captured in one HIP graph and replayed `reps` times back to back:
+    microseconds per i."""
+    for i in range(R):
+        launch(i)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        for wc, ws in copies:
-            outs.append(torch.amax(wc.view(torch.int64), dim=1))
-            outs.append(torch.amax(ws.view(torch.int64), dim=1))
+        for i in range(R):
+            launch(i)
     graph.replay()
     torch.cuda.synchronize()
-    reps = 20
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
         graph.replay()
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / (reps * R)
-    del graph, outs
+    us = e0.elapsed_time(e1) * 1e3 / (reps * R)
+    del graph
+    return us
+
+
+def _ceiling_lib():
+    """The benchmark's reference kernels (a plain read in the decode kernel's launch shape, and an
+    empty launch), built beside libnvfp4.so."""
+    import ctypes
+
+    path = os.path.join(ROOT, "bit_block_scaled_nvfp4_amd", "libnvfp4_ceiling.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    c_vp, c_i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.nvfp4_ceiling_stream_read.argtypes = [c_vp, c_i64, c_vp, c_i64, c_vp, ctypes.c_int, c_vp]
+    lib.nvfp4_ceiling_stream_read.restype = ctypes.c_int
+    lib.nvfp4_ceiling_empty_launch.argtypes = [c_vp]
+    lib.nvfp4_ceiling_empty_launch.restype = ctypes.c_int
+    return lib
+
+
+def _decode_ceilings(torch, copies, R):
+    """What the hardware gives for one decode weight at this size, each over the same R rotated
+    copies from a HIP graph like the product:
+    ``read``: a plain read of the weight's codes and scales (14.75 MB) in the decode kernel's launch
+    shape (one workgroup of 512 lanes per compute unit, 16-byte loads, all in flight), folded to one
+    word per wavefront -- the bytes the product reads, with no decode, product or output;
+    ``empty_launch``: a kernel that does nothing, the fixed cost of one launch in a graph;
+    ``vendor_copy``: torch's device copy of the codes and of the scales (reads and writes them)."""
+    lib = _ceiling_lib()
+    dev = copies[0][0].device
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(cus * 8, dtype=torch.int32, device=dev)
     nbytes = copies[0][0].numel() + copies[0][1].numel()
-    return {"us_per_weight": round(ms * 1e3, 3), "bytes_read": nbytes, "rows": rows,
-            "read_GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
-            "note": "vendor row-wise max over the codes and the scales (two kernels per weight)"}
 
+    def read(i):
+        wc, ws = copies[i]
+        st = lib.nvfp4_ceiling_stream_read(wc.data_ptr(), wc.numel(), ws.data_ptr(), ws.numel(),
+                                           out.data_ptr(), cus, torch.cuda.current_stream().cuda_stream)
+        assert st == 0, st
 
-def _copy_ceiling(torch, copies, R):
-    """The measured ceiling for streaming one decode weight: the vendor device copy of the same
-    14.75 MB (codes and scales of one 5120 x 5120 weight) from each of the R rotated copies into one
-    destination, replayed back to back from a HIP graph, total / R.  A copy reads and writes the
-    bytes; the decode product reads them once."""
+    def empty(i):
+        st = lib.nvfp4_ceiling_empty_launch(torch.cuda.current_stream().cuda_stream)
+        assert st == 0, st
+
     dst_c = torch.empty_like(copies[0][0])
     dst_s = torch.empty_like(copies[0][1])
-    for wc, ws in copies:
-        dst_c.copy_(wc)
-        dst_s.copy_(ws)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for wc, ws in copies:
-            dst_c.copy_(wc)
-            dst_s.copy_(ws)
-    graph.replay()
-    torch.cuda.synchronize()
-    reps = 20
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / (reps * R)
-    del graph
-    nbytes = copies[0][0].numel() + copies[0][1].numel()
-    return {"us_per_weight": round(ms * 1e3, 3), "bytes_read": nbytes,
-            "read_GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
-            "note": "vendor device copy of one weight's codes and scales (two copies per weight)"}
+
+    def copy(i):
+        dst_c.copy_(copies[i][0])
+        dst_s.copy_(copies[i][1])
+
+    r_us = _graph_us(torch, read, R)
+    e_us = _graph_us(torch, empty, R)
+    c_us = _graph_us(torch, copy, R)
+    return {"bytes_read": nbytes,
+            "read": {"us_per_weight": round(r_us, 3), "read_GB/s": round(nbytes / r_us / 1e3, 1),
+                     "workgroups": cus},
+            "empty_launch_us": round(e_us, 3),
+            "vendor_copy": {"us_per_weight": round(c_us, 3), "read_GB/s": round(nbytes / c_us / 1e3, 1),
+                            "launches": 2}}
 
 
 def decode_mlp(args, torch, nv, W):

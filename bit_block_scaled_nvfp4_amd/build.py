@@ -18,6 +18,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libnvfp4.so")
+# reference kernels the benchmark times beside the decode product (not part of the product's ABI)
+CEILING_SRC = "ceiling.hip"
+CEILING_LIB = os.path.join(PKG, "libnvfp4_ceiling.so")
 
 SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "gemm_skinny.hip", "gemm_stream.hip", "kv_cache.hip",
            "fake_quant.hip"]
@@ -64,7 +67,8 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
-    """Compile every source for gfx950 and link libnvfp4.so; return its path."""
+    """Compile every source for gfx950, link libnvfp4.so (and the benchmark's reference kernels,
+    libnvfp4_ceiling.so); return the path of libnvfp4.so."""
     hipcc = _hipcc()
     os.makedirs(BUILD, exist_ok=True)
     flags = HIPCC_FLAGS + list(extra_flags or [])
@@ -74,11 +78,14 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         cmds.append([hipcc, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
+    ceil_obj = os.path.join(BUILD, os.path.splitext(CEILING_SRC)[0] + ".o")
+    cmds.append([hipcc, *flags, "-c", os.path.join(CSRC, CEILING_SRC), "-o", ceil_obj])
     with ThreadPoolExecutor(max_workers=min(len(cmds), 4)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB)
+    for lib, lib_objs in ((LIB, objs), (CEILING_LIB, [ceil_obj])):
+        tmp = lib + ".tmp"
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *lib_objs], verbose)
+        os.replace(tmp, lib)
     return LIB
 
 

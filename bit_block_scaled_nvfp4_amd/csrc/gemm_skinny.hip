@@ -16,9 +16,13 @@
 // MFMA step j (j = 0..3), inside 16-blocks 2g and 2g + 1 (two scale bytes).  Both operands use this
 // map.  So a wavefront's weight load of one tile and phase reads 16 rows x 64 contiguous bytes, the
 // eight wavefronts together 16 rows x 512 bytes, straight into registers: no LDS staging and no
-// workgroup barrier while the weights stream.  All loads of the launch are issued up front, the
-// activation's first (small, and the same for every workgroup, so served from L2), then the weight
-// scales, then the weight codes phase by phase.  The activation fragments of all phases are decoded
+// workgroup barrier while the weights stream.  The weight scales are loaded 8 bytes per lane (a
+// wavefront's chunk of one row holds the scale bytes of all four k groups): lane (r, g) loads those
+// of phases g and 4 + g, and each lane then fetches phase q's word from lane (q % 4) * 16 + r with a
+// cross-lane permute, so a tile's scales take one or two load instructions instead of one per
+// phase.  All loads of the launch are issued up front, the activation's first (small, and the same
+// for every workgroup, so served from L2), then the weight scales, then the weight codes phase by
+// phase.  The activation fragments of all phases are decoded
 // to f16 while the weights are in flight, so once phase q's weights land only their decode and the
 // MFMAs remain.  Rows of the activation at or past M are zero.
 //
@@ -58,6 +62,7 @@ __device__ __forceinline__ uint4 load16(const uint8_t* p) {
 __device__ __forceinline__ uint32_t load2(const uint8_t* p) {
   return *reinterpret_cast<const uint16_t*>(p);
 }
+__device__ __forceinline__ uint2 load8(const uint8_t* p) { return *reinterpret_cast<const uint2*>(p); }
 
 // Encode activation rows [0, M) x [0, K) with the static scale *a_g into LDS (codes [M][K/2], scales
 // [M][K/16]) with the encoder's block routine, blocks spread over the workgroup's threads; workgroup
@@ -168,11 +173,16 @@ gemm_skinny_kernel(GemmArgs p, DecodeEncode e, int ncols) {
   int wrow[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) wrow[t] = min(c0 + t * 16 + r, clast);
-  uint32_t ws2[NPH][T];
+  // weight scales: lane (r, g) loads the 8 scale bytes of this wavefront's chunk of row r (those of
+  // all four k groups) for phases g and 4 + g, so one load per tile covers four phases; each lane
+  // later fetches phase q's bytes from lane (q % 4) * 16 + r and keeps its own two
+  constexpr int kSq = (NPH + 3) / 4;
+  uint2 sq[kSq][T];
 #pragma unroll
-  for (int q = 0; q < NPH; ++q)
+  for (int i = 0; i < kSq; ++i)
 #pragma unroll
-    for (int t = 0; t < T; ++t) ws2[q][t] = load2(p.w_scales + wrow[t] * ks + q * 64 + sofs);
+    for (int t = 0; t < T; ++t)
+      sq[i][t] = load8(p.w_scales + wrow[t] * ks + min(4 * i + g, NPH - 1) * 64 + wave * 8);
   __builtin_amdgcn_sched_barrier(0);
   uint4 wq[NPH][T];
 #pragma unroll
@@ -210,6 +220,18 @@ gemm_skinny_kernel(GemmArgs p, DecodeEncode e, int ncols) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) av[q][j] = decode8(w4[j], j < 2 ? sa[0] : sa[1]);
   }
+
+  // this lane's two weight scale bytes of every phase and tile (low half of ws2)
+  uint32_t ws2[NPH][T];
+#pragma unroll
+  for (int q = 0; q < NPH; ++q)
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int src = ((q & 3) * 16 + r) * 4;
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)sq[q >> 2][t].x);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)sq[q >> 2][t].y);
+      ws2[q][t] = ((g & 2) ? hi : lo) >> ((g & 1) * 16);
+    }
 
   floatx4_t acc[T];
 #pragma unroll

@@ -62,6 +62,27 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name)
 
 
+def test_benchmark_reference_library_exports_its_two_kernels():
+    """The benchmark's reference kernels (a plain read and an empty launch) are built beside the
+    product library, outside its ABI: the product library exports neither."""
+    path = os.path.join(os.path.dirname(nv.LIB_PATH), "libnvfp4_ceiling.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert {"nvfp4_ceiling_stream_read", "nvfp4_ceiling_empty_launch"} <= exported
+    lib = ctypes.CDLL(path)
+    lib.nvfp4_ceiling_stream_read.restype = ctypes.c_int
+    lib.nvfp4_ceiling_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                              ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                              ctypes.c_void_p]
+    # rejected on the host before any HIP call: sizes that are not whole 16-byte pieces, no blocks
+    assert lib.nvfp4_ceiling_stream_read(None, 8, None, 0, ctypes.c_void_p(16), 1, None) != 0
+    assert lib.nvfp4_ceiling_stream_read(None, 0, None, 0, ctypes.c_void_p(16), 0, None) != 0
+    prod = subprocess.run(["nm", "-D", "--defined-only", nv.LIB_PATH], capture_output=True,
+                          text=True, check=True).stdout
+    assert "nvfp4_ceiling" not in prod
+
+
 def test_status_strings_and_version():
     for s in range(5):
         assert nv.status_string(s).startswith("NVFP4")
