@@ -64,41 +64,55 @@ __device__ __forceinline__ uint32_t load2(const uint8_t* p) {
 }
 __device__ __forceinline__ uint2 load8(const uint8_t* p) { return *reinterpret_cast<const uint2*>(p); }
 
-// Encode activation rows [0, M) x [0, K) with the static scale *a_g into LDS (codes [M][K/2], scales
-// [M][K/16]) with the encoder's block routine, blocks spread over the workgroup's threads; workgroup
-// 0 also writes them to `e`.  Each thread keeps the loads of its next batch of blocks in flight
-// while it encodes the current one, so the activation's load latency is paid once, not per block.
+// The encoding form's activation loads: B blocks per thread and batch, 32-bit words per block.
+constexpr int kEncodeBatch = 4;
 template <nvfp4_dtype XDT>
-__device__ __forceinline__ void encode_activation(const GemmArgs& p, const DecodeEncode& e,
-                                                  uint8_t* lcodes, uint8_t* lscales) {
-  constexpr int B = 4;                                     // blocks per thread and batch
-  constexpr int W = 4 * codec::elem_bytes<XDT>();          // 32-bit words per block
-  const float g = __builtin_nontemporal_load(p.a_g);
-  const float gs6 = g / 6.0f;
+constexpr int encode_words() {
+  return 4 * codec::elem_bytes<XDT>();
+}
+
+// Load batch `base` (blocks base + j * threads + thread, j < B, clamped to the last block) of the
+// raw activation into registers.
+template <nvfp4_dtype XDT>
+__device__ __forceinline__ void encode_load(const GemmArgs& p, const DecodeEncode& e, int base,
+                                            uint32_t (&raw)[kEncodeBatch][encode_words<XDT>()]) {
+  constexpr int W = encode_words<XDT>();
   const int bpr = p.K / 16;  // blocks per row
   const int nblk = p.M * bpr;
-  const bool out = blockIdx.x == 0 && e.codes != nullptr;
   const uint8_t* const xb = reinterpret_cast<const uint8_t*>(e.x);
-  auto load = [&](int base, uint32_t (&raw)[B][W]) {
 #pragma unroll
-    for (int j = 0; j < B; ++j) {
-      const int b = min(base + j * kSkinnyThreads + (int)threadIdx.x, nblk - 1);
-      const int row = b / bpr, blk = b - row * bpr;
-      const uint8_t* src = xb + ((int64_t)row * e.ldx + (int64_t)blk * 16) * codec::elem_bytes<XDT>();
+  for (int j = 0; j < kEncodeBatch; ++j) {
+    const int b = min(base + j * kSkinnyThreads + (int)threadIdx.x, nblk - 1);
+    const int row = b / bpr, blk = b - row * bpr;
+    const uint8_t* src = xb + ((int64_t)row * e.ldx + (int64_t)blk * 16) * codec::elem_bytes<XDT>();
 #pragma unroll
-      for (int i = 0; i < W / 4; ++i) {
-        const uint4 v = *reinterpret_cast<const uint4*>(src + 16 * i);
-        raw[j][4 * i] = v.x;
-        raw[j][4 * i + 1] = v.y;
-        raw[j][4 * i + 2] = v.z;
-        raw[j][4 * i + 3] = v.w;
-      }
+    for (int i = 0; i < W / 4; ++i) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src + 16 * i);
+      raw[j][4 * i] = v.x;
+      raw[j][4 * i + 1] = v.y;
+      raw[j][4 * i + 2] = v.z;
+      raw[j][4 * i + 3] = v.w;
     }
-  };
-  uint32_t cur[B][W], nxt[B][W];
-  load(0, cur);
+  }
+}
+
+// Encode activation rows [0, M) x [0, K) with the static scale g into LDS (codes [M][K/2], scales
+// [M][K/16]) with the encoder's block routine, blocks spread over the workgroup's threads; workgroup
+// 0 also writes them to `e`.  `cur` holds the first batch, loaded by the caller before the weight
+// loads so that encoding it waits for nothing else; each later batch is loaded while the one
+// before it is encoded.
+template <nvfp4_dtype XDT>
+__device__ __forceinline__ void encode_activation(const GemmArgs& p, const DecodeEncode& e, float g,
+                                                  uint32_t (&cur)[kEncodeBatch][encode_words<XDT>()],
+                                                  uint8_t* lcodes, uint8_t* lscales) {
+  constexpr int B = kEncodeBatch;
+  constexpr int W = encode_words<XDT>();
+  const float gs6 = g / 6.0f;
+  const int nblk = p.M * (p.K / 16);
+  const bool out = blockIdx.x == 0 && e.codes != nullptr;
+  uint32_t nxt[B][W];
   for (int base = 0; base < nblk; base += B * kSkinnyThreads) {
-    if (base + B * kSkinnyThreads < nblk) load(base + B * kSkinnyThreads, nxt);
+    if (base + B * kSkinnyThreads < nblk) encode_load<XDT>(p, e, base + B * kSkinnyThreads, nxt);
 #pragma unroll
     for (int j = 0; j < B; ++j) {
       const int b = base + j * kSkinnyThreads + (int)threadIdx.x;
@@ -167,6 +181,15 @@ gemm_skinny_kernel(GemmArgs p, DecodeEncode e, int ncols) {
       as2[q] = load2(p.a_scales + arow * ks + q * 64 + sofs);
     }
   }
+  // encoding form: the activation's global scale and first batch of blocks, loaded before any weight
+  // load so that the encode waits only for them
+  constexpr nvfp4_dtype kXdt = kEncode ? (nvfp4_dtype)XDT : NVFP4_BF16;
+  float enc_g = 0.0f;
+  uint32_t enc_raw[kEncodeBatch][encode_words<kXdt>()];
+  if constexpr (kEncode) {
+    enc_g = __builtin_nontemporal_load(p.a_g);
+    encode_load<kXdt>(p, e, 0, enc_raw);
+  }
   __builtin_amdgcn_sched_barrier(0);
   // weight scales of every phase, then the weight codes phase by phase (rows past the workgroup's
   // columns load its last column, never stored)
@@ -201,8 +224,15 @@ gemm_skinny_kernel(GemmArgs p, DecodeEncode e, int ncols) {
   if constexpr (kEncode) {
     uint8_t* const lcodes = act;
     uint8_t* const lscales = act + 16 * (p.K / 2);
-    encode_activation<(nvfp4_dtype)XDT>(p, e, lcodes, lscales);
-    __syncthreads();
+    encode_activation<kXdt>(p, e, enc_g, enc_raw, lcodes, lscales);
+    // LDS-only barrier: this wavefront's LDS writes are done (lgkmcnt 0), then the barrier; the
+    // weight loads stay in flight
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int q = 0; q < NPH; ++q) {
       aq[q] = *reinterpret_cast<const uint4*>(lcodes + arow * (p.K / 2) + q * 512 + cofs);
