@@ -55,14 +55,20 @@ struct DecodeEncode {
   uint8_t* scales;
 };
 
-// 16-byte and 2-byte loads of one lane's fragment bytes.
+// 16-byte and 8-byte loads of one lane's fragment bytes.
 __device__ __forceinline__ uint4 load16(const uint8_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
-__device__ __forceinline__ uint32_t load2(const uint8_t* p) {
-  return *reinterpret_cast<const uint16_t*>(p);
-}
 __device__ __forceinline__ uint2 load8(const uint8_t* p) { return *reinterpret_cast<const uint2*>(p); }
+
+// Phase q's two scale bytes of lane (r, g) (low half of the result), from the 8-byte scale words
+// that lanes (r, g') loaded for phases g' and 4 + g': lane (q % 4) * 16 + r holds them.
+__device__ __forceinline__ uint32_t pick_scales(uint2 v, int q, int r, int g) {
+  const int src = ((q & 3) * 16 + r) * 4;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v.x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v.y);
+  return ((g & 2) ? hi : lo) >> ((g & 1) * 16);
+}
 
 // The encoding form's activation loads: B blocks per thread and batch, 32-bit words per block.
 constexpr int kEncodeBatch = 4;
@@ -147,8 +153,9 @@ __device__ __forceinline__ void encode_activation(const GemmArgs& p, const Decod
 }
 
 // K = NPH * 1024, T tiles of 16 columns, XDT = the raw activation's type in the encoding form
-// (NVFP4_F32 / BF16 / F16) or -1 when the activation comes encoded.
-template <int NPH, int T, int XDT>
+// (NVFP4_F32 / BF16 / F16) or -1 when the activation comes encoded; ASPREAD: the encoded
+// activation has more than 4 rows (how its scales are loaded, below).
+template <int NPH, int T, int XDT, bool ASPREAD>
 __global__ void __launch_bounds__(kSkinnyThreads)
 gemm_skinny_kernel(GemmArgs p, DecodeEncode e, int ncols) {
   constexpr bool kEncode = XDT >= 0;
@@ -174,11 +181,20 @@ gemm_skinny_kernel(GemmArgs p, DecodeEncode e, int ncols) {
   const int arow = min(r, p.M - 1);
   uint4 aq[NPH];
   uint32_t as2[NPH];
+  constexpr int kSq = (NPH + 3) / 4;  // 8-byte scale loads per row (phases g and 4 + g, see below)
+  uint2 asq[kSq];
+  // the activation's scales: with at most 4 rows most lanes share a row and one 2-byte load per
+  // phase is cheapest; with more rows, 8-byte loads and the cross-lane pick used for the weights
   if constexpr (!kEncode) {
 #pragma unroll
-    for (int q = 0; q < NPH; ++q) {
-      aq[q] = load16(p.a_codes + arow * kb + q * 512 + cofs);
-      as2[q] = load2(p.a_scales + arow * ks + q * 64 + sofs);
+    for (int q = 0; q < NPH; ++q) aq[q] = load16(p.a_codes + arow * kb + q * 512 + cofs);
+    if constexpr (ASPREAD) {
+#pragma unroll
+      for (int i = 0; i < kSq; ++i)
+        asq[i] = load8(p.a_scales + arow * ks + min(4 * i + g, NPH - 1) * 64 + wave * 8);
+    } else {
+#pragma unroll
+      for (int q = 0; q < NPH; ++q) as2[q] = *reinterpret_cast<const uint16_t*>(p.a_scales + arow * ks + q * 64 + sofs);
     }
   }
   // encoding form: the activation's global scale and first batch of blocks, loaded before any weight
@@ -199,7 +215,6 @@ gemm_skinny_kernel(GemmArgs p, DecodeEncode e, int ncols) {
   // weight scales: lane (r, g) loads the 8 scale bytes of this wavefront's chunk of row r (those of
   // all four k groups) for phases g and 4 + g, so one load per tile covers four phases; each lane
   // later fetches phase q's bytes from lane (q % 4) * 16 + r and keeps its own two
-  constexpr int kSq = (NPH + 3) / 4;
   uint2 sq[kSq][T];
 #pragma unroll
   for (int i = 0; i < kSq; ++i)
@@ -240,6 +255,13 @@ gemm_skinny_kernel(GemmArgs p, DecodeEncode e, int ncols) {
     }
   }
 
+  if constexpr (!kEncode) {
+    if constexpr (ASPREAD) {
+#pragma unroll
+      for (int q = 0; q < NPH; ++q) as2[q] = pick_scales(asq[q >> 2], q, r, g);
+    }
+  }
+
   // decode every phase's activation fragment (the weights are still streaming in)
   const uint32_t keep = arow_valid ? 0xFFFFFFFFu : 0u;  // padded rows contribute zeros
   half8_t av[NPH][4];
@@ -256,12 +278,7 @@ gemm_skinny_kernel(GemmArgs p, DecodeEncode e, int ncols) {
 #pragma unroll
   for (int q = 0; q < NPH; ++q)
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const int src = ((q & 3) * 16 + r) * 4;
-      const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)sq[q >> 2][t].x);
-      const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)sq[q >> 2][t].y);
-      ws2[q][t] = ((g & 2) ? hi : lo) >> ((g & 1) * 16);
-    }
+    for (int t = 0; t < T; ++t) ws2[q][t] = pick_scales(sq[q >> 2][t], q, r, g);
 
   floatx4_t acc[T];
 #pragma unroll
@@ -313,13 +330,21 @@ template <int NPH, int XDT>
 hipError_t launch_skinny_nph(const GemmArgs& a, const DecodeEncode& e, int cus, hipStream_t stream) {
   const dim3 block(kSkinnyThreads);
   const int per_cu = (a.N + cus - 1) / cus;
+  // more than 4 encoded activation rows: the spread scale loads (the encoding form has none)
+  constexpr bool kSpreadForm = XDT < 0;
+  const bool spread = kSpreadForm && a.M > 4;
+  const int ncols = per_cu > 16 ? (per_cu <= 32 ? per_cu : 32) : 16;
+  const dim3 grid((a.N + ncols - 1) / ncols);
   if (per_cu > 16) {
-    const int ncols = per_cu <= 32 ? per_cu : 32;
-    const dim3 grid((a.N + ncols - 1) / ncols);
-    hipLaunchKernelGGL((gemm_skinny_kernel<NPH, 2, XDT>), grid, block, 0, stream, a, e, ncols);
+    if (spread)
+      hipLaunchKernelGGL((gemm_skinny_kernel<NPH, 2, XDT, kSpreadForm>), grid, block, 0, stream, a, e, ncols);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<NPH, 2, XDT, false>), grid, block, 0, stream, a, e, ncols);
   } else {
-    const dim3 grid((a.N + 15) / 16);
-    hipLaunchKernelGGL((gemm_skinny_kernel<NPH, 1, XDT>), grid, block, 0, stream, a, e, 16);
+    if (spread)
+      hipLaunchKernelGGL((gemm_skinny_kernel<NPH, 1, XDT, kSpreadForm>), grid, block, 0, stream, a, e, ncols);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<NPH, 1, XDT, false>), grid, block, 0, stream, a, e, ncols);
   }
   return hipGetLastError();
 }
