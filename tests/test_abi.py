@@ -65,7 +65,7 @@ def test_library_exports_every_declared_symbol():
 def test_benchmark_reference_library_exports_its_two_kernels():
     """The benchmark's reference kernels (a plain read and an empty launch) are built beside the
     product library, outside its ABI: the product library exports neither."""
-    path = os.path.join(os.path.dirname(nv.LIB_PATH), "libnvfp4_ceiling.so")
+    path = os.path.join(os.path.dirname(os.path.abspath(nv.__file__)), "libnvfp4_ceiling.so")
     out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
                          check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
