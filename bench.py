@@ -341,7 +341,8 @@ def decode_mlp(args, torch, nv, W):
     two modules) and down (N = 5120, K = 17408), each one launch of the streaming kernel.  NVFP4
     weights encoded from seeded N(0, 0.02) draws, rotated over copies of about 300 MB in total
     (beyond the last-level cache); kernel time per product from HIP-graph replays, as in
-    `decode`."""
+    `decode`.  ``<name>_read``: a plain read of the same weight bytes over the same copies (the
+    reference kernel of `decode`'s ceilings)."""
     dev = "cuda:0"
     gen = torch.Generator(device=dev)
     gen.manual_seed(4242)
@@ -384,6 +385,22 @@ def decode_mlp(args, torch, nv, W):
             out[f"{name}_M{M}"] = {"N": N, "K": K, "kernel_us": round(k_ms * 1e3, 3),
                                    "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
                                    "bytes": nbytes}
+        # a plain read of the same weight bytes in one launch of the decode kernels' shape
+        cl = _ceiling_lib()
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        sink = torch.empty(cus * 8, dtype=torch.int32, device=dev)
+
+        def read(i):
+            wc_i, ws_i = copies[i]
+            st = cl.nvfp4_ceiling_stream_read(wc_i.data_ptr(), wc_i.numel(), ws_i.data_ptr(),
+                                              ws_i.numel(), sink.data_ptr(), cus,
+                                              torch.cuda.current_stream().cuda_stream)
+            assert st == 0, st
+
+        r_us = _graph_us(torch, read, R, reps=10)
+        wbytes = N * K * 9 // 16
+        out[f"{name}_read"] = {"us": round(r_us, 3), "bytes": wbytes,
+                               "read_GB/s": round(wbytes / r_us / 1e3, 1)}
         del copies
         torch.cuda.empty_cache()
     return out

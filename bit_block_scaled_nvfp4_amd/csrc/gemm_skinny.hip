@@ -8,23 +8,27 @@
 // [b * ncols, (b + 1) * ncols) -- ncols = ceil(N / compute units), so every compute unit streams the
 // same number of weight bytes -- as T = 1 or 2 MFMA tiles of 16 columns (the second tile may be
 // partly empty), plus all M <= 16 activation rows.  K is cut into phases of 1024 and each phase
-// into 8 chunks of 128; wavefront w of the 8 owns chunk w of every phase.
+// into 8 chunks of 128 (64 code bytes of a row); each wavefront owns one chunk of every phase.
+// Phases go in pairs, and in a pair wavefront w owns chunks 2w and 2w + 1 of the pair's 16, so its
+// loads of one row in the two phases fill the two halves of one 128-byte line (an unpaired last
+// phase keeps chunk q * 8 + w): half as many cache lines touched per wavefront as with one chunk
+// per wavefront in each phase's 512 bytes.
 //
 // Every lane loads exactly the bytes it feeds to the MFMA: in a 16x16x32 MFMA, lane l supplies
 // row/column r = l % 16 and 8 of the 32 k-slots (group g = l / 16); within a chunk of 128, lane
 // group g uses the 16 bytes holding elements [32g, 32g + 32) of its row, 32-bit word j of them in
 // MFMA step j (j = 0..3), inside 16-blocks 2g and 2g + 1 (two scale bytes).  Both operands use this
-// map.  So a wavefront's weight load of one tile and phase reads 16 rows x 64 contiguous bytes, the
-// eight wavefronts together 16 rows x 512 bytes, straight into registers: no LDS staging and no
-// workgroup barrier while the weights stream.  The weight scales are loaded 8 bytes per lane (a
-// wavefront's chunk of one row holds the scale bytes of all four k groups): lane (r, g) loads those
-// of phases g and 4 + g, and each lane then fetches phase q's word from lane (q % 4) * 16 + r with a
-// cross-lane permute, so a tile's scales take one or two load instructions instead of one per
-// phase.  All loads of the launch are issued up front, the activation's first (small, and the same
-// for every workgroup, so served from L2), then the weight scales, then the weight codes phase by
-// phase.  The activation fragments of all phases are decoded
-// to f16 while the weights are in flight, so once phase q's weights land only their decode and the
-// MFMAs remain.  Rows of the activation at or past M are zero.
+// map.  So a wavefront's weight load of one tile and phase reads 16 rows x 64 contiguous bytes,
+// straight into registers: no LDS staging and no workgroup barrier while the weights stream.  The
+// weight scales are loaded 8 bytes per lane (a wavefront's chunk of one row holds the scale bytes
+// of all four k groups): lane (r, g) loads those of phases g and 4 + g, and each lane then fetches
+// phase q's word from lane (q % 4) * 16 + r with a cross-lane permute, so a tile's scales take one
+// or two load instructions instead of one per phase.  Up to 8 phases, all loads of the launch are
+// issued up front, the activation's first (small, and the same for every workgroup, so served from
+// L2), then the weight scales, then the weight codes phase by phase; the activation fragments of
+// all phases are decoded to f16 while the weights are in flight, so once phase q's weights land
+// only their decode and the MFMAs remain.  Longer K streams through registers a fixed number of
+// phases ahead (gemm_skinny_long_kernel).  Rows of the activation at or past M are zero.
 //
 // Activation input.  Either its NVFP4 codes and scales (the product alone), or the raw activation
 // (f32, bf16 or f16) with its static global scale: then every workgroup first encodes the M x K
@@ -35,6 +39,8 @@
 // Reduction: the 8 wavefronts' partial 16x16 tiles of each tile are summed through LDS in a fixed
 // order (deterministic), scaled per column by 1 / (gA * gW[seg(n)]) and stored.  Every output
 // element is accumulated the same way whichever workgroup and tile slot its column falls in.
+#include <utility>
+
 #include "codec.h"
 #include "gemm_common.h"
 
@@ -60,6 +66,30 @@ __device__ __forceinline__ uint4 load16(const uint8_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 __device__ __forceinline__ uint2 load8(const uint8_t* p) { return *reinterpret_cast<const uint2*>(p); }
+
+// Chunk of K (128 elements, 64 code bytes of a row) that wavefront w owns in phase q.  Phases go
+// in pairs, and in a pair wavefront w owns chunks 2w and 2w + 1 of the pair's 16, so its loads of
+// one row in the two phases fill the two halves of one 128-byte line; an unpaired last phase keeps
+// chunk q * 8 + w.  Activation and weights use the same map, so every k is contracted once.
+template <int NPH>
+__device__ __forceinline__ int chunk_of(int q, int w) {
+  constexpr int kPaired = NPH - NPH % 2;
+  return q < kPaired ? (q / 2) * 16 + 2 * w + (q % 2) : q * 8 + w;
+}
+
+// An empty asm that takes and returns the value in registers: arithmetic on a loaded value stays
+// behind the point where this is called.
+__device__ __forceinline__ void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void pin(uint2& v) {
+  pin(v.x);
+  pin(v.y);
+}
+__device__ __forceinline__ void pin(uint4& v) {
+  pin(v.x);
+  pin(v.y);
+  pin(v.z);
+  pin(v.w);
+}
 
 // Phase q's two scale bytes of lane (r, g) (low half of the result), from the 8-byte scale words
 // that lanes (r, g') loaded for phases g' and 4 + g': lane (q % 4) * 16 + r holds them.
@@ -174,7 +204,6 @@ gemm_skinny_kernel(GemmArgs p, DecodeEncode e, int ncols) {
   const int64_t kb = p.k_pitch / 2, ks = p.k_pitch / 16;
   // byte offsets of this lane's 16 code bytes and 2 scale bytes within a row, for phase q:
   // chunk c = q * 8 + wave, codes at c * 64 + g * 16, scales at c * 8 + g * 2
-  const int cofs = wave * 64 + g * 16, sofs = wave * 8 + g * 2;
 
   // activation fragments (encoded form: straight from global memory, L2-resident after the first
   // workgroup); rows >= M load the last row and are zeroed at decode
@@ -187,14 +216,15 @@ gemm_skinny_kernel(GemmArgs p, DecodeEncode e, int ncols) {
   // phase is cheapest; with more rows, 8-byte loads and the cross-lane pick used for the weights
   if constexpr (!kEncode) {
 #pragma unroll
-    for (int q = 0; q < NPH; ++q) aq[q] = load16(p.a_codes + arow * kb + q * 512 + cofs);
+    for (int q = 0; q < NPH; ++q) aq[q] = load16(p.a_codes + arow * kb + chunk_of<NPH>(q, wave) * 64 + g * 16);
     if constexpr (ASPREAD) {
 #pragma unroll
       for (int i = 0; i < kSq; ++i)
-        asq[i] = load8(p.a_scales + arow * ks + min(4 * i + g, NPH - 1) * 64 + wave * 8);
+        asq[i] = load8(p.a_scales + arow * ks + chunk_of<NPH>(min(4 * i + g, NPH - 1), wave) * 8);
     } else {
 #pragma unroll
-      for (int q = 0; q < NPH; ++q) as2[q] = *reinterpret_cast<const uint16_t*>(p.a_scales + arow * ks + q * 64 + sofs);
+      for (int q = 0; q < NPH; ++q)
+        as2[q] = *reinterpret_cast<const uint16_t*>(p.a_scales + arow * ks + chunk_of<NPH>(q, wave) * 8 + g * 2);
     }
   }
   // encoding form: the activation's global scale and first batch of blocks, loaded before any weight
@@ -220,13 +250,13 @@ gemm_skinny_kernel(GemmArgs p, DecodeEncode e, int ncols) {
   for (int i = 0; i < kSq; ++i)
 #pragma unroll
     for (int t = 0; t < T; ++t)
-      sq[i][t] = load8(p.w_scales + wrow[t] * ks + min(4 * i + g, NPH - 1) * 64 + wave * 8);
+      sq[i][t] = load8(p.w_scales + wrow[t] * ks + chunk_of<NPH>(min(4 * i + g, NPH - 1), wave) * 8);
   __builtin_amdgcn_sched_barrier(0);
   uint4 wq[NPH][T];
 #pragma unroll
   for (int q = 0; q < NPH; ++q) {
 #pragma unroll
-    for (int t = 0; t < T; ++t) wq[q][t] = load16(p.w_codes + wrow[t] * kb + q * 512 + cofs);
+    for (int t = 0; t < T; ++t) wq[q][t] = load16(p.w_codes + wrow[t] * kb + chunk_of<NPH>(q, wave) * 64 + g * 16);
     __builtin_amdgcn_sched_barrier(0);  // keep the phases' loads in phase order
   }
   // global scales for the epilogue factors 1 / (gA * gW[seg(n)]), used only at the end
@@ -250,8 +280,8 @@ gemm_skinny_kernel(GemmArgs p, DecodeEncode e, int ncols) {
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int q = 0; q < NPH; ++q) {
-      aq[q] = *reinterpret_cast<const uint4*>(lcodes + arow * (p.K / 2) + q * 512 + cofs);
-      as2[q] = *reinterpret_cast<const uint16_t*>(lscales + arow * (p.K / 16) + q * 64 + sofs);
+      aq[q] = *reinterpret_cast<const uint4*>(lcodes + arow * (p.K / 2) + chunk_of<NPH>(q, wave) * 64 + g * 16);
+      as2[q] = *reinterpret_cast<const uint16_t*>(lscales + arow * (p.K / 16) + chunk_of<NPH>(q, wave) * 8 + g * 2);
     }
   }
 
@@ -320,6 +350,128 @@ gemm_skinny_kernel(GemmArgs p, DecodeEncode e, int ncols) {
   }
 }
 
+// Long-K form of the product (K = NPH * 1024 above the one-pass kernel's 8 phases): the same work
+// split, fragments and scale loads, but the loads stream through registers D phases ahead instead of
+// all being issued at once, and each phase's activation fragment is decoded when its phase comes.
+// Phase q's loads (activation codes and scales, then the weights' scale group when q % 4 == 0, then
+// the weight codes) are issued right after phase q - D has been contracted, so D phases' bytes are
+// always in flight and the register footprint is that of D phases.  Every index is a compile-time
+// constant (the phase loop is unrolled), so each wait is for exactly the phase it needs.
+template <int NPH, int T, bool ASPREAD, int D>
+__global__ void __launch_bounds__(kSkinnyThreads)
+gemm_skinny_long_kernel(GemmArgs p, int ncols) {
+  __shared__ floatx4_t partial[T][kSkinnyWaves][64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int c0 = blockIdx.x * ncols;
+  const int cend = min(c0 + ncols, p.N);
+  const int clast = cend - 1;
+  const int64_t kb = p.k_pitch / 2, ks = p.k_pitch / 16;
+  const int arow = min(r, p.M - 1);
+  const uint32_t keep = r < p.M ? 0xFFFFFFFFu : 0u;  // padded activation rows contribute zeros
+  int wrow[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) wrow[t] = min(c0 + t * 16 + r, clast);
+  const uint8_t* const ac = p.a_codes + arow * kb + g * 16;
+  const uint8_t* const asb = p.a_scales + arow * ks;
+
+  constexpr int kSq = (NPH + 3) / 4;
+  uint4 aq[NPH];
+  uint32_t as2[NPH];
+  uint2 asq[kSq];
+  uint2 sq[kSq][T];
+  uint4 wq[NPH][T];
+  auto issue = [&](int q) {
+    aq[q] = load16(ac + chunk_of<NPH>(q, wave) * 64);
+    if constexpr (ASPREAD) {
+      if (q % 4 == 0) asq[q / 4] = load8(asb + chunk_of<NPH>(min(q + g, NPH - 1), wave) * 8);
+    } else {
+      // the aligned word holding this lane's two scale bytes (shifted out at use)
+      as2[q] = *reinterpret_cast<const uint32_t*>(asb + chunk_of<NPH>(q, wave) * 8 + (g >> 1) * 4);
+    }
+    if (q % 4 == 0) {
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        sq[q / 4][t] = load8(p.w_scales + wrow[t] * ks + chunk_of<NPH>(min(q + g, NPH - 1), wave) * 8);
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) wq[q][t] = load16(p.w_codes + wrow[t] * kb + chunk_of<NPH>(q, wave) * 64 + g * 16);
+  };
+
+#pragma unroll
+  for (int q = 0; q < D; ++q) {
+    issue(q);
+    __builtin_amdgcn_sched_barrier(0);  // keep the phases' loads in phase order
+  }
+  const float ga = p.a_g[0];
+  float gw[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) gw[t] = p.seg_g[column_segment(p.seg, wrow[t])];
+  __builtin_amdgcn_sched_barrier(0);
+
+  floatx4_t acc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int q = 0; q < NPH; ++q) {
+    // phase q: the activation fragment, then the weights (the compiler waits for exactly these).
+    // Its loaded words pass through an empty asm first, so no arithmetic on them is hoisted into
+    // the prologue, where it would wait for phases still streaming in.
+    if constexpr (ASPREAD) {
+      if (q % 4 == 0) pin(asq[q / 4]);
+    } else {
+      pin(as2[q]);
+    }
+    pin(aq[q]);
+    if (q % 4 == 0) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) pin(sq[q / 4][t]);
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) pin(wq[q][t]);
+    const uint32_t sa_bits = ASPREAD ? pick_scales(asq[q / 4], q, r, g) : as2[q] >> ((g & 1) * 16);
+    const half2_t sa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sa_bits & keep, 1.0f, false);
+    const uint32_t a4[4] = {aq[q].x & keep, aq[q].y & keep, aq[q].z & keep, aq[q].w & keep};
+    half8_t av[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) av[j] = decode8(a4[j], j < 2 ? sa[0] : sa[1]);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const half2_t sw =
+          __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pick_scales(sq[q / 4][t], q, r, g), 1.0f, false);
+      const uint32_t w4[4] = {wq[q][t].x, wq[q][t].y, wq[q][t].z, wq[q][t].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const half8_t bv = decode8(w4[j], j < 2 ? sw[0] : sw[1]);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[j], bv, acc[t], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (q + D < NPH) issue(q + D);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // deterministic reduction of the 8 partial tiles of each tile, as in the one-pass kernel
+#pragma unroll
+  for (int t = 0; t < T; ++t) partial[t][wave][lane] = acc[t];
+  __syncthreads();
+  if (wave >= T) return;
+  floatx4_t sum = partial[wave][0][lane];
+#pragma unroll
+  for (int w = 1; w < kSkinnyWaves; ++w) sum += partial[wave][w][lane];
+  const int n = c0 + wave * 16 + r;
+  if (n >= cend) return;
+  const float al = 1.0f / (ga * (wave == 0 ? gw[0] : gw[T - 1]));
+#pragma unroll
+  for (int e4 = 0; e4 < 4; ++e4) {
+    const int m = 4 * g + e4;
+    if (m < p.M) store_c(p.c, p.c_bf16, p.ldc, m, n, sum[e4] * al);
+  }
+}
+
 }  // namespace
 
 namespace {
@@ -369,6 +521,45 @@ hipError_t launch_skinny_piece(const GemmArgs& a, const DecodeEncode& e, int cus
   }
 }
 
+// Phases in flight in the long-K form.
+constexpr int kLongDepth = 8;
+
+template <int NPH>
+hipError_t launch_skinny_long_nph(const GemmArgs& a, int cus, hipStream_t stream) {
+  const dim3 block(kSkinnyThreads);
+  const int per_cu = (a.N + cus - 1) / cus;
+  const int ncols = per_cu > 16 ? per_cu : 16;
+  const dim3 grid((a.N + ncols - 1) / ncols);
+  constexpr int D = kLongDepth;
+  if (per_cu > 16) {
+    if (a.M > 4)
+      hipLaunchKernelGGL((gemm_skinny_long_kernel<NPH, 2, true, D>), grid, block, 0, stream, a, ncols);
+    else
+      hipLaunchKernelGGL((gemm_skinny_long_kernel<NPH, 2, false, D>), grid, block, 0, stream, a, ncols);
+  } else {
+    if (a.M > 4)
+      hipLaunchKernelGGL((gemm_skinny_long_kernel<NPH, 1, true, D>), grid, block, 0, stream, a, ncols);
+    else
+      hipLaunchKernelGGL((gemm_skinny_long_kernel<NPH, 1, false, D>), grid, block, 0, stream, a, ncols);
+  }
+  return hipGetLastError();
+}
+
+template <int... Q>
+hipError_t launch_skinny_long_switch(const GemmArgs& a, int cus, hipStream_t stream,
+                                     std::integer_sequence<int, Q...>) {
+  hipError_t e = hipErrorInvalidValue;
+  const int nph = (int)(a.K / kPhaseK);
+  ((nph == Q + kSkinnyMaxK / kPhaseK + 1 ? (e = launch_skinny_long_nph<Q + kSkinnyMaxK / kPhaseK + 1>(a, cus, stream), 0) : 0), ...);
+  return e;
+}
+
+// K above kSkinnyMaxK up to kStreamMaxK, at most 32 columns per compute unit.
+hipError_t launch_skinny_long(const GemmArgs& a, int cus, hipStream_t stream) {
+  return launch_skinny_long_switch(
+      a, cus, stream, std::make_integer_sequence<int, (int)((kStreamMaxK - kSkinnyMaxK) / kPhaseK)>{});
+}
+
 hipError_t compute_units(int& cus) {
   int dev = 0;
   cus = 0;
@@ -402,14 +593,15 @@ hipError_t launch_gemm_skinny_encode(const GemmArgs& a, const void* x, nvfp4_dty
   return hipErrorInvalidValue;
 }
 
-// Decode-shaped products.  Up to 32 columns per compute unit and K up to kSkinnyMaxK: this
-// kernel, in one pass.  More columns, or K up to kStreamMaxK: the streaming kernels
-// (gemm_stream.hip), which keep their weight copies always in flight.  K beyond that
-// (f32 output only): the streaming kernel on the fewest pieces of K of at most 8 phases, as equal
-// as possible; the first piece writes C and each later one, launched after it on the same stream,
-// adds its scaled partial product: C = fl(...fl(acc_0 a) + acc_1 a ...).  (Pieces are slower than
-// one pass at K = 17408, N = 5120: every piece meets the uneven share of 320 tiles among the
-// compute units again.)
+// Decode-shaped products.  Up to 32 columns per compute unit and K up to kSkinnyMaxK: the one-pass
+// kernel.  K up to kStreamMaxK with up to 16 columns per compute unit, or up to 32 with at most 4
+// activation rows: its long-K form.  More columns (or more rows on two tiles of a long K): the
+// streaming kernels (gemm_stream.hip), which stream weight copies through LDS.  K beyond
+// kStreamMaxK (f32 output only): the streaming kernel on the fewest pieces of K of at most 8
+// phases, as equal as possible; the first piece writes C and each later one, launched after it on
+// the same stream, adds its scaled partial product: C = fl(...fl(acc_0 a) + acc_1 a ...).  The
+// one-pass and long-K forms accumulate every element the same way as each other, the streaming
+// kernels in another order (one chunk per wavefront in each phase), within the same tolerance.
 hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
   int cus = 0;
   hipError_t e = compute_units(cus);
@@ -417,6 +609,10 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
   const int per_cu = (a.N + cus - 1) / cus;
   if (a.K <= kSkinnyMaxK && per_cu <= 32)
     return launch_skinny_piece<-1>(a, DecodeEncode{nullptr, 0, nullptr, nullptr}, cus, stream);
+  // long K: the register-streaming form for one tile per workgroup, or two with at most 4
+  // activation rows; with more rows on two tiles the column-pair streaming form measured faster
+  if (a.K <= kStreamMaxK && (per_cu <= 16 || (per_cu <= 32 && a.M <= 4)))
+    return launch_skinny_long(a, cus, stream);
   if (a.K <= kStreamMaxK) return launch_gemm_stream(a, stream);
   const int phases = a.K / kPhaseK;
   const int pieces = (phases + 7) / 8;

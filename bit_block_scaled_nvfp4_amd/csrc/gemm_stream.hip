@@ -13,12 +13,9 @@
 //  * K <= 8192 (gemm_stream_cached_kernel): every wavefront decodes its activation fragments of all
 //    phases once and keeps them in registers; slots hold two tiles, unit (t + 1, q) is copied
 //    while unit (t, q) is computed, two copies per unit.
-//  * longer K, at most 16 columns per compute unit (gemm_stream_kernel): a ring of
-//    kRing slots with kAhead units in flight; the activation block scales of all K are copied once
-//    and the activation codes reloaded per unit from L2 (three vector memory instructions per
-//    unit).
 //  * longer K, more than 16 columns per compute unit (gemm_stream_pair_kernel): equal column
 //    ranges instead of tiles dealt round robin, two tiles per unit; described at the kernel.
+// (Longer K with fewer columns per compute unit runs the skinny kernel's long-K form.)
 // Every wavefront issues the same vector memory instructions per unit, so each wait is a
 // compile-time vmcnt.
 //
@@ -35,14 +32,11 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRing = 3;             // LDS slots (3 measured faster than 4 to 8)
-constexpr int kAhead = kRing - 1;    // units in flight beyond the one computed
 constexpr int kUnitK = 1024;         // K elements per unit
 constexpr int kPieces = kUnitK / 32;               // 16-byte code pieces per row per unit (32)
 constexpr int kCodeBytes = 16 * kPieces * 16;      // 8 KiB
 constexpr int kScaleBytes = 16 * (kUnitK / 16);    // 16 rows x 64 bytes
 constexpr int kSlotBytes = kCodeBytes + kScaleBytes;
-constexpr int kVmemPerUnit = 3;
 
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
@@ -91,172 +85,6 @@ __device__ __forceinline__ void stage_global_scales(const GemmArgs& p, float* gt
 #pragma unroll
     for (int t = 0; t <= NVFP4_MAX_SEGMENTS; ++t) gtab[t] = v[t];
   }
-}
-
-// Tile and phase of unit u of this workgroup; units past the last real one repeat it (their
-// copies are redundant and their compute is skipped).
-__device__ __forceinline__ void unit_coords(const StreamArgs& s, int units, int u, int& tile,
-                                            int& q) {
-  const int uu = u < units ? u : units - 1;
-  const int i = uu / s.nph;
-  q = uu - i * s.nph;
-  tile = (int)blockIdx.x + i * (int)gridDim.x;
-}
-
-// Copies of one unit into `slot` and this lane's activation fragment of it.
-__device__ __forceinline__ void issue_unit(const StreamArgs& s, int tile, int q, uint8_t* slot,
-                                           int wave, int lane, uint4& aw) {
-  const GemmArgs& p = s.p;
-  const int kb = p.k_pitch / 2, ks = p.k_pitch / 16;
-  const int t = wave * 64 + lane;
-  const int row = t / kPieces;                     // 0..15
-  const int jl = t - row * kPieces;
-  const int j = (jl & ~15) | ((jl ^ row) & 15);  // slot jl of the row holds global piece j
-  const int grow = min(tile * 16 + row, p.N - 1);
-  __builtin_amdgcn_global_load_lds(p.w_codes + (int64_t)grow * kb + q * (kUnitK / 2) + j * 16,
-                                   slot + wave * 64 * 16, 16, 0, 0);
-  // scale bytes, 16 rows x 64: thread t copies dword t % 16 of row (t % 256) / 16.  Wavefronts
-  // 4..7 repeat wavefronts 0..3's copies (the same bytes to the same place), so every wavefront
-  // issues the same count and every copy targets the slot's own array
-  {
-    const int ts = t & 255;
-    const int srow = ts >> 4, dw = ts & 15;
-    const int gsrow = min(tile * 16 + srow, p.N - 1);
-    __builtin_amdgcn_global_load_lds(p.w_scales + (int64_t)gsrow * ks + q * (kUnitK / 16) + dw * 4,
-                                     slot + kCodeBytes + (wave & 3) * 64 * 4, 4, 0, 0);
-  }
-  // activation fragment: chunk `wave` of the unit, row r = lane % 16 (rows >= M load the last row
-  // and are zeroed at use), group g = lane / 16
-  const int r = lane & 15, g = lane >> 4;
-  const int arow = min(r, p.M - 1);
-  aw = *reinterpret_cast<const uint4*>(p.a_codes + (int64_t)arow * kb + q * (kUnitK / 2) +
-                                       wave * 64 + g * 16);
-  __builtin_amdgcn_sched_barrier(0);  // the three instructions stay in this order
-}
-
-// Contract this wavefront's 128 elements of a unit into acc.
-__device__ __forceinline__ void compute_unit(const uint8_t* slot, const uint8_t* asc, int ksa,
-                                             int q, int wave, int r, int g, bool arow_valid,
-                                             const uint4& aw_in, floatx4_t& acc) {
-  const uint32_t keep = arow_valid ? 0xFFFFFFFFu : 0u;  // padded activation rows contribute zeros
-  const uint32_t aq[4] = {aw_in.x & keep, aw_in.y & keep, aw_in.z & keep, aw_in.w & keep};
-  const int c = q * (kUnitK / 128) + wave;  // chunk of 128 elements within K
-  const uint32_t as2 = *reinterpret_cast<const uint16_t*>(asc + r * ksa + c * 8 + g * 2) & keep;
-  const half2_t sa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(as2, 1.0f, false);
-  const int j = wave * 4 + g;
-  const uint4 ww =
-      *reinterpret_cast<const uint4*>(slot + (r * kPieces + ((j & ~15) | ((j ^ r) & 15))) * 16);
-  const uint32_t ws2 = *reinterpret_cast<const uint16_t*>(slot + kCodeBytes + r * 64 + j * 2);
-  const half2_t sw = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ws2, 1.0f, false);
-  const uint32_t wq[4] = {ww.x, ww.y, ww.z, ww.w};
-#pragma unroll
-  for (int s2 = 0; s2 < 4; ++s2) {
-    const half8_t av = decode8(aq[s2], s2 < 2 ? sa[0] : sa[1]);
-    const half8_t bv = decode8(wq[s2], s2 < 2 ? sw[0] : sw[1]);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc, 0, 0, 0);
-  }
-}
-
-__global__ void __launch_bounds__(kThreads) gemm_stream_kernel(StreamArgs s) {
-  // one statically named array per ring slot: with the unit loop unrolled over the ring, every
-  // LDS read names the slot it depends on, so the compiler waits only for that slot's copies
-  __shared__ __attribute__((aligned(16))) uint8_t s0[kSlotBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t s1[kSlotBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t s2[kSlotBytes];
-  uint8_t* const ring[kRing] = {s0, s1, s2};
-  __shared__ __attribute__((aligned(16))) uint8_t asc[16 * (kStreamMaxK / 16)];
-  __shared__ floatx4_t partial[kWaves][64];
-  __shared__ float gtab[NVFP4_MAX_SEGMENTS + 1];  // gW[0 .. nseg-1], then gA
-
-  const GemmArgs& p = s.p;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int r = lane & 15, g = lane >> 4;
-  const bool arow_valid = r < p.M;
-  const int ksa = p.K / 16;
-  // tiles b, b + G, ...: the same count for every wavefront of the workgroup
-  const int my_tiles = (s.ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
-  const int units = my_tiles * s.nph;
-
-
-  // the activation block scales of all K, copied once.  They are older than every unit's copies,
-  // and the wait for a unit leaves only later units' instructions outstanding (the same number in
-  // every wavefront), so it covers them whatever number each wavefront issued here.
-  {
-    const int per_row = ksa / 16;  // 16-byte pieces per row
-    for (int i = threadIdx.x; i < p.M * per_row; i += kThreads) {
-      const int row = i / per_row;
-      __builtin_amdgcn_global_load_lds(
-          p.a_scales + (int64_t)row * (p.k_pitch / 16) + (i - row * per_row) * 16,
-          asc + (i & ~63) * 16, 16, 0, 0);
-    }
-  }
-
-  uint4 aw[kRing];
-#pragma unroll
-  for (int k = 0; k < kAhead; ++k) {
-    int tile, q;
-    unit_coords(s, units, k, tile, q);
-    issue_unit(s, tile, q, ring[k], wave, lane, aw[k]);
-  }
-  stage_global_scales(p, gtab);
-
-  floatx4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int u0 = 0; u0 < units; u0 += kRing) {
-#pragma unroll
-    for (int k = 0; k < kRing; ++k) {
-      const int u = u0 + k;
-      // unit u has landed once only the kAhead - 1 later units' instructions are outstanding;
-      // after the barrier every wavefront's copies of it are in LDS and every wavefront is done
-      // with unit u - 1, whose slot the copies issued below reuse
-      __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<(kAhead - 1) * kVmemPerUnit>();
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      {
-        int tile, q;
-        unit_coords(s, units, u + kAhead, tile, q);
-        issue_unit(s, tile, q, ring[(k + kAhead) % kRing], wave, lane,
-                   aw[(k + kAhead) % kRing]);
-      }
-      if (u < units) {  // uniform over the workgroup
-        int tile, q;
-        unit_coords(s, units, u, tile, q);
-        compute_unit(ring[k], asc, ksa, q, wave, r, g, arow_valid, aw[k], acc);
-        if (q == s.nph - 1) {
-          // end of a tile: fixed-order sum of the 8 wavefronts' partial tiles, then the store
-          partial[wave][lane] = acc;
-          // LDS-only barrier: this wavefront's LDS writes are done (lgkmcnt 0), then the barrier.
-          // __syncthreads() (a workgroup fence) would also wait for every copy in flight.
-          __builtin_amdgcn_sched_barrier(0);
-          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt not waited for
-          __builtin_amdgcn_s_barrier();
-          __builtin_amdgcn_sched_barrier(0);
-          if (wave == 0) {
-            floatx4_t sum = partial[0][lane];
-#pragma unroll
-            for (int w = 1; w < kWaves; ++w) sum += partial[w][lane];
-            // lane holds column tile * 16 + r, rows 4 g .. 4 g + 3
-            const int n = tile * 16 + r;
-            if (n < p.N) {
-              const float al = 1.0f / (gtab[NVFP4_MAX_SEGMENTS] * gtab[column_segment(p.seg, n)]);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int m = 4 * g + e;
-                if (m < p.M) store_c(p.c, p.c_bf16, p.ldc, m, n, sum[e] * al);
-              }
-            }
-          }
-          acc = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
-          // partial[] is next written at the following tile's end, after at least one more
-          // unit barrier
-        }
-      }
-    }
-  }
-  // the redundant copies issued past the last unit must land before the workgroup's LDS is
-  // released
-  wait_vmcnt<0>();
 }
 
 // K <= 8192 (NPH phases): the same stream with the activations decoded once.  Every tile reuses
@@ -613,7 +441,8 @@ __global__ void __launch_bounds__(kThreads) gemm_stream_pair_kernel(PairArgs s) 
   const int clast = cend - 1;
   const int units = ((cend - c0 + 31) / 32) * s.nph;
 
-  // activation block scales: as in gemm_stream_kernel, the unit waits cover these copies
+  // activation block scales of all K, copied once to LDS: they are older than every unit's copies,
+  // so the unit waits cover them
   {
     const int per_row = ksa / 16;
     for (int i = threadIdx.x; i < p.M * per_row; i += kThreads) {
@@ -698,7 +527,7 @@ hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream) {
     case 6: hipLaunchKernelGGL(gemm_stream_cached_kernel<6>, dim3(grid), dim3(kThreads), 0, stream, s); break;
     case 7: hipLaunchKernelGGL(gemm_stream_cached_kernel<7>, dim3(grid), dim3(kThreads), 0, stream, s); break;
     case 8: hipLaunchKernelGGL(gemm_stream_cached_kernel<8>, dim3(grid), dim3(kThreads), 0, stream, s); break;
-    default: hipLaunchKernelGGL(gemm_stream_kernel, dim3(grid), dim3(kThreads), 0, stream, s); break;
+    default: return hipErrorInvalidValue;  // longer K with at most 16 columns per compute unit: not here
   }
   return hipGetLastError();
 }

@@ -29,7 +29,7 @@ _LONG = {}
 
 def _long_weight():
     """One NVFP4 weight of 4500 x 9216 shared (read only) by every thread: its decode products take
-    the streaming kernel's column-pair form."""
+    the decode kernel's long-K form with two tiles per workgroup."""
     import bit_block_scaled_nvfp4_amd as nv
 
     if "w" not in _LONG:

@@ -75,9 +75,10 @@ def test_ragged_shapes(M, N, K):
 @pytest.mark.parametrize("M,N,K", [(1, 48, 9216), (16, 320, 17408), (7, 130, 15360), (4, 40, 31744),
                                    (2, 40, 33792), (3, 50, 65536)])
 def test_decode_long_k(M, N, K):
-    # at most 16 rows and K above 8192: the streaming kernel up to K = 32768 (9 to 31 phases of
-    # 1024), beyond that pieces of at most 8 phases (5 at K = 33792, 8 at K = 65536) through its
-    # cached form, each later piece adding into C; three fused modules
+    # at most 16 rows and K above 8192, at most 16 columns per compute unit: the decode kernel's
+    # long-K form up to K = 32768 (9 to 31 phases of 1024), beyond that pieces of at most 8 phases
+    # (5 at K = 33792, 8 at K = 65536) through the streaming kernel's cached form, each later piece
+    # adding into C; three fused modules
     a = random_matrix(M * 11 + K, M, K, outlier_cols=max(1, K // 200))
     wt = random_matrix(N * 3 + K, N, K, std=0.02)
     segs = [0, N // 3, N // 2, N]
@@ -96,12 +97,14 @@ def test_decode_many_columns(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(3, 4200, 9216), (16, 8250, 10240), (1, 5120, 17408),
-                                   (2, 4500, 10240)])
+                                   (2, 4500, 10240), (16, 5120, 17408), (5, 4500, 10240)])
 def test_decode_even_column_share(M, N, K):
     # K above 8192 and more than 16 columns per compute unit (256 of them): workgroups own equal
-    # column ranges walked in groups of 32 (17 columns and a last workgroup of one; 33 columns, two
-    # groups; 20 columns, the MLP down projection's shape; 18 columns), three fused modules.  Their
-    # 9, 20, 17 and 10 units of one group-phase end in closing runs of 3, 2, 2 and 4 units
+    # column ranges (17 columns and a last workgroup of one; 33; 20, the MLP down projection's
+    # shape; 18), three fused modules.  Up to 32 columns and at most 4 rows: the decode kernel's
+    # long-K form with two tiles.  More rows, or more columns: the streaming kernel's column-pair
+    # form, groups of 32 columns whose 9, 20, 17 and 10 units of one group-phase end in closing
+    # runs of 3, 2, 2 and 4 units
     a = random_matrix(M * 17 + N, M, K, outlier_cols=max(1, K // 300))
     wt = random_matrix(N * 5 + K, N, K, std=0.02)
     segs = [0, N // 3 + 7, N // 2 + 1, N]
@@ -120,7 +123,7 @@ def test_decode_even_column_share_bf16_output():
 
 
 def test_decode_long_k_bf16_output():
-    # bf16 C with a long K: the streaming kernel (one pass over K, so no partial sums are rounded)
+    # bf16 C with a long K: the long-K decode form (one pass over K, so no partial sums are rounded)
     a = random_matrix(71, 3, 17408, outlier_cols=40)
     wt = random_matrix(72, 96, 17408, std=0.02)
     ac, as_, ga, wc, ws, gw = _encode(a, wt, [0, 96])
@@ -222,6 +225,27 @@ def test_single_row_fused_equals_per_segment_calls_bitwise(M):
     assert np.array_equal(fused, np.concatenate(parts, axis=1))
     R = oracle.gemm_exact(ac, as_, ga, wc, ws, gw, segs)
     check_gemm(fused, R, oracle.gemm_abs_bound(ac, as_, ga, wc, ws, gw, segs), f"decode M={M}")
+
+
+@pytest.mark.parametrize("M", [2, 16])
+def test_long_k_fused_equals_per_segment_calls_bitwise(M):
+    """Long K on the decode path (the long-K form, two tiles per workgroup fused, one per segment):
+    the fused product and the per-segment products agree bit for bit."""
+    K = 10240
+    sizes = [2048, 2048, 48, 48]
+    segs = list(np.cumsum([0] + sizes))
+    a = random_matrix(60 + M, M, K, outlier_cols=20)
+    wt = random_matrix(61, segs[-1], K, std=0.02)
+    ac, as_, ga, wc, ws, gw = _encode(a, wt, segs)
+    fused = _gpu_product(ac, as_, ga, wc, ws, gw, segs)
+    parts = [_gpu_product(ac, as_, ga, wc[segs[j]:segs[j + 1]], ws[segs[j]:segs[j + 1]], [gw[j]],
+                          [0, sizes[j]]) for j in range(len(sizes))]
+    if M <= 4:  # with more rows the fused call's two-tile share runs the streaming kernel
+        assert np.array_equal(fused, np.concatenate(parts, axis=1))
+    R = oracle.gemm_exact(ac, as_, ga, wc, ws, gw, segs)
+    bound = oracle.gemm_abs_bound(ac, as_, ga, wc, ws, gw, segs)
+    check_gemm(fused, R, bound, f"long K fused M={M}")
+    check_gemm(np.concatenate(parts, axis=1), R, bound, f"long K per segment M={M}")
 
 
 def test_fused_equals_per_segment_calls_bitwise():

@@ -3,8 +3,8 @@
 One captured sequence covers both product kernels and the encoders:
 - a dynamic activation encode;
 - a two-module fused product (tiled kernel) and a decode-shaped product (M = 4, skinny kernel);
-- a decode-shaped product with K = 9216 and 4500 columns (M = 2, streaming kernel, column-pair
-  form);
+- a decode-shaped product with K = 9216 and 4500 columns (M = 2, the decode kernel's long-K form,
+  two tiles per workgroup);
 - a dynamic SiLU-mul encode;
 - an FP8 KV store into paged slots;
 - a dynamic fake quantisation.
