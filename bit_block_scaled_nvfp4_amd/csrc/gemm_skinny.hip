@@ -352,7 +352,9 @@ gemm_skinny_kernel(GemmArgs p, DecodeEncode e, int ncols) {
 
 // Long-K form of the product (K = NPH * 1024 above the one-pass kernel's 8 phases): the same work
 // split, fragments and scale loads, but the loads stream through registers D phases ahead instead of
-// all being issued at once, and each phase's activation fragment is decoded when its phase comes.
+// all being issued at once, each phase's activation fragment is decoded when its phase comes, and
+// the weight codes arrive as whole cache lines that the wavefront rearranges into fragments through
+// its own LDS area (below).
 // Phase q's loads (activation codes and scales, then the weights' scale group when q % 4 == 0, then
 // the weight codes) are issued right after phase q - D has been contracted, so D phases' bytes are
 // always in flight and the register footprint is that of D phases.  Every index is a compile-time
@@ -378,12 +380,32 @@ gemm_skinny_long_kernel(GemmArgs p, int ncols) {
   const uint8_t* const ac = p.a_codes + arow * kb + g * 16;
   const uint8_t* const asb = p.a_scales + arow * ks;
 
+  // Weight codes of a phase pair come as whole 128-byte lines: the load of the pair's first phase
+  // brings rows 0..7 of the tile and that of its second rows 8..15, lane L holding piece L % 8 of
+  // row L / 8; at the pair's first phase each lane writes its piece to the wavefront's LDS area
+  // (piece h of row r at slot h ^ (r % 8) ^ (r / 8): conflict-free writes and reads) and reads back
+  // its fragments of both phases.  An unpaired last phase loads its fragments directly.
+  constexpr int kPaired = NPH - NPH % 2;
+  __shared__ __attribute__((aligned(16))) uint8_t xpose[kSkinnyWaves][T * 2048];
+  int lrow[T][2];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) lrow[t][i] = min(c0 + t * 16 + 8 * i + (lane >> 3), clast);
+  const int wslot0 = (lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3)) * 16);
+  const int wslot1 = 1024 + (lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3) ^ 1) * 16);
+  const int r8 = r & 7, ri = r >> 3;
+  const int rslot0 = ri * 1024 + r8 * 128 + ((g ^ r8 ^ ri) * 16);
+  const int rslot1 = ri * 1024 + r8 * 128 + (((4 + g) ^ r8 ^ ri) * 16);
+  uint8_t* const xw = xpose[wave];
+
   constexpr int kSq = (NPH + 3) / 4;
   uint4 aq[NPH];
   uint32_t as2[NPH];
   uint2 asq[kSq];
   uint2 sq[kSq][T];
   uint4 wq[NPH][T];
+  uint4 wodd[T];  // the fragments of a pair's second phase, read with the first's
   auto issue = [&](int q) {
     aq[q] = load16(ac + chunk_of<NPH>(q, wave) * 64);
     if constexpr (ASPREAD) {
@@ -398,7 +420,14 @@ gemm_skinny_long_kernel(GemmArgs p, int ncols) {
         sq[q / 4][t] = load8(p.w_scales + wrow[t] * ks + chunk_of<NPH>(min(q + g, NPH - 1), wave) * 8);
     }
 #pragma unroll
-    for (int t = 0; t < T; ++t) wq[q][t] = load16(p.w_codes + wrow[t] * kb + chunk_of<NPH>(q, wave) * 64 + g * 16);
+    for (int t = 0; t < T; ++t) {
+      if (q < kPaired) {
+        // whole lines: rows 8 (q % 2) .. + 7 of the tile, the wavefront's 128 bytes of the pair
+        wq[q][t] = load16(p.w_codes + lrow[t][q % 2] * kb + (q / 2) * 1024 + wave * 128 + (lane & 7) * 16);
+      } else {
+        wq[q][t] = load16(p.w_codes + wrow[t] * kb + chunk_of<NPH>(q, wave) * 64 + g * 16);
+      }
+    }
   };
 
 #pragma unroll
@@ -430,8 +459,28 @@ gemm_skinny_long_kernel(GemmArgs p, int ncols) {
 #pragma unroll
       for (int t = 0; t < T; ++t) pin(sq[q / 4][t]);
     }
+    uint4 wf[T];
+    if (q < kPaired && q % 2 == 0) {
+      // the pair's lines through the LDS area into fragments of both phases
 #pragma unroll
-    for (int t = 0; t < T; ++t) pin(wq[q][t]);
+      for (int t = 0; t < T; ++t) {
+        pin(wq[q][t]);
+        pin(wq[q + 1][t]);
+        *reinterpret_cast<uint4*>(xw + t * 2048 + wslot0) = wq[q][t];
+        *reinterpret_cast<uint4*>(xw + t * 2048 + wslot1) = wq[q + 1][t];
+        wf[t] = *reinterpret_cast<const uint4*>(xw + t * 2048 + rslot0);
+        wodd[t] = *reinterpret_cast<const uint4*>(xw + t * 2048 + rslot1);
+      }
+    } else if (q < kPaired) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) wf[t] = wodd[t];
+    } else {
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        pin(wq[q][t]);
+        wf[t] = wq[q][t];
+      }
+    }
     const uint32_t sa_bits = ASPREAD ? pick_scales(asq[q / 4], q, r, g) : as2[q] >> ((g & 1) * 16);
     const half2_t sa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sa_bits & keep, 1.0f, false);
     const uint32_t a4[4] = {aq[q].x & keep, aq[q].y & keep, aq[q].z & keep, aq[q].w & keep};
@@ -442,7 +491,7 @@ gemm_skinny_long_kernel(GemmArgs p, int ncols) {
     for (int t = 0; t < T; ++t) {
       const half2_t sw =
           __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pick_scales(sq[q / 4][t], q, r, g), 1.0f, false);
-      const uint32_t w4[4] = {wq[q][t].x, wq[q][t].y, wq[q][t].z, wq[q][t].w};
+      const uint32_t w4[4] = {wf[t].x, wf[t].y, wf[t].z, wf[t].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const half8_t bv = decode8(w4[j], j < 2 ? sw[0] : sw[1]);
@@ -594,9 +643,8 @@ hipError_t launch_gemm_skinny_encode(const GemmArgs& a, const void* x, nvfp4_dty
 }
 
 // Decode-shaped products.  Up to 32 columns per compute unit and K up to kSkinnyMaxK: the one-pass
-// kernel.  K up to kStreamMaxK with up to 16 columns per compute unit, or up to 32 with at most 4
-// activation rows: its long-K form.  More columns (or more rows on two tiles of a long K): the
-// streaming kernels (gemm_stream.hip), which stream weight copies through LDS.  K beyond
+// kernel; K up to kStreamMaxK: its long-K form.  More columns: the streaming kernels
+// (gemm_stream.hip), which stream weight copies through LDS.  K beyond
 // kStreamMaxK (f32 output only): the streaming kernel on the fewest pieces of K of at most 8
 // phases, as equal as possible; the first piece writes C and each later one, launched after it on
 // the same stream, adds its scaled partial product: C = fl(...fl(acc_0 a) + acc_1 a ...).  The
@@ -609,10 +657,7 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
   const int per_cu = (a.N + cus - 1) / cus;
   if (a.K <= kSkinnyMaxK && per_cu <= 32)
     return launch_skinny_piece<-1>(a, DecodeEncode{nullptr, 0, nullptr, nullptr}, cus, stream);
-  // long K: the register-streaming form for one tile per workgroup, or two with at most 4
-  // activation rows; with more rows on two tiles the column-pair streaming form measured faster
-  if (a.K <= kStreamMaxK && (per_cu <= 16 || (per_cu <= 32 && a.M <= 4)))
-    return launch_skinny_long(a, cus, stream);
+  if (a.K <= kStreamMaxK && per_cu <= 32) return launch_skinny_long(a, cus, stream);
   if (a.K <= kStreamMaxK) return launch_gemm_stream(a, stream);
   const int phases = a.K / kPhaseK;
   const int pieces = (phases + 7) / 8;

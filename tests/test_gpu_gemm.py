@@ -101,10 +101,9 @@ def test_decode_many_columns(M, N, K):
 def test_decode_even_column_share(M, N, K):
     # K above 8192 and more than 16 columns per compute unit (256 of them): workgroups own equal
     # column ranges (17 columns and a last workgroup of one; 33; 20, the MLP down projection's
-    # shape; 18), three fused modules.  Up to 32 columns and at most 4 rows: the decode kernel's
-    # long-K form with two tiles.  More rows, or more columns: the streaming kernel's column-pair
-    # form, groups of 32 columns whose 9, 20, 17 and 10 units of one group-phase end in closing
-    # runs of 3, 2, 2 and 4 units
+    # shape; 18), three fused modules.  Up to 32 columns: the decode kernel's long-K form with two
+    # tiles; 33 columns: the streaming kernel's column-pair form, groups of 32 columns whose 20
+    # units of one group-phase end in a closing run of 2 units
     a = random_matrix(M * 17 + N, M, K, outlier_cols=max(1, K // 300))
     wt = random_matrix(N * 5 + K, N, K, std=0.02)
     segs = [0, N // 3 + 7, N // 2 + 1, N]
@@ -240,8 +239,7 @@ def test_long_k_fused_equals_per_segment_calls_bitwise(M):
     fused = _gpu_product(ac, as_, ga, wc, ws, gw, segs)
     parts = [_gpu_product(ac, as_, ga, wc[segs[j]:segs[j + 1]], ws[segs[j]:segs[j + 1]], [gw[j]],
                           [0, sizes[j]]) for j in range(len(sizes))]
-    if M <= 4:  # with more rows the fused call's two-tile share runs the streaming kernel
-        assert np.array_equal(fused, np.concatenate(parts, axis=1))
+    assert np.array_equal(fused, np.concatenate(parts, axis=1))
     R = oracle.gemm_exact(ac, as_, ga, wc, ws, gw, segs)
     bound = oracle.gemm_abs_bound(ac, as_, ga, wc, ws, gw, segs)
     check_gemm(fused, R, bound, f"long K fused M={M}")

@@ -68,7 +68,8 @@ RAW_SHAPES = [
     (4, 9000, 2048, "streaming, cached form"),
     (2, 1000, 9216, "long-K decode, one tile per workgroup"),
     (3, 4500, 10240, "long-K decode, two tiles per workgroup"),
-    (8, 4500, 10240, "streaming, column-pair form"),
+    (8, 4500, 10240, "long-K decode, two tiles, 8 rows"),
+    (3, 8500, 10240, "streaming, column-pair form"),
     (2, 40, 33792, "K pieces adding into C"),
 ]
 
