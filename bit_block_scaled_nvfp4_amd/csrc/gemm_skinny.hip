@@ -521,6 +521,179 @@ gemm_skinny_long_kernel(GemmArgs p, int ncols) {
   }
 }
 
+// Many-column form (more than 32 columns per compute unit, K up to kWideMaxPhases phases): the
+// one-pass kernel's fragments, phase pairing, whole-line weight loads and scale loads, walking the
+// workgroup's ncols columns as up to kWideMaxTiles tiles of 16.  The activation's fragments of all
+// phases are decoded once and reused by every tile.  Tiles stream through registers kWideRing tiles
+// ahead: tile t + kWideRing's loads are issued once tile t has been contracted, into the register
+// set tile t used (the tile loop is unrolled over the ring, so every set is statically named and
+// each wait is for exactly the tile it needs; the loads of tiles past the last repeat the last
+// tile and are never used).  Each tile's 8 partial sums wait in LDS; after the last tile every
+// wavefront reduces its share of the tiles in the one-pass kernel's fixed order, so every element
+// is accumulated exactly as there.
+constexpr int kWideMaxTiles = 16;
+constexpr int kWideMaxPhases = 5;
+constexpr int kWideRing = 2;
+
+template <int NPH>
+struct WideTile {
+  uint4 w[NPH];              // weight codes (whole lines for paired phases)
+  uint2 s[(NPH + 3) / 4];    // weight scale words (phases g and 4 + g)
+};
+
+template <int NPH, bool ASPREAD>
+__global__ void __launch_bounds__(kSkinnyThreads)
+gemm_skinny_wide_kernel(GemmArgs p, int ncols) {
+  constexpr int kPaired = NPH - NPH % 2;
+  constexpr int kSq = (NPH + 3) / 4;
+  __shared__ floatx4_t partial[kWideMaxTiles][kSkinnyWaves][64];
+  __shared__ __attribute__((aligned(16))) uint8_t xpose[kSkinnyWaves][2048];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int c0 = blockIdx.x * ncols;
+  const int cend = min(c0 + ncols, p.N);
+  const int clast = cend - 1;
+  const int ntiles = (cend - c0 + 15) / 16;
+  const int64_t kb = p.k_pitch / 2, ks = p.k_pitch / 16;
+  const int arow = min(r, p.M - 1);
+  const uint32_t keep = r < p.M ? 0xFFFFFFFFu : 0u;
+
+  // the activation, loaded first (the same for every workgroup, so served from L2)
+  uint4 aq[NPH];
+  uint32_t as2[NPH];
+  uint2 asq[kSq];
+#pragma unroll
+  for (int q = 0; q < NPH; ++q) aq[q] = load16(p.a_codes + arow * kb + chunk_of<NPH>(q, wave) * 64 + g * 16);
+  if constexpr (ASPREAD) {
+#pragma unroll
+    for (int i = 0; i < kSq; ++i)
+      asq[i] = load8(p.a_scales + arow * ks + chunk_of<NPH>(min(4 * i + g, NPH - 1), wave) * 8);
+  } else {
+#pragma unroll
+    for (int q = 0; q < NPH; ++q)
+      as2[q] = *reinterpret_cast<const uint16_t*>(p.a_scales + arow * ks + chunk_of<NPH>(q, wave) * 8 + g * 2);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  auto issue_tile = [&](int t, WideTile<NPH>& L) {
+    const int base = c0 + min(t, ntiles - 1) * 16;
+    const int wrow = min(base + r, clast);
+#pragma unroll
+    for (int i = 0; i < kSq; ++i)
+      L.s[i] = load8(p.w_scales + wrow * ks + chunk_of<NPH>(min(4 * i + g, NPH - 1), wave) * 8);
+#pragma unroll
+    for (int q = 0; q < NPH; ++q) {
+      if (q < kPaired) {
+        const int lrow = min(base + 8 * (q % 2) + (lane >> 3), clast);
+        L.w[q] = load16(p.w_codes + lrow * kb + (q / 2) * 1024 + wave * 128 + (lane & 7) * 16);
+      } else {
+        L.w[q] = load16(p.w_codes + wrow * kb + chunk_of<NPH>(q, wave) * 64 + g * 16);
+      }
+    }
+  };
+
+  WideTile<NPH> ring[kWideRing];
+#pragma unroll
+  for (int k = 0; k < kWideRing; ++k) {
+    issue_tile(k, ring[k]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // the activation's fragments of every phase, decoded once (the weights are streaming in)
+  if constexpr (ASPREAD) {
+#pragma unroll
+    for (int q = 0; q < NPH; ++q) as2[q] = pick_scales(asq[q >> 2], q, r, g);
+  }
+  half8_t av[NPH][4];
+#pragma unroll
+  for (int q = 0; q < NPH; ++q) {
+    const half2_t sa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(as2[q] & keep, 1.0f, false);
+    const uint32_t a4[4] = {aq[q].x & keep, aq[q].y & keep, aq[q].z & keep, aq[q].w & keep};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) av[q][j] = decode8(a4[j], j < 2 ? sa[0] : sa[1]);
+  }
+
+  const int wslot0 = (lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3)) * 16);
+  const int wslot1 = 1024 + (lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3) ^ 1) * 16);
+  const int r8 = r & 7, ri = r >> 3;
+  const int rslot0 = ri * 1024 + r8 * 128 + ((g ^ r8 ^ ri) * 16);
+  const int rslot1 = ri * 1024 + r8 * 128 + (((4 + g) ^ r8 ^ ri) * 16);
+  uint8_t* const xw = xpose[wave];
+
+  // contract tile t from register set L (when t is a real tile), leave its partial sums in LDS,
+  // and load tile t + ring into L
+  auto tile_step = [&](int t, WideTile<NPH>& L) {
+    if (t < ntiles) {
+#pragma unroll
+      for (int i = 0; i < kSq; ++i) pin(L.s[i]);
+      floatx4_t acc = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int q = 0; q < NPH; q += 2) {
+        uint4 wf0, wf1;
+        if (q < kPaired) {
+          pin(L.w[q]);
+          pin(L.w[q + 1]);
+          *reinterpret_cast<uint4*>(xw + wslot0) = L.w[q];
+          *reinterpret_cast<uint4*>(xw + wslot1) = L.w[q + 1];
+          wf0 = *reinterpret_cast<const uint4*>(xw + rslot0);
+          wf1 = *reinterpret_cast<const uint4*>(xw + rslot1);
+        } else {
+          pin(L.w[q]);
+          wf0 = L.w[q];
+          wf1 = wf0;
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int qq = q + h;
+          if (qq < NPH) {
+            const uint4 wf = h ? wf1 : wf0;
+            const half2_t sw = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+                pick_scales(L.s[qq / 4], qq, r, g), 1.0f, false);
+            const uint32_t w4[4] = {wf.x, wf.y, wf.z, wf.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const half8_t bv = decode8(w4[j], j < 2 ? sw[0] : sw[1]);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[qq][j], bv, acc, 0, 0, 0);
+            }
+          }
+        }
+      }
+      partial[t][wave][lane] = acc;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    issue_tile(t + kWideRing, L);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // whole rounds of the ring (steps past the last tile only refill, with the last tile's bytes)
+  for (int t0 = 0; t0 < ntiles; t0 += kWideRing) {
+#pragma unroll
+    for (int k = 0; k < kWideRing; ++k) tile_step(t0 + k, ring[k]);
+  }
+
+  // every wavefront's loads have landed (the last refills repeat the last tile); reduce the tiles
+  // in the fixed order of the one-pass kernel: wavefront w takes tiles w, w + 8, ...
+  __syncthreads();
+  const float ga = p.a_g[0];
+  for (int t = wave; t < ntiles; t += kSkinnyWaves) {
+    floatx4_t sum = partial[t][0][lane];
+#pragma unroll
+    for (int w = 1; w < kSkinnyWaves; ++w) sum += partial[t][w][lane];
+    const int n = c0 + t * 16 + r;
+    if (n < cend) {
+      const float al = 1.0f / (ga * p.seg_g[column_segment(p.seg, n)]);
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int m = 4 * g + e4;
+        if (m < p.M) store_c(p.c, p.c_bf16, p.ldc, m, n, sum[e4] * al);
+      }
+    }
+  }
+}
+
 }  // namespace
 
 namespace {
@@ -566,6 +739,36 @@ hipError_t launch_skinny_piece(const GemmArgs& a, const DecodeEncode& e, int cus
     case 6: return f32enc ? hipErrorInvalidValue : launch_skinny_nph<(f32enc ? 1 : 6), XDT>(a, e, cus, stream);
     case 7: return f32enc ? hipErrorInvalidValue : launch_skinny_nph<(f32enc ? 1 : 7), XDT>(a, e, cus, stream);
     case 8: return f32enc ? hipErrorInvalidValue : launch_skinny_nph<(f32enc ? 1 : 8), XDT>(a, e, cus, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int NPH>
+hipError_t launch_skinny_wide_nph(const GemmArgs& a, int ncols, hipStream_t stream) {
+  const dim3 grid((a.N + ncols - 1) / ncols), block(kSkinnyThreads);
+  if (a.M > 4)
+    hipLaunchKernelGGL((gemm_skinny_wide_kernel<NPH, true>), grid, block, 0, stream, a, ncols);
+  else
+    hipLaunchKernelGGL((gemm_skinny_wide_kernel<NPH, false>), grid, block, 0, stream, a, ncols);
+  return hipGetLastError();
+}
+
+// More than 32 and at most 16 * kWideMaxTiles columns per compute unit, K up to kWideMaxPhases
+// phases.
+bool skinny_wide(const GemmArgs& a, int cus) {
+  const int per_cu = (a.N + cus - 1) / cus;
+  return per_cu > 32 && (per_cu + 15) / 16 <= kWideMaxTiles && a.K % kPhaseK == 0 &&
+         a.K / kPhaseK <= kWideMaxPhases;
+}
+
+hipError_t launch_skinny_wide(const GemmArgs& a, int cus, hipStream_t stream) {
+  const int ncols = (a.N + cus - 1) / cus;
+  switch (a.K / kPhaseK) {
+    case 1: return launch_skinny_wide_nph<1>(a, ncols, stream);
+    case 2: return launch_skinny_wide_nph<2>(a, ncols, stream);
+    case 3: return launch_skinny_wide_nph<3>(a, ncols, stream);
+    case 4: return launch_skinny_wide_nph<4>(a, ncols, stream);
+    case 5: return launch_skinny_wide_nph<5>(a, ncols, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -643,13 +846,15 @@ hipError_t launch_gemm_skinny_encode(const GemmArgs& a, const void* x, nvfp4_dty
 }
 
 // Decode-shaped products.  Up to 32 columns per compute unit and K up to kSkinnyMaxK: the one-pass
-// kernel; K up to kStreamMaxK: its long-K form.  More columns: the streaming kernels
-// (gemm_stream.hip), which stream weight copies through LDS.  K beyond
+// kernel; K up to kStreamMaxK: its long-K form.  More columns, up to 16 * kWideMaxTiles per compute
+// unit with K up to kWideMaxPhases phases: the many-column form.  Other shapes with more columns:
+// the streaming kernels (gemm_stream.hip), which stream weight copies through LDS.  K beyond
 // kStreamMaxK (f32 output only): the streaming kernel on the fewest pieces of K of at most 8
 // phases, as equal as possible; the first piece writes C and each later one, launched after it on
 // the same stream, adds its scaled partial product: C = fl(...fl(acc_0 a) + acc_1 a ...).  The
-// one-pass and long-K forms accumulate every element the same way as each other, the streaming
-// kernels in another order (one chunk per wavefront in each phase), within the same tolerance.
+// one-pass, long-K and many-column forms accumulate every element the same way as each other, the
+// streaming kernels in another order (one chunk per wavefront in each phase), within the same
+// tolerance.
 hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
   int cus = 0;
   hipError_t e = compute_units(cus);
@@ -658,6 +863,7 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
   if (a.K <= kSkinnyMaxK && per_cu <= 32)
     return launch_skinny_piece<-1>(a, DecodeEncode{nullptr, 0, nullptr, nullptr}, cus, stream);
   if (a.K <= kStreamMaxK && per_cu <= 32) return launch_skinny_long(a, cus, stream);
+  if (skinny_wide(a, cus)) return launch_skinny_wide(a, cus, stream);
   if (a.K <= kStreamMaxK) return launch_gemm_stream(a, stream);
   const int phases = a.K / kPhaseK;
   const int pieces = (phases + 7) / 8;

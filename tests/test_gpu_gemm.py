@@ -88,8 +88,9 @@ def test_decode_long_k(M, N, K):
 @pytest.mark.parametrize("M,N,K", [(1, 9000, 2048), (16, 8250, 1024), (5, 12345, 3072),
                                    (3, 8500, 4096), (16, 8250, 8192)])
 def test_decode_many_columns(M, N, K):
-    # more than 32 columns per compute unit: the streaming kernel walks several 16-column tiles per
-    # workgroup (ragged last tile), with 1 to 8 phases of K, two fused modules
+    # more than 32 columns per compute unit: the decode kernel's many-column form walks several
+    # 16-column tiles per workgroup (ragged last tile) up to 5 phases of K, the streaming kernel's
+    # cached form beyond (8 phases), two fused modules
     a = random_matrix(M * 13 + N, M, K, outlier_cols=3)
     wt = random_matrix(N + K, N, K, std=0.02)
     segs = [0, N // 2 + 5, N]
@@ -246,6 +247,24 @@ def test_long_k_fused_equals_per_segment_calls_bitwise(M):
     check_gemm(np.concatenate(parts, axis=1), R, bound, f"long K per segment M={M}")
 
 
+@pytest.mark.parametrize("M", [1, 16])
+def test_many_column_fused_equals_per_segment_calls_bitwise(M):
+    """More than 32 columns per compute unit fused (the many-column form), at most 32 per segment
+    (the one-pass form): every element is accumulated the same way, so the two agree bit for bit."""
+    K = 2048
+    sizes = [4096, 4096, 808]
+    segs = list(np.cumsum([0] + sizes))
+    a = random_matrix(70 + M, M, K, outlier_cols=20)
+    wt = random_matrix(71, segs[-1], K, std=0.02)
+    ac, as_, ga, wc, ws, gw = _encode(a, wt, segs)
+    fused = _gpu_product(ac, as_, ga, wc, ws, gw, segs)
+    parts = [_gpu_product(ac, as_, ga, wc[segs[j]:segs[j + 1]], ws[segs[j]:segs[j + 1]], [gw[j]],
+                          [0, sizes[j]]) for j in range(len(sizes))]
+    assert np.array_equal(fused, np.concatenate(parts, axis=1))
+    R = oracle.gemm_exact(ac, as_, ga, wc, ws, gw, segs)
+    check_gemm(fused, R, oracle.gemm_abs_bound(ac, as_, ga, wc, ws, gw, segs), f"many columns M={M}")
+
+
 def test_fused_equals_per_segment_calls_bitwise():
     M, K = 96, 512
     sizes = [64, 64, 128, 48, 48, 7]
@@ -387,6 +406,14 @@ def test_full_size_sampled(wid):
 @pytest.mark.parametrize("M", [1, 4, 16])
 def test_decode_shapes(M):
     _sampled_full_size(4, M)
+
+
+@pytest.mark.parametrize("wid,M", [(3, 1), (3, 16), (5, 1), (5, 16)])
+def test_mlp_decode_shapes_full_size(wid, M):
+    # decode steps on the full MLP weights: gate+up (34816 x 5120, two modules: the decode kernel's
+    # many-column form) and down (5120 x 17408 behind the fused SiLU(g) * u encode: its long-K
+    # form), every 256-column band sampled
+    _sampled_full_size(wid, M)
 
 
 def test_fused_equals_per_segment_calls_across_tile_shapes():

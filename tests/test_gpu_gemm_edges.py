@@ -8,8 +8,8 @@ every kernel the dispatch can choose, and on mid-size problems compared in full.
   and streaming kernels, a bit-level decode in the general one), so each is driven over the whole
   scale range: general (K % 64 != 0), tiled (odd and even numbers of 64-element K chunks), the
   one-pass decode kernel with one and two 16-column tiles per workgroup, its long-K form with one
-  and two tiles, the streaming kernel's cached and column-pair forms, and K split into pieces that
-  add into C.
+  and two tiles and its many-column form, the streaming kernel's cached and column-pair forms, and
+  K split into pieces that add into C.
 * Mid-size problems compared element by element over the whole output: more tiles than compute
   units with a tile count that is not a multiple of 8 (the persistent kernel's plain tile order),
   partial edge tiles, and an odd number of K chunks (the last chunk of a tile read from the first
@@ -65,7 +65,8 @@ RAW_SHAPES = [
     (1, 3000, 2048, "one-pass decode, one tile per workgroup"),
     (16, 6000, 2048, "one-pass decode, two tiles per workgroup"),
     (3, 8100, 8192, "one-pass decode, K = 8192"),
-    (4, 9000, 2048, "streaming, cached form"),
+    (4, 9000, 2048, "many-column decode form"),
+    (4, 9000, 8192, "streaming, cached form"),
     (2, 1000, 9216, "long-K decode, one tile per workgroup"),
     (3, 4500, 10240, "long-K decode, two tiles per workgroup"),
     (8, 4500, 10240, "long-K decode, two tiles, 8 rows"),
