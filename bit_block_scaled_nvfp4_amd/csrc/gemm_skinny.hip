@@ -31,10 +31,11 @@
 // phases ahead (gemm_skinny_long_kernel).  Rows of the activation at or past M are zero.
 //
 // Activation input.  Either its NVFP4 codes and scales (the product alone), or the raw activation
-// (f32, bf16 or f16) with its static global scale: then every workgroup first encodes the M x K
-// activation into LDS with the encoder's block routine (bit-identical codes and scales), workgroup
-// 0 also writes them out for the caller, and the lanes read their fragments from LDS.  That makes
-// a decode step's activation encode and product one launch.
+// (f32, bf16 or f16) with its static global scale: then every wavefront first encodes exactly the
+// blocks its own fragments need (its chunk of every phase, all M rows) with the encoder's block
+// routine (bit-identical codes and scales) into its own LDS area, the wavefronts of workgroup 0
+// also write theirs out for the caller, and the lanes read their fragments back -- no workgroup
+// barrier.  That makes a decode step's activation encode and product one launch.
 //
 // Reduction: the 8 wavefronts' partial 16x16 tiles of each tile are summed through LDS in a fixed
 // order (deterministic), scaled per column by 1 / (gA * gW[seg(n)]) and stored.  Every output
@@ -107,20 +108,29 @@ constexpr int encode_words() {
   return 4 * codec::elem_bytes<XDT>();
 }
 
-// Load batch `base` (blocks base + j * threads + thread, j < B, clamped to the last block) of the
-// raw activation into registers.
-template <nvfp4_dtype XDT>
-__device__ __forceinline__ void encode_load(const GemmArgs& p, const DecodeEncode& e, int base,
+// The blocks a wavefront encodes are exactly those its fragments need: block b of its M * NPH * 8
+// is row b / (8 NPH), phase (b / 8) % NPH, block b % 8 of the wavefront's chunk of that phase.
+template <int NPH>
+__device__ __forceinline__ void wave_block(int b, int wave, int& row, int& col) {
+  row = b / (NPH * 8);
+  const int rem = b - row * (NPH * 8);
+  col = chunk_of<NPH>(rem >> 3, wave) * 128 + (rem & 7) * 16;  // element offset within the row
+}
+
+// Load batch `base` (this wavefront's blocks base + j * 64 + lane, j < B, clamped to its last
+// block) of the raw activation into registers.
+template <nvfp4_dtype XDT, int NPH>
+__device__ __forceinline__ void encode_load(const GemmArgs& p, const DecodeEncode& e, int wave,
+                                            int lane, int base,
                                             uint32_t (&raw)[kEncodeBatch][encode_words<XDT>()]) {
   constexpr int W = encode_words<XDT>();
-  const int bpr = p.K / 16;  // blocks per row
-  const int nblk = p.M * bpr;
+  const int nblk = p.M * NPH * 8;
   const uint8_t* const xb = reinterpret_cast<const uint8_t*>(e.x);
 #pragma unroll
   for (int j = 0; j < kEncodeBatch; ++j) {
-    const int b = min(base + j * kSkinnyThreads + (int)threadIdx.x, nblk - 1);
-    const int row = b / bpr, blk = b - row * bpr;
-    const uint8_t* src = xb + ((int64_t)row * e.ldx + (int64_t)blk * 16) * codec::elem_bytes<XDT>();
+    int row, col;
+    wave_block<NPH>(min(base + j * 64 + lane, nblk - 1), wave, row, col);
+    const uint8_t* src = xb + ((int64_t)row * e.ldx + col) * codec::elem_bytes<XDT>();
 #pragma unroll
     for (int i = 0; i < W / 4; ++i) {
       const uint4 v = *reinterpret_cast<const uint4*>(src + 16 * i);
@@ -132,26 +142,29 @@ __device__ __forceinline__ void encode_load(const GemmArgs& p, const DecodeEncod
   }
 }
 
-// Encode activation rows [0, M) x [0, K) with the static scale g into LDS (codes [M][K/2], scales
-// [M][K/16]) with the encoder's block routine, blocks spread over the workgroup's threads; workgroup
-// 0 also writes them to `e`.  `cur` holds the first batch, loaded by the caller before the weight
-// loads so that encoding it waits for nothing else; each later batch is loaded while the one
-// before it is encoded.
-template <nvfp4_dtype XDT>
+// Encode this wavefront's blocks of the activation with the static scale g and the encoder's block
+// routine into its own LDS area (codes [row][phase][64 bytes of its chunk], scales
+// [row][phase][8]), spread over its 64 lanes; the wavefronts of workgroup 0 also write their blocks
+// to `e` (together, the whole encoded activation).  No other wavefront reads the area, so no
+// barrier is needed: the wavefront's LDS accesses complete in order.  `cur` holds the first batch,
+// loaded by the caller before the weight loads so that encoding it waits for nothing else; each
+// later batch is loaded while the one before it is encoded.
+template <nvfp4_dtype XDT, int NPH>
 __device__ __forceinline__ void encode_activation(const GemmArgs& p, const DecodeEncode& e, float g,
+                                                  int wave, int lane,
                                                   uint32_t (&cur)[kEncodeBatch][encode_words<XDT>()],
                                                   uint8_t* lcodes, uint8_t* lscales) {
   constexpr int B = kEncodeBatch;
   constexpr int W = encode_words<XDT>();
   const float gs6 = g / 6.0f;
-  const int nblk = p.M * (p.K / 16);
+  const int nblk = p.M * NPH * 8;
   const bool out = blockIdx.x == 0 && e.codes != nullptr;
   uint32_t nxt[B][W];
-  for (int base = 0; base < nblk; base += B * kSkinnyThreads) {
-    if (base + B * kSkinnyThreads < nblk) encode_load<XDT>(p, e, base + B * kSkinnyThreads, nxt);
+  for (int base = 0; base < nblk; base += B * 64) {
+    if (base + B * 64 < nblk) encode_load<XDT, NPH>(p, e, wave, lane, base + B * 64, nxt);
 #pragma unroll
     for (int j = 0; j < B; ++j) {
-      const int b = base + j * kSkinnyThreads + (int)threadIdx.x;
+      const int b = base + j * 64 + lane;
       if (b >= nblk) continue;
       float v[16];
 #pragma unroll
@@ -171,8 +184,10 @@ __device__ __forceinline__ void encode_activation(const GemmArgs& p, const Decod
       *reinterpret_cast<uint2*>(lcodes + b * 8) = uint2{word[0], word[1]};
       lscales[b] = (uint8_t)sc;
       if (out) {
-        *reinterpret_cast<uint2*>(e.codes + (int64_t)b * 8) = uint2{word[0], word[1]};
-        e.scales[b] = (uint8_t)sc;
+        int row, col;
+        wave_block<NPH>(b, wave, row, col);
+        *reinterpret_cast<uint2*>(e.codes + (int64_t)row * (p.K / 2) + col / 2) = uint2{word[0], word[1]};
+        e.scales[(int64_t)row * (p.K / 16) + col / 16] = (uint8_t)sc;
       }
     }
 #pragma unroll
@@ -191,7 +206,9 @@ gemm_skinny_kernel(GemmArgs p, DecodeEncode e, int ncols) {
   constexpr bool kEncode = XDT >= 0;
   __shared__ floatx4_t partial[T][kSkinnyWaves][64];
   // the encoded activation (encoding form only): codes [M][K/2], scales [M][K/16]
-  __shared__ __attribute__((aligned(16))) uint8_t act[kEncode ? 16 * (kSkinnyMaxK / 2 + kSkinnyMaxK / 16) : 16];
+  // the encoded activation, each wavefront's own blocks (encoding form only): codes
+  // [row][phase][64], then scales [row][phase][8], for up to 16 rows
+  __shared__ __attribute__((aligned(16))) uint8_t act[kSkinnyWaves][kEncode ? 16 * NPH * 72 : 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -234,7 +251,7 @@ gemm_skinny_kernel(GemmArgs p, DecodeEncode e, int ncols) {
   uint32_t enc_raw[kEncodeBatch][encode_words<kXdt>()];
   if constexpr (kEncode) {
     enc_g = __builtin_nontemporal_load(p.a_g);
-    encode_load<kXdt>(p, e, 0, enc_raw);
+    encode_load<kXdt, NPH>(p, e, wave, lane, 0, enc_raw);
   }
   __builtin_amdgcn_sched_barrier(0);
   // weight scales of every phase, then the weight codes phase by phase (rows past the workgroup's
@@ -267,21 +284,13 @@ gemm_skinny_kernel(GemmArgs p, DecodeEncode e, int ncols) {
   __builtin_amdgcn_sched_barrier(0);
 
   if constexpr (kEncode) {
-    uint8_t* const lcodes = act;
-    uint8_t* const lscales = act + 16 * (p.K / 2);
-    encode_activation<kXdt>(p, e, enc_g, enc_raw, lcodes, lscales);
-    // LDS-only barrier: this wavefront's LDS writes are done (lgkmcnt 0), then the barrier; the
-    // weight loads stay in flight
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
+    uint8_t* const lcodes = act[wave];
+    uint8_t* const lscales = act[wave] + 16 * NPH * 64;
+    encode_activation<kXdt, NPH>(p, e, enc_g, wave, lane, enc_raw, lcodes, lscales);
 #pragma unroll
     for (int q = 0; q < NPH; ++q) {
-      aq[q] = *reinterpret_cast<const uint4*>(lcodes + arow * (p.K / 2) + chunk_of<NPH>(q, wave) * 64 + g * 16);
-      as2[q] = *reinterpret_cast<const uint16_t*>(lscales + arow * (p.K / 16) + chunk_of<NPH>(q, wave) * 8 + g * 2);
+      aq[q] = *reinterpret_cast<const uint4*>(lcodes + (arow * NPH + q) * 64 + g * 16);
+      as2[q] = *reinterpret_cast<const uint16_t*>(lscales + (arow * NPH + q) * 8 + g * 2);
     }
   }
 
