@@ -11,16 +11,16 @@
 //  * gemm_general_kernel: any K that is a multiple of 16.  One wavefront per 32x32 output tile,
 //    operands read straight from global memory 4 bytes (8 codes) per lane per K step.
 //  * gemm_tiled_kernel: K a multiple of 64.  A workgroup owns a BM x BN output tile (256 x 256 or
-//    256 x 192, chosen per problem); each K chunk of 64 is staged in LDS as raw 4-bit codes plus
+//    256 x 192, chosen per problem); each K chunk of 128 is staged in LDS as raw 4-bit codes plus
 //    E4M3 bytes (9/16 byte per element instead of 2 for f16, so staging costs a quarter of the LDS
 //    space and bandwidth of an f16 GEMM), then every wavefront decodes its own fragments in
-//    registers right before the MFMAs.
+//    registers right before the MFMAs, one sub-chunk of 64 at a time.
 //
 // K-slot permutation.  In a 32x32x16 MFMA, lane l supplies row (l % 32) and 8 of the 16 k-slots
-// (half h = l / 32).  Within a K chunk of 64, lane half h reads the 16 contiguous bytes holding
+// (half h = l / 32).  Within a sub-chunk of 64, lane half h reads the 16 contiguous bytes holding
 // elements [32h, 32h + 32) of its row and uses 32-bit word j of them in MFMA step j (j = 0..3).
-// A and W use the same map, so after 4 steps every k of the chunk has been contracted once.  Word
-// j covers elements 32h + 8j .. +7, which lie in 16-block 2h + j/2 of the chunk.
+// A and W use the same map, so after 4 steps every k of the sub-chunk has been contracted once.
+// Word j covers elements 32h + 8j .. +7, which lie in 16-block 2h + j/2 of the sub-chunk.
 #include <type_traits>
 
 #include "gemm_common.h"
@@ -77,24 +77,21 @@ struct TileCfg {
   static constexpr int kThreads = WAVES_M * WAVES_N * 64;
   static constexpr int BM = WAVES_M * FM * 32;
   static constexpr int BN = WAVES_N * FN * 32;
-  // scale words per lane group in LDS: a lane reads the words of its F fragments from one group
-  // of 4 (16 bytes) or 8 (32 bytes) slots
-  static constexpr int GA = FM <= 4 ? 4 : 8;
-  static constexpr int GB = FN <= 4 ? 4 : 8;
-  // one LDS stage: the codes of BM + BN rows (32 bytes each per K chunk of 64), then the scale
-  // slots of each operand (4 bytes per slot: one row's 4 scale bytes)
-  static constexpr int kCodesA = BM * 32;
-  static constexpr int kCodesB = BN * 32;
-  static constexpr int kScalesA = WAVES_M * 32 * GA * 4;
-  static constexpr int kScalesB = WAVES_N * 32 * GB * 4;
+  // one LDS stage holds a K chunk of 128: the codes of BM + BN rows (64 bytes each), then the
+  // scales of each operand (8 bytes each)
+  static constexpr int kCodesA = BM * 64;
+  static constexpr int kCodesB = BN * 64;
+  static constexpr int kScalesA = BM * 8;
+  static constexpr int kScalesB = BN * 8;
   static constexpr int kStage = kCodesA + kCodesB + kScalesA + kScalesB;
   // 16-byte code copies and 4-byte scale copies per thread per chunk (the last may be partial)
-  static constexpr int kPiecesA = (BM * 2 + kThreads - 1) / kThreads;
-  static constexpr int kPiecesB = (BN * 2 + kThreads - 1) / kThreads;
-  static constexpr int kWordsA = (kScalesA / 4 + kThreads - 1) / kThreads;
-  static constexpr int kWordsB = (kScalesB / 4 + kThreads - 1) / kThreads;
+  static constexpr int kPiecesA = (BM * 4 + kThreads - 1) / kThreads;
+  static constexpr int kPiecesB = (BN * 4 + kThreads - 1) / kThreads;
+  static constexpr int kWordsA = (BM * 2 + kThreads - 1) / kThreads;
+  static constexpr int kWordsB = (BN * 2 + kThreads - 1) / kThreads;
   static_assert(FM >= 1 && FM <= 8 && FN >= 1 && FN <= 8, "fragments per wavefront");
-  static_assert((BM * 2) % 64 == 0 && (BN * 2) % 64 == 0, "whole wavefronts of code copies");
+  static_assert((BM * 4) % 64 == 0 && (BN * 4) % 64 == 0, "whole wavefronts of code copies");
+  static_assert((BM * 2) % 64 == 0 && (BN * 2) % 64 == 0, "whole wavefronts of scale copies");
 };
 
 // Per-thread byte offsets of the global rows this thread copies (rows beyond the matrix are
@@ -107,87 +104,104 @@ struct RowOffsets {
   uint32_t sb[Cfg::kWordsB];
 };
 
-// LDS layout of one stage and the copy that fills it.  Copies are direct global->LDS: copy index
+// LDS layout of one stage and the copy that fills it.  Copies are direct memory->LDS: copy index
 // d = i * threads + tid lands at LDS slot d (16 bytes for codes, 4 bytes for scales), because the
-// 64 lanes of a wavefront write consecutive slots.  The layout is chosen by which global row each
-// copy index fetches:
-//  * codes: slot d holds row (d / 64) * 32 + (d % 32), bytes [16 * ((d % 64) / 32), +16) of the
-//    chunk.  Each 32-row group is 1 KiB laid out [half][row][16 B] -- exactly the order in which
-//    the 64 lanes of a fragment read it (lane l at 16 l): reads are contiguous, conflict-free.
-//  * scales: with F fragments per wavefront and lane groups of G >= F slots, slot
-//    d = (g * 32 + r) * G + i holds the 4 scale bytes of row g * 32 F + i * 32 + r (the lane of
-//    row r in wavefront group g, fragment i): the F words one lane needs sit in one group of 16 or
-//    32 bytes.  Padding slots (i >= F) repeat fragment F - 1's row and are never read.
-template <int F, int G>
-__device__ __forceinline__ int scale_slot_row(int d) {
-  const int g = d / (32 * G), r = (d / G) % 32, i = min(d % G, F - 1);
-  return g * 32 * F + i * 32 + r;
-}
+// 64 lanes of a wavefront write consecutive slots.  The layout is chosen by which global bytes
+// each copy index fetches, so that one wavefront copy reads few rows, many bytes each, and every
+// fragment read is conflict-free:
+//  * codes: slot d holds row (d / 128) * 32 + ((d / 64) % 2) * 16 + (d / 4) % 16, 16-byte piece
+//    (d % 4) ^ swz((d / 4) % 16) of the row's 64 bytes in the chunk.  A wavefront copy covers
+//    16 rows x 64 contiguous bytes; each 32-row group is 2 KiB.  Lane (r, h) of a fragment reads
+//    piece 2u + h of its row for sub-chunk u; the XOR swizzle puts the 16 rows of a half-group on
+//    distinct bank groups for every piece.
+//  * scales: slot d holds 4-byte word (d % 2) ^ ((d / 32) % 2) of row d / 2's 8 bytes in the
+//    chunk.  A wavefront copy covers 32 rows x 8 bytes; a lane reads its rows' word u for
+//    sub-chunk u, and the swap on the second 16 rows of each 32 keeps those reads conflict-free.
+__host__ __device__ constexpr int piece_swizzle(int row16) { return ((row16 >> 1) ^ (row16 >> 3)) & 3; }
 
 template <class Cfg, int FM, int FN>
 __device__ __forceinline__ void row_offsets(const GemmArgs& p, int m0, int n0, int tid,
                                             RowOffsets<Cfg>& o) {
   const uint32_t kb = (uint32_t)p.K / 2, ks = (uint32_t)p.K / 16;
+  auto code_row = [](int d) { return (d >> 7) * 32 + ((d >> 6) & 1) * 16 + ((d >> 2) & 15); };
+  auto code_piece = [](int d) { return (d & 3) ^ piece_swizzle((d >> 2) & 15); };
+  auto scale_word = [](int d) { return (d & 1) ^ ((d >> 5) & 1); };
 #pragma unroll
   for (int i = 0; i < Cfg::kPiecesA; ++i) {
     const int d = tid + i * Cfg::kThreads;
-    const int row = (d >> 6) * 32 + (d & 31);
-    o.a[i] = (uint32_t)min(m0 + row, p.M - 1) * kb + ((d >> 5) & 1) * 16;
+    o.a[i] = (uint32_t)min(m0 + code_row(d), p.M - 1) * kb + code_piece(d) * 16;
   }
 #pragma unroll
   for (int i = 0; i < Cfg::kPiecesB; ++i) {
     const int d = tid + i * Cfg::kThreads;
-    const int row = (d >> 6) * 32 + (d & 31);
-    o.b[i] = (uint32_t)min(n0 + row, p.N - 1) * kb + ((d >> 5) & 1) * 16;
+    o.b[i] = (uint32_t)min(n0 + code_row(d), p.N - 1) * kb + code_piece(d) * 16;
   }
 #pragma unroll
-  for (int i = 0; i < Cfg::kWordsA; ++i)
-    o.sa[i] = (uint32_t)min(m0 + scale_slot_row<FM, Cfg::GA>(tid + i * Cfg::kThreads), p.M - 1) * ks;
+  for (int i = 0; i < Cfg::kWordsA; ++i) {
+    const int d = tid + i * Cfg::kThreads;
+    o.sa[i] = (uint32_t)min(m0 + (d >> 1), p.M - 1) * ks + scale_word(d) * 4;
+  }
 #pragma unroll
-  for (int i = 0; i < Cfg::kWordsB; ++i)
-    o.sb[i] = (uint32_t)min(n0 + scale_slot_row<FN, Cfg::GB>(tid + i * Cfg::kThreads), p.N - 1) * ks;
+  for (int i = 0; i < Cfg::kWordsB; ++i) {
+    const int d = tid + i * Cfg::kThreads;
+    o.sb[i] = (uint32_t)min(n0 + (d >> 1), p.N - 1) * ks + scale_word(d) * 4;
+  }
 }
 
-// Issue the direct global->LDS copies of K chunk `kc` into `stage`.  A wavefront whose copy
-// slots of the last, partial round lie past the area skips that copy (the test is uniform across
-// the wavefront).
+// Copies go through buffer loads, whose range check returns zeros instead of touching memory
+// past an operand: a chunk of 128 that extends past K (K an odd multiple of 64) reads the next
+// row's first bytes, or zeros past the last row, into LDS slots that are never used.  Each chunk's
+// resource starts at the chunk (base + chunk offset, size reduced by as much), so the whole
+// per-lane offset is range-checked.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const uint8_t* base, int64_t bytes,
+                                                           int offset) {
+  // raw buffer (stride 0), 32-bit data format word of the gfx9 resource descriptor
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base) + offset, (short)0,
+                                           (int)(bytes - offset), 0x00020000);
+}
+
+template <int BYTES>  // 16 or 4
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint8_t* lds) {
+  auto* const dst = (__attribute__((address_space(3))) void*)lds;
+  if constexpr (BYTES == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, (int)voff, 0, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, (int)voff, 0, 0, 0);
+}
+
+// Issue the direct memory->LDS copies of K chunk `kc` (of 128) into `stage`.  A wavefront whose
+// copy slots of the last, partial round lie past the area skips that copy (the test is uniform
+// across the wavefront).
 template <class Cfg>
 __device__ __forceinline__ void issue_chunk(const GemmArgs& p, const RowOffsets<Cfg>& o, int kc,
                                             uint8_t* stage) {
-  // the wavefront's first copy slot and the chunk's global base are uniform: scalar registers, so
-  // each copy is a scalar base plus this lane's 32-bit row offset
+  // the wavefront's first copy slot and the resources are uniform (scalar registers); each copy
+  // is a resource plus this lane's 32-bit row offset
   const int wave_slot = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * 64;
-  const uint8_t* const ac = p.a_codes + kc * 32;
-  const uint8_t* const wc = p.w_codes + kc * 32;
-  const uint8_t* const as = p.a_scales + kc * 4;
-  const uint8_t* const ws = p.w_scales + kc * 4;
+  const int64_t kb = p.K / 2, ks = p.K / 16;
+  const __amdgpu_buffer_rsrc_t ac = chunk_rsrc(p.a_codes, p.M * kb, kc * 64);
+  const __amdgpu_buffer_rsrc_t wc = chunk_rsrc(p.w_codes, p.N * kb, kc * 64);
+  const __amdgpu_buffer_rsrc_t as = chunk_rsrc(p.a_scales, p.M * ks, kc * 8);
+  const __amdgpu_buffer_rsrc_t ws = chunk_rsrc(p.w_scales, p.N * ks, kc * 8);
 #pragma unroll
   for (int i = 0; i < Cfg::kPiecesA; ++i)
-    if ((i + 1) * Cfg::kThreads <= Cfg::BM * 2 || i * Cfg::kThreads + wave_slot < Cfg::BM * 2)
-      __builtin_amdgcn_global_load_lds(ac + o.a[i], stage + (i * Cfg::kThreads + wave_slot) * 16,
-                                       16, 0, 0);
+    if ((i + 1) * Cfg::kThreads <= Cfg::BM * 4 || i * Cfg::kThreads + wave_slot < Cfg::BM * 4)
+      copy_to_lds<16>(ac, o.a[i], stage + (i * Cfg::kThreads + wave_slot) * 16);
 #pragma unroll
   for (int i = 0; i < Cfg::kPiecesB; ++i)
-    if ((i + 1) * Cfg::kThreads <= Cfg::BN * 2 || i * Cfg::kThreads + wave_slot < Cfg::BN * 2)
-      __builtin_amdgcn_global_load_lds(wc + o.b[i],
-                                       stage + Cfg::kCodesA + (i * Cfg::kThreads + wave_slot) * 16,
-                                       16, 0, 0);
+    if ((i + 1) * Cfg::kThreads <= Cfg::BN * 4 || i * Cfg::kThreads + wave_slot < Cfg::BN * 4)
+      copy_to_lds<16>(wc, o.b[i], stage + Cfg::kCodesA + (i * Cfg::kThreads + wave_slot) * 16);
 #pragma unroll
   for (int i = 0; i < Cfg::kWordsA; ++i)
-    if ((i + 1) * Cfg::kThreads * 4 <= Cfg::kScalesA ||
-        (i * Cfg::kThreads + wave_slot) * 4 < Cfg::kScalesA)
-      __builtin_amdgcn_global_load_lds(as + o.sa[i],
-                                       stage + Cfg::kCodesA + Cfg::kCodesB +
-                                           (i * Cfg::kThreads + wave_slot) * 4,
-                                       4, 0, 0);
+    if ((i + 1) * Cfg::kThreads <= Cfg::BM * 2 || i * Cfg::kThreads + wave_slot < Cfg::BM * 2)
+      copy_to_lds<4>(as, o.sa[i],
+                     stage + Cfg::kCodesA + Cfg::kCodesB + (i * Cfg::kThreads + wave_slot) * 4);
 #pragma unroll
   for (int i = 0; i < Cfg::kWordsB; ++i)
-    if ((i + 1) * Cfg::kThreads * 4 <= Cfg::kScalesB ||
-        (i * Cfg::kThreads + wave_slot) * 4 < Cfg::kScalesB)
-      __builtin_amdgcn_global_load_lds(ws + o.sb[i],
-                                       stage + Cfg::kCodesA + Cfg::kCodesB + Cfg::kScalesA +
-                                           (i * Cfg::kThreads + wave_slot) * 4,
-                                       4, 0, 0);
+    if ((i + 1) * Cfg::kThreads <= Cfg::BN * 2 || i * Cfg::kThreads + wave_slot < Cfg::BN * 2)
+      copy_to_lds<4>(ws, o.sb[i],
+                     stage + Cfg::kCodesA + Cfg::kCodesB + Cfg::kScalesA +
+                         (i * Cfg::kThreads + wave_slot) * 4);
 }
 
 // Tile order: hardware hands workgroup ids to the 8 XCDs round-robin, so id b runs on XCD b % 8.
@@ -210,9 +224,8 @@ __device__ __forceinline__ void tile_coords(uint32_t bid, uint32_t tiles_m, uint
   tn = in_group / gsize;
 }
 
-// One K chunk of a wavefront's fragments, read from LDS: FM + FN code words of 16 bytes (32
-// codes) and the scale words of each fragment row (one 16-byte read per operand, a second 4-byte
-// read for a fifth fragment).
+// One sub-chunk (K = 64) of a wavefront's fragments, read from LDS: FM + FN code words of 16
+// bytes (32 codes) and one 4-byte scale word (four E4M3 bytes) per fragment row.
 template <int FM, int FN>
 struct Frags {
   uint4 qa[FM];
@@ -221,29 +234,41 @@ struct Frags {
   uint32_t sb[FN];
 };
 
-template <int F>
-__device__ __forceinline__ void read_scale_words(const uint8_t* p, uint32_t (&w)[F]) {
-  const uint4 v = *reinterpret_cast<const uint4*>(p);
-  const uint32_t x[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < (F < 4 ? F : 4); ++i) w[i] = x[i];
-  if constexpr (F > 4) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p + 16);
-    const uint32_t y[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 4; i < F; ++i) w[i] = y[i - 4];
-  }
+// Byte offsets of this lane's reads within a stage: fragment 0 of each operand for sub-chunk 0
+// (sub-chunk 1 is the same XOR 32 for codes, XOR 4 for scales); fragment i adds i * 2048 (codes)
+// or i * 256 (scales).
+struct FragOffsets {
+  int a_frag, b_frag, a_scl, b_scl;
+};
+
+template <class Cfg, int FM, int FN>
+__device__ __forceinline__ FragOffsets frag_offsets(int wm, int wn, int lane) {
+  const int r = lane & 31, h = lane >> 5;
+  const int row16 = r & 15;
+  const int in_group = (r >> 4) * 1024 + row16 * 64 + ((h ^ piece_swizzle(row16)) * 16);
+  const int in_scales = r * 8 + ((r >> 4) & 1) * 4;
+  return FragOffsets{wm * FM * 2048 + in_group, Cfg::kCodesA + wn * FN * 2048 + in_group,
+                     Cfg::kCodesA + Cfg::kCodesB + wm * FM * 256 + in_scales,
+                     Cfg::kCodesA + Cfg::kCodesB + Cfg::kScalesA + wn * FN * 256 + in_scales};
+}
+
+template <int U>
+__device__ __forceinline__ FragOffsets sub_chunk(const FragOffsets& o) {
+  if constexpr (U == 0) return o;
+  return FragOffsets{o.a_frag ^ 32, o.b_frag ^ 32, o.a_scl ^ 4, o.b_scl ^ 4};
 }
 
 template <int FM, int FN>
-__device__ __forceinline__ void read_frags(const uint8_t* stage, int a_frag, int b_frag, int a_scl,
-                                           int b_scl, Frags<FM, FN>& f) {
+__device__ __forceinline__ void read_frags(const uint8_t* stage, const FragOffsets& o,
+                                           Frags<FM, FN>& f) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i) f.qa[i] = *reinterpret_cast<const uint4*>(stage + a_frag + i * 1024);
+  for (int i = 0; i < FM; ++i) f.qa[i] = *reinterpret_cast<const uint4*>(stage + o.a_frag + i * 2048);
 #pragma unroll
-  for (int j = 0; j < FN; ++j) f.qb[j] = *reinterpret_cast<const uint4*>(stage + b_frag + j * 1024);
-  read_scale_words<FM>(stage + a_scl, f.sa);
-  read_scale_words<FN>(stage + b_scl, f.sb);
+  for (int j = 0; j < FN; ++j) f.qb[j] = *reinterpret_cast<const uint4*>(stage + o.b_frag + j * 2048);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) f.sa[i] = *reinterpret_cast<const uint32_t*>(stage + o.a_scl + i * 256);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) f.sb[j] = *reinterpret_cast<const uint32_t*>(stage + o.b_scl + j * 256);
 }
 
 template <int STEP>
@@ -299,15 +324,15 @@ __device__ __forceinline__ void decode_scales(const Frags<FM, FN>& f, uint32_t s
 
 // Wait until this wavefront's copies of the chunk in `stage` have landed, meet the other
 // wavefronts (after which the chunk is complete in LDS and every wavefront has read its fragments
-// of the chunk before it), and read this lane's fragments.  The scheduling fences keep the work
-// issued before this point ahead of the wait.
+// of the chunk before it), and read this lane's fragments of its first sub-chunk.  The scheduling
+// fences keep the work issued before this point ahead of the wait.
 template <int FM, int FN>
-__device__ __forceinline__ void sync_and_read(const uint8_t* stage, int a_frag, int b_frag,
-                                              int a_scl, int b_scl, Frags<FM, FN>& f) {
+__device__ __forceinline__ void sync_and_read(const uint8_t* stage, const FragOffsets& o,
+                                              Frags<FM, FN>& f) {
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0)
   __builtin_amdgcn_s_barrier();
-  read_frags(stage, a_frag, b_frag, a_scl, b_scl, f);
+  read_frags(stage, o, f);
 }
 
 // MFMAs k = FROM .. TO-1 of one step, k = i * FN + j.
@@ -320,42 +345,48 @@ __device__ __forceinline__ void mfma_range(const half8_t (&av)[FM], const half8_
         __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[k % FN], av[k / FN], acc[k / FN][k % FN], 0, 0, 0);
 }
 
-// MFMAs of step 2 issued before the mid-chunk barrier: they keep the matrix core busy while the
-// wavefronts meet.
+// MFMAs of step 2 issued before the mid-sub-chunk hand-over: they keep the matrix core busy while
+// the wavefronts meet.
 constexpr int kPreBarrierMfma = 4;
 
-// Schedule of the MFMAs after the mid-chunk barrier: the next chunk's LDS reads (two per MFMA) and
-// the copies of the chunk after it go out between MFMAs, with the decode VALU spread over all of
-// them, rather than as one block in front of the MFMAs.
+// Schedule of the MFMAs after the hand-over: the next sub-chunk's LDS reads (two per MFMA) and the
+// copies of the chunk after the next go out between MFMAs, with the decode VALU spread over all
+// of them, rather than as one block in front of the MFMAs.
 template <int FM, int FN, int NDS, int NVM>
 __device__ __forceinline__ void interleave_after_barrier() {
   constexpr int kM = FM * FN - kPreBarrierMfma;
-  constexpr int kDsMfma = (NDS + 1) / 2;  // MFMAs carrying two LDS reads
-  constexpr int kValu = (8 * (FM + FN) + NVM + kM - 1) / kM + 1;
+  constexpr int kDsMfma = (NDS + 1) / 2;          // MFMAs carrying two LDS reads
+  constexpr int kVmPerMfma = (NVM + kM - 1) / kM;  // copies per MFMA (the last group may be short)
+  constexpr int kValu = (8 * (FM + FN) + kM - 1) / kM + 1;
 #pragma unroll
   for (int k = 0; k < kM; ++k) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     if (k < kDsMfma) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
-    else if (k - kDsMfma < NVM) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM
+    if constexpr (NVM > 0) {  // VMEM
+      if ((k + 1) * kVmPerMfma <= NVM) __builtin_amdgcn_sched_group_barrier(0x010, kVmPerMfma, 0);
+      else if (k * kVmPerMfma < NVM) __builtin_amdgcn_sched_group_barrier(0x010, NVM % kVmPerMfma, 0);
+    }
     __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);  // VALU
   }
 }
 
-// One K chunk, software-pipelined with the next.  The MFMAs of steps 0-1 of chunk kc run under
-// the decode of steps 1-2.  The first MFMAs of step 2 are issued; then every wavefront waits for
-// its own copies of chunk kc+1 and meets the others at a barrier (chunk kc+1 is complete in LDS,
-// and every wavefront has read chunk kc, whose stage is free).  The remaining MFMAs of step 2 run
-// under the LDS reads of chunk kc+1's fragments, the copies of chunk kc+2 (`issue`, into chunk
-// kc's stage) and the decode of step 3; the MFMAs of step 3 run under the decode of the next
-// chunk's step 0.  On entry `cur` holds chunk kc's fragments and a0/b0 its decoded step 0; on exit
-// (HAS_NEXT) `nxt` holds chunk kc+1's fragments and a0/b0 its decoded step 0.
-template <bool HAS_NEXT, int NVM, int FM, int FN, class Issue>
+// One sub-chunk (K = 64), software-pipelined with the next.  The MFMAs of steps 0-1 run under the
+// decode of steps 1-2.  The first MFMAs of step 2 are issued; then comes the hand-over to the next
+// sub-chunk.  For the second sub-chunk of a chunk (SYNC), every wavefront first waits for its own
+// copies of the next chunk and meets the others at a barrier (the next chunk is complete in LDS,
+// and every wavefront has read the current chunk, whose stage is free); for the first sub-chunk,
+// the next one is already in the same stage.  The remaining MFMAs of step 2 run under the LDS reads
+// of the next sub-chunk's fragments (from `nstage` at offsets `no`), for SYNC the copies of the
+// chunk after the next (`issue`, into the current stage), and the decode of step 3; the MFMAs of
+// step 3 run under the decode of the next sub-chunk's step 0.  On entry `cur` holds this
+// sub-chunk's fragments and a0/b0 its decoded step 0; on exit (HAS_NEXT) `nxt` holds the next
+// sub-chunk's fragments and a0/b0 its decoded step 0.
+template <bool HAS_NEXT, bool SYNC, int NVM, int FM, int FN, class Issue>
 __device__ __forceinline__ void pipelined_chunk(const Frags<FM, FN>& cur, Frags<FM, FN>& nxt,
-                                                const uint8_t* nstage, int a_frag, int b_frag,
-                                                int a_scl, int b_scl, half2_t (&sa)[FM],
-                                                half2_t (&sb)[FN], half8_t (&a0)[FM],
-                                                half8_t (&b0)[FN], half8_t (&a1)[FM],
-                                                half8_t (&b1)[FN], uint32_t sh,
+                                                const uint8_t* nstage, const FragOffsets& no,
+                                                half2_t (&sa)[FM], half2_t (&sb)[FN],
+                                                half8_t (&a0)[FM], half8_t (&b0)[FN],
+                                                half8_t (&a1)[FM], half8_t (&b1)[FN], uint32_t sh,
                                                 floatx16 (&acc)[FM][FN], Issue&& issue) {
   mfma_step(a0, b0, acc);
   decode_step<1>(cur, sa, sb, a1, b1);
@@ -367,15 +398,17 @@ __device__ __forceinline__ void pipelined_chunk(const Frags<FM, FN>& cur, Frags<
   mfma_range<0, kPreBarrierMfma>(a0, b0, acc);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (HAS_NEXT) {
-    __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): this lane's copies of chunk kc+1 landed
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(nstage, a_frag, b_frag, a_scl, b_scl, nxt);
-    issue();
+    if constexpr (SYNC) {
+      __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): this lane's copies of the next chunk landed
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    read_frags(nstage, no, nxt);
+    if constexpr (SYNC) issue();
   }
   mfma_range<kPreBarrierMfma, FM * FN>(a0, b0, acc);
   decode_step<3>(cur, sa, sb, a1, b1);
-  interleave_after_barrier<FM, FN, HAS_NEXT ? FM + FN + 2 : 0, HAS_NEXT ? NVM : 0>();
+  interleave_after_barrier<FM, FN, HAS_NEXT ? 2 * (FM + FN) : 0, HAS_NEXT && SYNC ? NVM : 0>();
   __builtin_amdgcn_sched_barrier(0);
   mfma_step(a1, b1, acc);
   if constexpr (HAS_NEXT) {
@@ -486,15 +519,16 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const floatx16 (&a
 }
 
 // Main kernel, persistent: workgroup b runs tiles b, b + G, b + 2G, ... (G = grid size, at most
-// one workgroup per compute unit).  Two LDS stages filled by direct global->LDS copies, two
-// register sets of fragments.  In the middle of K chunk kc (after its second MFMA step) every
-// wavefront waits for its own copies of chunk kc+1, meets the others at a barrier (chunk kc+1 is
-// then complete in LDS and every wavefront has read chunk kc, whose stage is free), reads its
-// fragments of chunk kc+1, and issues the copies of chunk kc+2 into chunk kc's stage.  The
-// remaining MFMA steps of chunk kc then cover the LDS reads and the decode of chunk kc+1's first
-// step, so the matrix core does not idle across chunks.
-// The K loop is unrolled by 2 so each stage and register set is named statically; past the last
-// chunk, reads and copies are clamped to it (redundant, never used), keeping the loop branch-free.
+// one workgroup per compute unit).  Two LDS stages of one K chunk (128) each, filled by direct
+// memory->LDS copies; two register sets of fragments, one per sub-chunk (64).  In the middle of
+// the second sub-chunk of chunk kc every wavefront waits for its own copies of chunk kc+1, meets
+// the others at a barrier (chunk kc+1 is then complete in LDS and every wavefront has read chunk
+// kc, whose stage is free), reads its fragments of chunk kc+1's first sub-chunk, and issues the
+// copies of chunk kc+2 into chunk kc's stage; in the middle of the first sub-chunk it reads the
+// second sub-chunk's fragments from the same stage.  The remaining MFMA steps of each sub-chunk
+// cover those LDS reads and the decode of the next sub-chunk's first step, so the matrix core does
+// not idle across sub-chunks.  Past the last chunk, reads and copies are clamped to it (redundant,
+// never used), keeping the loop branch-free.
 // Between tiles, the copies of the next tile's first two chunks are issued before the stores of
 // the finished tile, so the store traffic and the next tile's first loads are in flight together.
 // Each lane copies into LDS slots of its own wavefront only, and waits for its own copies before
@@ -518,16 +552,14 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
   const int r = lane & 31;
   const uint32_t sh = 16u * (uint32_t)h;  // lane half h uses scale bytes 2h, 2h+1
   const uint32_t ntiles = tiles_m * tiles_n;
-  const int nchunks = p.K / 64;
-  const int last = nchunks - 1;
+  const int nsub = p.K / 64;            // sub-chunks of 64
+  const int last = (nsub + 1) / 2 - 1;  // last chunk of 128 (it may hold one sub-chunk)
   const float ga = *p.a_g;
   const bool vec = (p.ldc & 3) == 0;  // rows of C start 16-byte aligned (C itself is)
 
-  // LDS read offsets of this lane's fragments and scale groups (within a stage)
-  const int a_frag = (wm * FM) * 1024 + lane * 16;
-  const int b_frag = Cfg::kCodesA + (wn * FN) * 1024 + lane * 16;
-  const int a_scl = Cfg::kCodesA + Cfg::kCodesB + (wm * 32 + r) * Cfg::GA * 4;
-  const int b_scl = Cfg::kCodesA + Cfg::kCodesB + Cfg::kScalesA + (wn * 32 + r) * Cfg::GB * 4;
+  // LDS read offsets of this lane's fragments (within a stage), for each sub-chunk
+  const FragOffsets fo = frag_offsets<Cfg, FM, FN>(wm, wn, lane);
+  const FragOffsets fo1 = sub_chunk<1>(fo);
 
   uint32_t v = blockIdx.x;
   uint32_t tmi, tni;
@@ -565,26 +597,32 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
     half2_t sa[FM], sb[FN];
     half8_t a0[FM], b0[FN], a1[FM], b1[FN];
 
-    // chunk 0 into registers (chunk 1 is already in flight into s1)
-    sync_and_read(s0, a_frag, b_frag, a_scl, b_scl, f0);
+    // chunk 0's first sub-chunk into registers (chunk 1 is already in flight into s1)
+    sync_and_read(s0, fo, f0);
     decode_scales(f0, sh, sa, sb);
     decode_step<0>(f0, sa, sb, a0, b0);
 
     constexpr int kCopies = Cfg::kPiecesA + Cfg::kPiecesB + Cfg::kWordsA + Cfg::kWordsB;
+    // One chunk: its first sub-chunk (in f0) with the second read from the same stage into f1,
+    // then the second sub-chunk (in f1) with the next chunk's first sub-chunk read into f0 after
+    // the barrier, and chunk kc+2 copied into this chunk's stage.  The stages are named statically
+    // (the loop runs two chunks per pass), so the compiler sees that reads of one stage do not
+    // alias the copies in flight into the other.
+    auto run_chunk = [&](uint8_t* stage, uint8_t* next_stage, int kc) {
+      pipelined_chunk<true, false, 0>(f0, f1, stage, fo1, sa, sb, a0, b0, a1, b1, sh, acc, [] {});
+      pipelined_chunk<true, true, kCopies>(f1, f0, next_stage, fo, sa, sb, a0, b0, a1, b1, sh, acc,
+                                           [&] { issue_chunk<Cfg>(p, ro, min(kc + 2, last), stage); });
+    };
     int kc = 0;
-    for (; kc + 1 < nchunks; kc += 2) {
-      // chunk kc (in f0; stage s0), chunk kc+1 in flight into s1
-      pipelined_chunk<true, kCopies>(f0, f1, s1, a_frag, b_frag, a_scl, b_scl, sa, sb, a0, b0,
-                                     a1, b1, sh, acc,
-                                     [&] { issue_chunk<Cfg>(p, ro, min(kc + 2, last), s0); });
-      // chunk kc+1 (in f1; stage s1), chunk kc+2 in flight into s0
-      pipelined_chunk<true, kCopies>(f1, f0, s0, a_frag, b_frag, a_scl, b_scl, sa, sb, a0, b0,
-                                     a1, b1, sh, acc,
-                                     [&] { issue_chunk<Cfg>(p, ro, min(kc + 3, last), s1); });
+    for (; 2 * kc + 3 < nsub; kc += 2) {
+      run_chunk(s0, s1, kc);
+      run_chunk(s1, s0, kc + 1);
     }
-    if (kc < nchunks)  // odd number of chunks: the last one is in f0
-      pipelined_chunk<false, kCopies>(f0, f1, s1, a_frag, b_frag, a_scl, b_scl, sa, sb, a0, b0,
-                                      a1, b1, sh, acc, [] {});
+    // 0 to 3 sub-chunks remain, the first in s0 (and in f0)
+    const int rest = nsub - 2 * kc;
+    if (rest >= 2) run_chunk(s0, s1, kc);
+    if (rest & 1)  // K an odd multiple of 64: the last chunk's only sub-chunk, in f0
+      pipelined_chunk<false, false, 0>(f0, f1, s0, fo, sa, sb, a0, b0, a1, b1, sh, acc, [] {});
     // this lane's redundant copies past the last chunk have landed before its stages are reused
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0x3F70);
@@ -597,10 +635,10 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
     v += gridDim.x;
     const bool more = v < ntiles;
     if (more) {
-      // With an odd number of chunks the last one was read from s0 after the last barrier; every
-      // wavefront must be past those reads before any copies of the next tile land in s0.  (With
-      // an even number, the last chunk's own barrier already orders them.)
-      if (nchunks & 1) __builtin_amdgcn_s_barrier();
+      // With an odd number of sub-chunks the last one was read from its stage after the last
+      // barrier; every wavefront must be past those reads before any copies of the next tile land
+      // there.  (With an even number, the last chunk's own barrier already orders them.)
+      if (nsub & 1) __builtin_amdgcn_s_barrier();
       tile_coords(v, tiles_m, tiles_n, tmi, tni);
       m0 = (int)tmi * Cfg::BM;
       n0 = (int)tni * Cfg::BN;

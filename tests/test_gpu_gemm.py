@@ -59,7 +59,8 @@ def test_workload1_full():
 
 @pytest.mark.parametrize("M,N,K", [
     (1, 1, 16), (1, 37, 64), (5, 70, 48), (33, 65, 80), (31, 129, 128), (64, 64, 64),
-    (129, 130, 192), (200, 300, 1024), (257, 255, 320), (96, 160, 5120),
+    (129, 130, 192), (200, 300, 1024), (257, 255, 320), (96, 160, 5120), (70, 90, 384),
+    (65, 200, 448),
     # decode-shaped (M <= 16): the skinny kernel for K a multiple of 1024 (in pieces above 8192),
     # the tiled or general kernel otherwise
     (1, 100, 512), (3, 77, 1536), (16, 40, 1024), (7, 33, 512), (16, 16, 2048), (5, 3, 16384),

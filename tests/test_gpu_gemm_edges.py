@@ -58,10 +58,13 @@ def _run(ac, as_, ga, wc, ws, gw, segs, what):
 RAW_SHAPES = [
     (40, 300, 2064, "general"),
     (33, 65, 48, "general, K = 48"),
-    (300, 260, 256, "tiled 256 x 192, 4 K chunks"),
-    (257, 513, 320, "tiled 256 x 192, 5 K chunks (odd)"),
+    (300, 260, 256, "tiled 256 x 192, 4 K sub-chunks: one pass of the two-chunk loop"),
+    (257, 513, 320, "tiled 256 x 192, 5 K sub-chunks: the loop, then a lone sub-chunk"),
+    (129, 200, 384, "tiled 256 x 192, 6 K sub-chunks: the loop, then one whole chunk"),
+    (300, 260, 448, "tiled 256 x 192, 7 K sub-chunks: the loop, a chunk and a lone sub-chunk"),
+    (65, 130, 192, "tiled 256 x 192, 3 K sub-chunks: no loop pass"),
     (17, 1000, 2048, "tiled 256 x 192, 17 rows"),
-    (4096, 4096, 128, "tiled 256 x 256, one full round"),
+    (4096, 4096, 128, "tiled 256 x 256, one full round, one K chunk"),
     (1, 3000, 2048, "one-pass decode, one tile per workgroup"),
     (16, 6000, 2048, "one-pass decode, two tiles per workgroup"),
     (3, 8100, 8192, "one-pass decode, K = 8192"),
