@@ -11,7 +11,7 @@
 //  * gemm_general_kernel: any K that is a multiple of 16.  One wavefront per 32x32 output tile,
 //    operands read straight from global memory 4 bytes (8 codes) per lane per K step.
 //  * gemm_tiled_kernel: K a multiple of 64.  A workgroup owns a BM x BN output tile (256 x 256 or
-//    256 x 192, chosen per problem); each K chunk of 128 is staged in LDS as raw 4-bit codes plus
+//    256 x 192, chosen per problem); each K chunk of 256 is staged in LDS as raw 4-bit codes plus
 //    E4M3 bytes (9/16 byte per element instead of 2 for f16, so staging costs a quarter of the LDS
 //    space and bandwidth of an f16 GEMM), then every wavefront decodes its own fragments in
 //    registers right before the MFMAs, one sub-chunk of 64 at a time.
@@ -77,21 +77,20 @@ struct TileCfg {
   static constexpr int kThreads = WAVES_M * WAVES_N * 64;
   static constexpr int BM = WAVES_M * FM * 32;
   static constexpr int BN = WAVES_N * FN * 32;
-  // one LDS stage holds a K chunk of 128: the codes of BM + BN rows (64 bytes each), then the
-  // scales of each operand (8 bytes each)
-  static constexpr int kCodesA = BM * 64;
-  static constexpr int kCodesB = BN * 64;
-  static constexpr int kScalesA = BM * 8;
-  static constexpr int kScalesB = BN * 8;
+  // one LDS stage holds a K chunk of 256: the codes of BM + BN rows (128 bytes each), then the
+  // scales of each operand (16 bytes each)
+  static constexpr int kCodesA = BM * 128;
+  static constexpr int kCodesB = BN * 128;
+  static constexpr int kScalesA = BM * 16;
+  static constexpr int kScalesB = BN * 16;
   static constexpr int kStage = kCodesA + kCodesB + kScalesA + kScalesB;
-  // 16-byte code copies and 4-byte scale copies per thread per chunk (the last may be partial)
-  static constexpr int kPiecesA = (BM * 4 + kThreads - 1) / kThreads;
-  static constexpr int kPiecesB = (BN * 4 + kThreads - 1) / kThreads;
-  static constexpr int kWordsA = (BM * 2 + kThreads - 1) / kThreads;
-  static constexpr int kWordsB = (BN * 2 + kThreads - 1) / kThreads;
+  // 16-byte copies per thread per chunk, of codes and of scales (the last may be partial)
+  static constexpr int kPiecesA = (BM * 8 + kThreads - 1) / kThreads;
+  static constexpr int kPiecesB = (BN * 8 + kThreads - 1) / kThreads;
+  static constexpr int kWordsA = (BM + kThreads - 1) / kThreads;
+  static constexpr int kWordsB = (BN + kThreads - 1) / kThreads;
   static_assert(FM >= 1 && FM <= 8 && FN >= 1 && FN <= 8, "fragments per wavefront");
-  static_assert((BM * 4) % 64 == 0 && (BN * 4) % 64 == 0, "whole wavefronts of code copies");
-  static_assert((BM * 2) % 64 == 0 && (BN * 2) % 64 == 0, "whole wavefronts of scale copies");
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "whole wavefronts of copies");
 };
 
 // Per-thread byte offsets of the global rows this thread copies (rows beyond the matrix are
@@ -105,27 +104,23 @@ struct RowOffsets {
 };
 
 // LDS layout of one stage and the copy that fills it.  Copies are direct memory->LDS: copy index
-// d = i * threads + tid lands at LDS slot d (16 bytes for codes, 4 bytes for scales), because the
-// 64 lanes of a wavefront write consecutive slots.  The layout is chosen by which global bytes
-// each copy index fetches, so that one wavefront copy reads few rows, many bytes each, and every
-// fragment read is conflict-free:
-//  * codes: slot d holds row (d / 128) * 32 + ((d / 64) % 2) * 16 + (d / 4) % 16, 16-byte piece
-//    (d % 4) ^ swz((d / 4) % 16) of the row's 64 bytes in the chunk.  A wavefront copy covers
-//    16 rows x 64 contiguous bytes; each 32-row group is 2 KiB.  Lane (r, h) of a fragment reads
-//    piece 2u + h of its row for sub-chunk u; the XOR swizzle puts the 16 rows of a half-group on
-//    distinct bank groups for every piece.
-//  * scales: slot d holds 4-byte word (d % 2) ^ ((d / 32) % 2) of row d / 2's 8 bytes in the
-//    chunk.  A wavefront copy covers 32 rows x 8 bytes; a lane reads its rows' word u for
-//    sub-chunk u, and the swap on the second 16 rows of each 32 keeps those reads conflict-free.
-__host__ __device__ constexpr int piece_swizzle(int row16) { return ((row16 >> 1) ^ (row16 >> 3)) & 3; }
+// d = i * threads + tid lands at LDS slot d (16 bytes), because the 64 lanes of a wavefront write
+// consecutive slots.  The layout is chosen by which global bytes each copy index fetches, so that
+// one wavefront copy reads whole 128-byte rows and every code fragment read is conflict-free:
+//  * codes: slot d holds row (d / 256) * 32 + (d / 8) % 32, 16-byte piece (d % 8) ^ swz((d / 8) %
+//    32) of the row's 128 bytes in the chunk.  A wavefront copy covers 8 rows x 128 bytes; each
+//    32-row group is 4 KiB.  Lane (r, h) of a fragment reads piece 2u + h of its row for sub-chunk
+//    u; the XOR swizzle puts any 8 consecutive rows on distinct bank groups for every piece.
+//  * scales: slot d holds row d's 16 scale bytes in the chunk (a wavefront copy covers 64 rows);
+//    a lane reads its rows' 4-byte word u for sub-chunk u.
+__host__ __device__ constexpr int piece_swizzle(int r) { return ((r >> 1) ^ (r << 2)) & 7; }
 
 template <class Cfg, int FM, int FN>
 __device__ __forceinline__ void row_offsets(const GemmArgs& p, int m0, int n0, int tid,
                                             RowOffsets<Cfg>& o) {
   const uint32_t kb = (uint32_t)p.K / 2, ks = (uint32_t)p.K / 16;
-  auto code_row = [](int d) { return (d >> 7) * 32 + ((d >> 6) & 1) * 16 + ((d >> 2) & 15); };
-  auto code_piece = [](int d) { return (d & 3) ^ piece_swizzle((d >> 2) & 15); };
-  auto scale_word = [](int d) { return (d & 1) ^ ((d >> 5) & 1); };
+  auto code_row = [](int d) { return (d >> 8) * 32 + ((d >> 3) & 31); };
+  auto code_piece = [](int d) { return (d & 7) ^ piece_swizzle((d >> 3) & 31); };
 #pragma unroll
   for (int i = 0; i < Cfg::kPiecesA; ++i) {
     const int d = tid + i * Cfg::kThreads;
@@ -137,19 +132,15 @@ __device__ __forceinline__ void row_offsets(const GemmArgs& p, int m0, int n0, i
     o.b[i] = (uint32_t)min(n0 + code_row(d), p.N - 1) * kb + code_piece(d) * 16;
   }
 #pragma unroll
-  for (int i = 0; i < Cfg::kWordsA; ++i) {
-    const int d = tid + i * Cfg::kThreads;
-    o.sa[i] = (uint32_t)min(m0 + (d >> 1), p.M - 1) * ks + scale_word(d) * 4;
-  }
+  for (int i = 0; i < Cfg::kWordsA; ++i)
+    o.sa[i] = (uint32_t)min(m0 + tid + i * Cfg::kThreads, p.M - 1) * ks;
 #pragma unroll
-  for (int i = 0; i < Cfg::kWordsB; ++i) {
-    const int d = tid + i * Cfg::kThreads;
-    o.sb[i] = (uint32_t)min(n0 + (d >> 1), p.N - 1) * ks + scale_word(d) * 4;
-  }
+  for (int i = 0; i < Cfg::kWordsB; ++i)
+    o.sb[i] = (uint32_t)min(n0 + tid + i * Cfg::kThreads, p.N - 1) * ks;
 }
 
 // Copies go through buffer loads, whose range check returns zeros instead of touching memory
-// past an operand: a chunk of 128 that extends past K (K an odd multiple of 64) reads the next
+// past an operand: a chunk of 256 that extends past K (K not a multiple of 256) reads the next
 // row's first bytes, or zeros past the last row, into LDS slots that are never used.  Each chunk's
 // resource starts at the chunk (base + chunk offset, size reduced by as much), so the whole
 // per-lane offset is range-checked.
@@ -169,7 +160,7 @@ __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t v
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, (int)voff, 0, 0, 0);
 }
 
-// Issue the direct memory->LDS copies of K chunk `kc` (of 128) into `stage`.  A wavefront whose
+// Issue the direct memory->LDS copies of K chunk `kc` (of 256) into `stage`.  A wavefront whose
 // copy slots of the last, partial round lie past the area skips that copy (the test is uniform
 // across the wavefront).
 template <class Cfg>
@@ -179,29 +170,29 @@ __device__ __forceinline__ void issue_chunk(const GemmArgs& p, const RowOffsets<
   // is a resource plus this lane's 32-bit row offset
   const int wave_slot = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * 64;
   const int64_t kb = p.K / 2, ks = p.K / 16;
-  const __amdgpu_buffer_rsrc_t ac = chunk_rsrc(p.a_codes, p.M * kb, kc * 64);
-  const __amdgpu_buffer_rsrc_t wc = chunk_rsrc(p.w_codes, p.N * kb, kc * 64);
-  const __amdgpu_buffer_rsrc_t as = chunk_rsrc(p.a_scales, p.M * ks, kc * 8);
-  const __amdgpu_buffer_rsrc_t ws = chunk_rsrc(p.w_scales, p.N * ks, kc * 8);
+  const __amdgpu_buffer_rsrc_t ac = chunk_rsrc(p.a_codes, p.M * kb, kc * 128);
+  const __amdgpu_buffer_rsrc_t wc = chunk_rsrc(p.w_codes, p.N * kb, kc * 128);
+  const __amdgpu_buffer_rsrc_t as = chunk_rsrc(p.a_scales, p.M * ks, kc * 16);
+  const __amdgpu_buffer_rsrc_t ws = chunk_rsrc(p.w_scales, p.N * ks, kc * 16);
 #pragma unroll
   for (int i = 0; i < Cfg::kPiecesA; ++i)
-    if ((i + 1) * Cfg::kThreads <= Cfg::BM * 4 || i * Cfg::kThreads + wave_slot < Cfg::BM * 4)
+    if ((i + 1) * Cfg::kThreads <= Cfg::BM * 8 || i * Cfg::kThreads + wave_slot < Cfg::BM * 8)
       copy_to_lds<16>(ac, o.a[i], stage + (i * Cfg::kThreads + wave_slot) * 16);
 #pragma unroll
   for (int i = 0; i < Cfg::kPiecesB; ++i)
-    if ((i + 1) * Cfg::kThreads <= Cfg::BN * 4 || i * Cfg::kThreads + wave_slot < Cfg::BN * 4)
+    if ((i + 1) * Cfg::kThreads <= Cfg::BN * 8 || i * Cfg::kThreads + wave_slot < Cfg::BN * 8)
       copy_to_lds<16>(wc, o.b[i], stage + Cfg::kCodesA + (i * Cfg::kThreads + wave_slot) * 16);
 #pragma unroll
   for (int i = 0; i < Cfg::kWordsA; ++i)
-    if ((i + 1) * Cfg::kThreads <= Cfg::BM * 2 || i * Cfg::kThreads + wave_slot < Cfg::BM * 2)
-      copy_to_lds<4>(as, o.sa[i],
-                     stage + Cfg::kCodesA + Cfg::kCodesB + (i * Cfg::kThreads + wave_slot) * 4);
+    if ((i + 1) * Cfg::kThreads <= Cfg::BM || i * Cfg::kThreads + wave_slot < Cfg::BM)
+      copy_to_lds<16>(as, o.sa[i],
+                      stage + Cfg::kCodesA + Cfg::kCodesB + (i * Cfg::kThreads + wave_slot) * 16);
 #pragma unroll
   for (int i = 0; i < Cfg::kWordsB; ++i)
-    if ((i + 1) * Cfg::kThreads <= Cfg::BN * 2 || i * Cfg::kThreads + wave_slot < Cfg::BN * 2)
-      copy_to_lds<4>(ws, o.sb[i],
-                     stage + Cfg::kCodesA + Cfg::kCodesB + Cfg::kScalesA +
-                         (i * Cfg::kThreads + wave_slot) * 4);
+    if ((i + 1) * Cfg::kThreads <= Cfg::BN || i * Cfg::kThreads + wave_slot < Cfg::BN)
+      copy_to_lds<16>(ws, o.sb[i],
+                      stage + Cfg::kCodesA + Cfg::kCodesB + Cfg::kScalesA +
+                          (i * Cfg::kThreads + wave_slot) * 16);
 }
 
 // Tile order: hardware hands workgroup ids to the 8 XCDs round-robin, so id b runs on XCD b % 8.
@@ -235,8 +226,8 @@ struct Frags {
 };
 
 // Byte offsets of this lane's reads within a stage: fragment 0 of each operand for sub-chunk 0
-// (sub-chunk 1 is the same XOR 32 for codes, XOR 4 for scales); fragment i adds i * 2048 (codes)
-// or i * 256 (scales).
+// (sub-chunk u is the same XOR 32 u for codes, plus 4 u for scales); fragment i adds i * 4096
+// (codes) or i * 512 (scales).
 struct FragOffsets {
   int a_frag, b_frag, a_scl, b_scl;
 };
@@ -244,31 +235,27 @@ struct FragOffsets {
 template <class Cfg, int FM, int FN>
 __device__ __forceinline__ FragOffsets frag_offsets(int wm, int wn, int lane) {
   const int r = lane & 31, h = lane >> 5;
-  const int row16 = r & 15;
-  const int in_group = (r >> 4) * 1024 + row16 * 64 + ((h ^ piece_swizzle(row16)) * 16);
-  const int in_scales = r * 8 + ((r >> 4) & 1) * 4;
-  return FragOffsets{wm * FM * 2048 + in_group, Cfg::kCodesA + wn * FN * 2048 + in_group,
-                     Cfg::kCodesA + Cfg::kCodesB + wm * FM * 256 + in_scales,
-                     Cfg::kCodesA + Cfg::kCodesB + Cfg::kScalesA + wn * FN * 256 + in_scales};
+  const int in_group = r * 128 + ((h ^ piece_swizzle(r)) * 16);
+  return FragOffsets{wm * FM * 4096 + in_group, Cfg::kCodesA + wn * FN * 4096 + in_group,
+                     Cfg::kCodesA + Cfg::kCodesB + (wm * FM * 32 + r) * 16,
+                     Cfg::kCodesA + Cfg::kCodesB + Cfg::kScalesA + (wn * FN * 32 + r) * 16};
 }
 
-template <int U>
-__device__ __forceinline__ FragOffsets sub_chunk(const FragOffsets& o) {
-  if constexpr (U == 0) return o;
-  return FragOffsets{o.a_frag ^ 32, o.b_frag ^ 32, o.a_scl ^ 4, o.b_scl ^ 4};
+__device__ __forceinline__ FragOffsets sub_chunk(const FragOffsets& o, int u) {
+  return FragOffsets{o.a_frag ^ (32 * u), o.b_frag ^ (32 * u), o.a_scl + 4 * u, o.b_scl + 4 * u};
 }
 
 template <int FM, int FN>
 __device__ __forceinline__ void read_frags(const uint8_t* stage, const FragOffsets& o,
                                            Frags<FM, FN>& f) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i) f.qa[i] = *reinterpret_cast<const uint4*>(stage + o.a_frag + i * 2048);
+  for (int i = 0; i < FM; ++i) f.qa[i] = *reinterpret_cast<const uint4*>(stage + o.a_frag + i * 4096);
 #pragma unroll
-  for (int j = 0; j < FN; ++j) f.qb[j] = *reinterpret_cast<const uint4*>(stage + o.b_frag + j * 2048);
+  for (int j = 0; j < FN; ++j) f.qb[j] = *reinterpret_cast<const uint4*>(stage + o.b_frag + j * 4096);
 #pragma unroll
-  for (int i = 0; i < FM; ++i) f.sa[i] = *reinterpret_cast<const uint32_t*>(stage + o.a_scl + i * 256);
+  for (int i = 0; i < FM; ++i) f.sa[i] = *reinterpret_cast<const uint32_t*>(stage + o.a_scl + i * 512);
 #pragma unroll
-  for (int j = 0; j < FN; ++j) f.sb[j] = *reinterpret_cast<const uint32_t*>(stage + o.b_scl + j * 256);
+  for (int j = 0; j < FN; ++j) f.sb[j] = *reinterpret_cast<const uint32_t*>(stage + o.b_scl + j * 512);
 }
 
 template <int STEP>
@@ -436,7 +423,12 @@ __device__ __forceinline__ int opaque_tid() {
 // of a wavefront execute in order, so no barrier is needed.  Rows and columns past the matrix are
 // masked at the store; a lane stores its four columns as one vector when they are all inside and
 // rows of C start 16-byte aligned (`vec`).
-constexpr int kEpiStride = 4 * 32 + 4;  // floats per staged row; the pad spreads rows over banks
+// Floats per staged row: the widest column group (4, 2 or 1 fragments of 32 columns) plus a pad
+// that spreads rows over banks.
+template <int FN>
+__host__ __device__ constexpr int epi_stride() {
+  return (FN >= 4 ? 4 : FN >= 2 ? 2 : 1) * 32 + 4;
+}
 
 template <bool BF16, int G, int J0, int FM, int FN>
 __device__ __forceinline__ void store_group(const GemmArgs& p, const floatx16 (&acc)[FM][FN],
@@ -444,7 +436,7 @@ __device__ __forceinline__ void store_group(const GemmArgs& p, const floatx16 (&
                                             int wn, int lane, bool vec, bool interior, int i) {
   using OutT = typename std::conditional<BF16, uint16_t, float>::type;
   OutT* const c = reinterpret_cast<OutT*>(p.c);
-  constexpr int S = kEpiStride;
+  constexpr int S = epi_stride<FN>();
   constexpr int LPR = G * 8;    // lanes per staged row (four columns each)
   constexpr int RPI = 64 / LPR;  // rows per read-back instruction
   constexpr int NT = 32 / RPI;   // read-backs per fragment row
@@ -519,20 +511,22 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const floatx16 (&a
 }
 
 // Main kernel, persistent: workgroup b runs tiles b, b + G, b + 2G, ... (G = grid size, at most
-// one workgroup per compute unit).  Two LDS stages of one K chunk (128) each, filled by direct
-// memory->LDS copies; two register sets of fragments, one per sub-chunk (64).  In the middle of
-// the second sub-chunk of chunk kc every wavefront waits for its own copies of chunk kc+1, meets
-// the others at a barrier (chunk kc+1 is then complete in LDS and every wavefront has read chunk
-// kc, whose stage is free), reads its fragments of chunk kc+1's first sub-chunk, and issues the
-// copies of chunk kc+2 into chunk kc's stage; in the middle of the first sub-chunk it reads the
-// second sub-chunk's fragments from the same stage.  The remaining MFMA steps of each sub-chunk
-// cover those LDS reads and the decode of the next sub-chunk's first step, so the matrix core does
-// not idle across sub-chunks.  Past the last chunk, reads and copies are clamped to it (redundant,
-// never used), keeping the loop branch-free.
-// Between tiles, the copies of the next tile's first two chunks are issued before the stores of
-// the finished tile, so the store traffic and the next tile's first loads are in flight together.
-// Each lane copies into LDS slots of its own wavefront only, and waits for its own copies before
-// issuing the next tile's, so stages never see two tiles' copies race.
+// one workgroup per compute unit).  Two LDS stages of one K chunk (256) each, filled by direct
+// memory->LDS copies; two register sets of fragments, alternating over the chunk's four
+// sub-chunks (64).  In the middle of the last sub-chunk of chunk kc every wavefront waits for its
+// own copies of chunk kc+1, meets the others at a barrier (chunk kc+1 is then complete in LDS and
+// every wavefront has read chunk kc, whose stage is free), reads its fragments of chunk kc+1's
+// first sub-chunk, and issues the copies of chunk kc+2 into chunk kc's stage; in the middle of
+// the other sub-chunks it reads the next sub-chunk's fragments from the same stage.  The remaining
+// MFMA steps of each sub-chunk cover those LDS reads and the decode of the next sub-chunk's first
+// step, so the matrix core does not idle across sub-chunks.  The loop runs two whole chunks per
+// pass; the 0-7 sub-chunks left after it run once every copy has landed, with no further barrier.
+// Past the last chunk, reads and copies are clamped to it (redundant, never used).
+// Between tiles, the copies of the next tile's first chunk are issued before the stores of the
+// finished tile, so the store traffic and the next tile's first loads are in flight together; the
+// stores stage the accumulators through the second stage, whose copies follow the stores.  Each
+// lane waits for its own copies and a barrier precedes every reuse of a stage, so stages never see
+// two tiles' copies or the staging race.
 template <int WAVES_M, int WAVES_N, int FM, int FN>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1)
 gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
@@ -541,8 +535,9 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
   __shared__ __attribute__((aligned(16))) uint8_t s1[Cfg::kStage];
   // per-column epilogue factors of the current tile, double-buffered by tile parity
   __shared__ __attribute__((aligned(16))) float alpha_s[2][Cfg::BN];
-  // epilogue staging, one area of 32 rows per wavefront
-  __shared__ __attribute__((aligned(16))) float epi_s[WAVES_M * WAVES_N][32 * kEpiStride];
+  // the epilogue stages accumulators in s1: one area of 32 rows per wavefront
+  constexpr int kEpiArea = 32 * epi_stride<FN>();
+  static_assert(WAVES_M * WAVES_N * kEpiArea * 4 <= Cfg::kStage, "epilogue staging fits a stage");
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -559,7 +554,6 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
 
   // LDS read offsets of this lane's fragments (within a stage), for each sub-chunk
   const FragOffsets fo = frag_offsets<Cfg, FM, FN>(wm, wn, lane);
-  const FragOffsets fo1 = sub_chunk<1>(fo);
 
   uint32_t v = blockIdx.x;
   uint32_t tmi, tni;
@@ -603,26 +597,44 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
     decode_step<0>(f0, sa, sb, a0, b0);
 
     constexpr int kCopies = Cfg::kPiecesA + Cfg::kPiecesB + Cfg::kWordsA + Cfg::kWordsB;
-    // One chunk: its first sub-chunk (in f0) with the second read from the same stage into f1,
-    // then the second sub-chunk (in f1) with the next chunk's first sub-chunk read into f0 after
-    // the barrier, and chunk kc+2 copied into this chunk's stage.  The stages are named statically
-    // (the loop runs two chunks per pass), so the compiler sees that reads of one stage do not
-    // alias the copies in flight into the other.
+    // One chunk: sub-chunks 0-2 each read the next one from the same stage; sub-chunk 3 reads the
+    // next chunk's first sub-chunk after the barrier and copies chunk kc+2 into this chunk's
+    // stage.  The register sets alternate f0, f1, f0, f1, so a chunk starts and ends with f0.  The
+    // stages are named statically (the loop runs two chunks per pass), so the compiler sees that
+    // reads of one stage do not alias the copies in flight into the other.
     auto run_chunk = [&](uint8_t* stage, uint8_t* next_stage, int kc) {
-      pipelined_chunk<true, false, 0>(f0, f1, stage, fo1, sa, sb, a0, b0, a1, b1, sh, acc, [] {});
+      pipelined_chunk<true, false, 0>(f0, f1, stage, sub_chunk(fo, 1), sa, sb, a0, b0, a1, b1, sh,
+                                      acc, [] {});
+      pipelined_chunk<true, false, 0>(f1, f0, stage, sub_chunk(fo, 2), sa, sb, a0, b0, a1, b1, sh,
+                                      acc, [] {});
+      pipelined_chunk<true, false, 0>(f0, f1, stage, sub_chunk(fo, 3), sa, sb, a0, b0, a1, b1, sh,
+                                      acc, [] {});
       pipelined_chunk<true, true, kCopies>(f1, f0, next_stage, fo, sa, sb, a0, b0, a1, b1, sh, acc,
                                            [&] { issue_chunk<Cfg>(p, ro, min(kc + 2, last), stage); });
     };
     int kc = 0;
-    for (; 2 * kc + 3 < nsub; kc += 2) {
+    for (; 4 * kc + 7 < nsub; kc += 2) {
       run_chunk(s0, s1, kc);
       run_chunk(s1, s0, kc + 1);
     }
-    // 0 to 3 sub-chunks remain, the first in s0 (and in f0)
-    const int rest = nsub - 2 * kc;
-    if (rest >= 2) run_chunk(s0, s1, kc);
-    if (rest & 1)  // K an odd multiple of 64: the last chunk's only sub-chunk, in f0
-      pipelined_chunk<false, false, 0>(f0, f1, s0, fo, sa, sb, a0, b0, a1, b1, sh, acc, [] {});
+    // 0 to 7 sub-chunks remain: chunk kc in s0 (its first sub-chunk already in f0), then chunk
+    // kc+1 in s1.  Once every copy of both has landed they run with no further barrier, two
+    // sub-chunks (f0 then f1) per pass; the last read of a pass is clamped to the last sub-chunk.
+    int sc = 4 * kc;
+    if (sc < nsub) {
+      __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      auto stage_of = [&](int c) -> const uint8_t* { return (c >> 2) > kc ? s1 : s0; };
+      for (; sc + 1 < nsub; sc += 2) {
+        pipelined_chunk<true, false, 0>(f0, f1, stage_of(sc + 1), sub_chunk(fo, (sc + 1) & 3), sa,
+                                        sb, a0, b0, a1, b1, sh, acc, [] {});
+        const int nx = min(sc + 2, nsub - 1);
+        pipelined_chunk<true, false, 0>(f1, f0, stage_of(nx), sub_chunk(fo, nx & 3), sa, sb, a0, b0,
+                                        a1, b1, sh, acc, [] {});
+      }
+      if (sc < nsub)
+        pipelined_chunk<false, false, 0>(f0, f1, s0, fo, sa, sb, a0, b0, a1, b1, sh, acc, [] {});
+    }
     // this lane's redundant copies past the last chunk have landed before its stages are reused
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0x3F70);
@@ -634,26 +646,32 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
     const int tm0 = m0, tn0 = n0;
     v += gridDim.x;
     const bool more = v < ntiles;
+    // every wavefront is past its last reads of both stages, and every copy into them has landed
+    __builtin_amdgcn_s_barrier();
     if (more) {
-      // With an odd number of sub-chunks the last one was read from its stage after the last
-      // barrier; every wavefront must be past those reads before any copies of the next tile land
-      // there.  (With an even number, the last chunk's own barrier already orders them.)
-      if (nsub & 1) __builtin_amdgcn_s_barrier();
       tile_coords(v, tiles_m, tiles_n, tmi, tni);
       m0 = (int)tmi * Cfg::BM;
       n0 = (int)tni * Cfg::BN;
       RowOffsets<Cfg> ron;
       row_offsets<Cfg, FM, FN>(p, m0, n0, tid_e, ron);
       issue_chunk<Cfg>(p, ron, 0, s0);
-      issue_chunk<Cfg>(p, ron, min(1, last), s1);
     }
     const bool interior = vec && tm0 + Cfg::BM <= p.M && tn0 + Cfg::BN <= p.N;
+    float* const epi = reinterpret_cast<float*>(s1) + wave_e * kEpiArea;
     if (p.c_bf16)
-      store_tile<true>(p, acc, alpha_s[par], epi_s[wave_e], tm0, tn0, wave_e / WAVES_N,
-                       wave_e % WAVES_N, lane_e, vec, interior);
+      store_tile<true>(p, acc, alpha_s[par], epi, tm0, tn0, wave_e / WAVES_N, wave_e % WAVES_N,
+                       lane_e, vec, interior);
     else
-      store_tile<false>(p, acc, alpha_s[par], epi_s[wave_e], tm0, tn0, wave_e / WAVES_N,
-                        wave_e % WAVES_N, lane_e, vec, interior);
+      store_tile<false>(p, acc, alpha_s[par], epi, tm0, tn0, wave_e / WAVES_N, wave_e % WAVES_N,
+                        lane_e, vec, interior);
+    if (more) {
+      // every wavefront has read back its staged accumulators before copies land in s1
+      __builtin_amdgcn_s_barrier();
+      const int tid_c = opaque_tid();
+      RowOffsets<Cfg> ron;
+      row_offsets<Cfg, FM, FN>(p, m0, n0, tid_c, ron);
+      issue_chunk<Cfg>(p, ron, min(1, last), s1);
+    }
     if (!more) break;
   }
 }
