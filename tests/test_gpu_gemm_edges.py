@@ -6,14 +6,16 @@ every kernel the dispatch can choose, and on mid-size problems compared in full.
   normal up to 0x7E = 448), all-zero blocks made by zero codes and by a zero scale.  Each product
   kernel decodes block scales its own way (a hardware fp8 conversion in the tiled, one-pass decode
   and streaming kernels, a bit-level decode in the general one), so each is driven over the whole
-  scale range: general (K % 64 != 0), tiled (odd and even numbers of 64-element K chunks), the
+  scale range: general (K % 64 != 0), tiled (every count of 64-element sub-chunks left after its
+  loop over pairs of 256-element chunks), the
   one-pass decode kernel with one and two 16-column tiles per workgroup, its long-K form with one
   and two tiles and its many-column form, the streaming kernel's cached and column-pair forms, and
   K split into pieces that add into C.
 * Mid-size problems compared element by element over the whole output: more tiles than compute
   units with a tile count that is not a multiple of 8 (the persistent kernel's plain tile order),
-  partial edge tiles, and an odd number of K chunks (the last chunk of a tile read from the first
-  LDS stage while the next tile's first copies are issued).
+  partial edge tiles, and K ending in a lone 64-element sub-chunk (read after the last barrier,
+  before the next tile's first copies are issued); larger K, where each tile also runs the loop
+  over pairs of chunks, on sampled rows of every tile row.
 
 Tolerance as everywhere (stated for FP32 accumulation of exact products): per element
 ``|C_gpu - C_ref| <= 1e-4 * sum_k |a*w| / (gA gW[seg])``, relative Frobenius error <= 1e-5.  The
@@ -134,9 +136,9 @@ def test_small_scales_under_a_static_activation_scale():
 
 @pytest.mark.parametrize("M,N,K,what", [
     (2304, 8485, 128, "405 tiles of 256 x 192 (not a multiple of 8), partial last tile column"),
-    (2304, 7936, 192, "378 tiles of 256 x 192, 3 K chunks per tile (odd)"),
-    (1100, 16400, 320, "430 tiles of 256 x 192, 5 K chunks, partial last tile row"),
-    (1100, 19653, 192, "385 tiles of 256 x 256, 3 K chunks, partial last tile row and column"),
+    (2304, 7936, 192, "378 tiles of 256 x 192, 3 K sub-chunks per tile (odd)"),
+    (1100, 16400, 320, "430 tiles of 256 x 192, 5 K sub-chunks, partial last tile row"),
+    (1100, 19653, 192, "385 tiles of 256 x 256, 3 K sub-chunks, partial last tile row and column"),
 ])
 def test_mid_size_full_output(M, N, K, what):
     """Every output element of problems with more tiles than compute units, so each persistent
@@ -155,4 +157,35 @@ def test_mid_size_raw_bytes_full_output():
     ac, as_ = random_nvfp4_bytes(5, M, K)
     wc, ws = random_nvfp4_bytes(6, N, K)
     _run(ac, as_, np.float32(0.75), wc, ws, np.array([3.0], np.float32), [0, N],
-         "raw bytes, full output, 378 tiles, odd K chunks")
+         "raw bytes, full output, 378 tiles, odd K sub-chunks")
+
+
+@pytest.mark.parametrize("M,N,K,what", [
+    (2304, 7936, 576, "378 tiles of 256 x 192; per tile one pass of the two-chunk loop and a lone "
+                      "sub-chunk"),
+    (1100, 19653, 704, "385 tiles of 256 x 256; per tile one loop pass, a chunk and a lone "
+                       "sub-chunk"),
+])
+def test_mid_size_loop_sampled_rows(M, N, K, what):
+    """Several tiles per persistent workgroup with K long enough for the K loop itself: the GPU
+    computes the whole output; the oracle checks the first and last rows of every 256-row tile
+    row, and every ninth row, over all columns."""
+    import torch
+
+    import bit_block_scaled_nvfp4_amd as nv
+
+    a = random_matrix(95 + K, M, K, outlier_cols=3)
+    wt = random_matrix(96 + K, N, K, std=0.02)
+    segs = [0, N // 3 + 5, N]
+    ac, as_, ga = oracle.quantize(a)
+    wc, ws, gw = oracle.quantize_segments(wt, segs)
+    log(f"{what}: M={M} N={N} K={K}")
+    C = nv.fused_nvfp4_gemm(_up(ac), _up(as_), scalar(ga), _up(wc), _up(ws),
+                            _up(np.asarray(gw, np.float32)), segs)
+    torch.cuda.synchronize()
+    C = C.cpu().numpy()
+    bands = [r for t in range(0, M, 256) for r in (t, t + 1, min(t + 255, M - 1))]
+    rows = np.unique(np.concatenate([np.arange(0, M, 9), bands, [M - 1]]))
+    R, B = oracle_product(ac[rows], as_[rows], ga, wc, ws, gw, segs)
+    worst = check_gemm(C[rows], R, B, f"{what}, {len(rows)} rows")
+    log(f"{what}: worst err / sum|ab| = {worst:.2e}")
