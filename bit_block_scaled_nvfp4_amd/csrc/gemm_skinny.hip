@@ -832,11 +832,19 @@ hipError_t compute_units(int& cus) {
 
 }  // namespace
 
+// Rows up to which the encoding form runs: every workgroup encodes all M activation rows itself,
+// so its encode work grows with M while a separate encode launch spreads it over the device.  On
+// the 5120 x 5120 decode product one launch took 8.2 / 9.1 / 9.7 us at M = 1 / 4 / 6 against
+// 9.0 / 9.6 / 9.9 us for encode + product as two launches (graph replays), but 11.1 / 14.4 us at
+// M = 8 / 16 against 9.9 / 10.0 us.
+constexpr int64_t kEncodeMaxRows = 6;
+
 bool skinny_one_pass(int64_t M, int64_t N, int64_t K, int x_dtype) {
   int cus = 0;
   if (compute_units(cus) != hipSuccess) return false;
   if (x_dtype == NVFP4_F32 && K > kEncodeF32MaxPhases * kPhaseK) return false;
-  return M >= 1 && M <= 16 && K % kPhaseK == 0 && K <= kSkinnyMaxK && (N + cus - 1) / cus <= 32;
+  return M >= 1 && M <= kEncodeMaxRows && K % kPhaseK == 0 && K <= kSkinnyMaxK &&
+         (N + cus - 1) / cus <= 32;
 }
 
 hipError_t launch_gemm_skinny_encode(const GemmArgs& a, const void* x, nvfp4_dtype x_dtype,
