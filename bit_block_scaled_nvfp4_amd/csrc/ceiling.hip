@@ -8,32 +8,30 @@
 namespace {
 
 constexpr int kThreads = 512;
-constexpr int kUnroll = 8;  // 16-byte loads per lane and region in flight at once
+constexpr int kUnroll = 8;  // 16-byte loads per lane in flight at once
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Workgroup w reads the w-th contiguous share of each region, 16 bytes per lane per load, with every
-// load of a batch issued before any is used; the bytes are folded by XOR so the loads stay live, and
-// each wavefront writes one word.
+// The two regions are read as one range (a's bytes, then b's): workgroup w reads the w-th
+// contiguous share of it, 16 bytes per lane per load, with every load of a batch issued before
+// any is used; the bytes are folded by XOR so the loads stay live, and each wavefront writes one
+// word.  (Reading each region's share separately issues twice the load instructions and took
+// 4.5 us against 4.1 us for one 14.75 MB weight.)
 __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __restrict__ a, int64_t na,
                                                                const u32x4* __restrict__ b, int64_t nb,
                                                                uint32_t* __restrict__ out) {
-  const int64_t g = gridDim.x;
-  const int64_t sa = (na + g - 1) / g, sb = (nb + g - 1) / g;
-  const int64_t a0 = blockIdx.x * sa, a1 = min(na, a0 + sa);
-  const int64_t b0 = blockIdx.x * sb, b1 = min(nb, b0 + sb);
+  const int64_t n = na + nb, g = gridDim.x;
+  const int64_t lo = n * blockIdx.x / g, hi = n * (blockIdx.x + 1) / g;
   uint32_t acc = 0;
-  for (int64_t i = threadIdx.x; a0 + i < a1 || b0 + i < b1; i += kUnroll * kThreads) {
-    u32x4 va[kUnroll], vb[kUnroll];
+  for (int64_t i = lo + threadIdx.x; i < hi; i += kUnroll * kThreads) {
+    u32x4 v[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t ia = a0 + i + u * kThreads, ib = b0 + i + u * kThreads;
-      va[u] = ia < a1 ? __builtin_nontemporal_load(a + ia) : u32x4{0, 0, 0, 0};
-      vb[u] = ib < b1 ? __builtin_nontemporal_load(b + ib) : u32x4{0, 0, 0, 0};
+      const int64_t j = i + u * kThreads;
+      v[u] = j < hi ? __builtin_nontemporal_load(j < na ? a + j : b + (j - na)) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      acc ^= va[u].x ^ va[u].y ^ va[u].z ^ va[u].w ^ vb[u].x ^ vb[u].y ^ vb[u].z ^ vb[u].w;
+    for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o);
