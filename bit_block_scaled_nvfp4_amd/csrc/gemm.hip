@@ -160,40 +160,52 @@ __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t v
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, (int)voff, 0, 0, 0);
 }
 
-// Issue the direct memory->LDS copies of K chunk `kc` (of 256) into `stage`.  A wavefront whose
+// Issue copies FROM .. TO-1 of K chunk `kc` (of 256) into `stage`, counting A's code pieces, W's
+// code pieces, A's scale rows, then W's scale rows (kCopies per thread in all).  A wavefront whose
 // copy slots of the last, partial round lie past the area skips that copy (the test is uniform
-// across the wavefront).
-template <class Cfg>
-__device__ __forceinline__ void issue_chunk(const GemmArgs& p, const RowOffsets<Cfg>& o, int kc,
-                                            uint8_t* stage) {
-  // the wavefront's first copy slot and the resources are uniform (scalar registers); each copy
-  // is a resource plus this lane's 32-bit row offset
+// across the wavefront).  The wavefront's first copy slot and the resources are uniform (scalar
+// registers); each copy is a resource plus this lane's 32-bit row offset.
+template <class Cfg, int FROM, int TO>
+__device__ __forceinline__ void issue_part(const GemmArgs& p, const RowOffsets<Cfg>& o, int kc,
+                                           uint8_t* stage) {
   const int wave_slot = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * 64;
   const int64_t kb = p.K / 2, ks = p.K / 16;
-  const __amdgpu_buffer_rsrc_t ac = chunk_rsrc(p.a_codes, p.M * kb, kc * 128);
-  const __amdgpu_buffer_rsrc_t wc = chunk_rsrc(p.w_codes, p.N * kb, kc * 128);
-  const __amdgpu_buffer_rsrc_t as = chunk_rsrc(p.a_scales, p.M * ks, kc * 16);
-  const __amdgpu_buffer_rsrc_t ws = chunk_rsrc(p.w_scales, p.N * ks, kc * 16);
+  constexpr int PA = Cfg::kPiecesA, PB = Cfg::kPiecesB, WA = Cfg::kWordsA;
 #pragma unroll
-  for (int i = 0; i < Cfg::kPiecesA; ++i)
-    if ((i + 1) * Cfg::kThreads <= Cfg::BM * 8 || i * Cfg::kThreads + wave_slot < Cfg::BM * 8)
-      copy_to_lds<16>(ac, o.a[i], stage + (i * Cfg::kThreads + wave_slot) * 16);
-#pragma unroll
-  for (int i = 0; i < Cfg::kPiecesB; ++i)
-    if ((i + 1) * Cfg::kThreads <= Cfg::BN * 8 || i * Cfg::kThreads + wave_slot < Cfg::BN * 8)
-      copy_to_lds<16>(wc, o.b[i], stage + Cfg::kCodesA + (i * Cfg::kThreads + wave_slot) * 16);
-#pragma unroll
-  for (int i = 0; i < Cfg::kWordsA; ++i)
-    if ((i + 1) * Cfg::kThreads <= Cfg::BM || i * Cfg::kThreads + wave_slot < Cfg::BM)
-      copy_to_lds<16>(as, o.sa[i],
-                      stage + Cfg::kCodesA + Cfg::kCodesB + (i * Cfg::kThreads + wave_slot) * 16);
-#pragma unroll
-  for (int i = 0; i < Cfg::kWordsB; ++i)
-    if ((i + 1) * Cfg::kThreads <= Cfg::BN || i * Cfg::kThreads + wave_slot < Cfg::BN)
-      copy_to_lds<16>(ws, o.sb[i],
-                      stage + Cfg::kCodesA + Cfg::kCodesB + Cfg::kScalesA +
-                          (i * Cfg::kThreads + wave_slot) * 16);
+  for (int x = FROM; x < TO; ++x) {
+    if (x < PA) {
+      const int i = x;
+      if ((i + 1) * Cfg::kThreads <= Cfg::BM * 8 || i * Cfg::kThreads + wave_slot < Cfg::BM * 8)
+        copy_to_lds<16>(chunk_rsrc(p.a_codes, p.M * kb, kc * 128), o.a[i],
+                        stage + (i * Cfg::kThreads + wave_slot) * 16);
+    } else if (x < PA + PB) {
+      const int i = x - PA;
+      if ((i + 1) * Cfg::kThreads <= Cfg::BN * 8 || i * Cfg::kThreads + wave_slot < Cfg::BN * 8)
+        copy_to_lds<16>(chunk_rsrc(p.w_codes, p.N * kb, kc * 128), o.b[i],
+                        stage + Cfg::kCodesA + (i * Cfg::kThreads + wave_slot) * 16);
+    } else if (x < PA + PB + WA) {
+      const int i = x - PA - PB;
+      if ((i + 1) * Cfg::kThreads <= Cfg::BM || i * Cfg::kThreads + wave_slot < Cfg::BM)
+        copy_to_lds<16>(chunk_rsrc(p.a_scales, p.M * ks, kc * 16), o.sa[i],
+                        stage + Cfg::kCodesA + Cfg::kCodesB + (i * Cfg::kThreads + wave_slot) * 16);
+    } else {
+      const int i = x - PA - PB - WA;
+      if ((i + 1) * Cfg::kThreads <= Cfg::BN || i * Cfg::kThreads + wave_slot < Cfg::BN)
+        copy_to_lds<16>(chunk_rsrc(p.w_scales, p.N * ks, kc * 16), o.sb[i],
+                        stage + Cfg::kCodesA + Cfg::kCodesB + Cfg::kScalesA +
+                            (i * Cfg::kThreads + wave_slot) * 16);
+    }
+  }
 }
+
+// The copies of a chunk go out in three parts: part 0 right after the barrier that frees the
+// stage, parts 1 and 2 during the first two sub-chunks of the chunk before it.  Spreading them keeps
+// each hand-over's burst of copies short (a variant issuing all of them at once was 2-3 % slower).
+template <class Cfg>
+struct CopyParts {
+  static constexpr int kCopies = Cfg::kPiecesA + Cfg::kPiecesB + Cfg::kWordsA + Cfg::kWordsB;
+  static constexpr int k1 = kCopies / 3, k2 = 2 * kCopies / 3;
+};
 
 // Tile order: hardware hands workgroup ids to the 8 XCDs round-robin, so id b runs on XCD b % 8.
 // Remap ids so each XCD walks a contiguous range of the logical order, and walk the logical order
@@ -363,8 +375,8 @@ __device__ __forceinline__ void interleave_after_barrier() {
 // copies of the next chunk and meets the others at a barrier (the next chunk is complete in LDS,
 // and every wavefront has read the current chunk, whose stage is free); for the first sub-chunk,
 // the next one is already in the same stage.  The remaining MFMAs of step 2 run under the LDS reads
-// of the next sub-chunk's fragments (from `nstage` at offsets `no`), for SYNC the copies of the
-// chunk after the next (`issue`, into the current stage), and the decode of step 3; the MFMAs of
+// of the next sub-chunk's fragments (from `nstage` at offsets `no`), NVM copies into the stage
+// that is free (`issue`), and the decode of step 3; the MFMAs of
 // step 3 run under the decode of the next sub-chunk's step 0.  On entry `cur` holds this
 // sub-chunk's fragments and a0/b0 its decoded step 0; on exit (HAS_NEXT) `nxt` holds the next
 // sub-chunk's fragments and a0/b0 its decoded step 0.
@@ -391,11 +403,11 @@ __device__ __forceinline__ void pipelined_chunk(const Frags<FM, FN>& cur, Frags<
       __builtin_amdgcn_sched_barrier(0);
     }
     read_frags(nstage, no, nxt);
-    if constexpr (SYNC) issue();
+    if constexpr (NVM > 0) issue();
   }
   mfma_range<kPreBarrierMfma, FM * FN>(a0, b0, acc);
   decode_step<3>(cur, sa, sb, a1, b1);
-  interleave_after_barrier<FM, FN, HAS_NEXT ? 2 * (FM + FN) : 0, HAS_NEXT && SYNC ? NVM : 0>();
+  interleave_after_barrier<FM, FN, HAS_NEXT ? 2 * (FM + FN) : 0, HAS_NEXT ? NVM : 0>();
   __builtin_amdgcn_sched_barrier(0);
   mfma_step(a1, b1, acc);
   if constexpr (HAS_NEXT) {
@@ -516,17 +528,18 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const floatx16 (&a
 // sub-chunks (64).  In the middle of the last sub-chunk of chunk kc every wavefront waits for its
 // own copies of chunk kc+1, meets the others at a barrier (chunk kc+1 is then complete in LDS and
 // every wavefront has read chunk kc, whose stage is free), reads its fragments of chunk kc+1's
-// first sub-chunk, and issues the copies of chunk kc+2 into chunk kc's stage; in the middle of
-// the other sub-chunks it reads the next sub-chunk's fragments from the same stage.  The remaining
+// first sub-chunk, and issues the first third of chunk kc+2's copies into chunk kc's stage (the
+// other two thirds go out during chunk kc+1's first two sub-chunks); in the middle of the other
+// sub-chunks it reads the next sub-chunk's fragments from the same stage.  The remaining
 // MFMA steps of each sub-chunk cover those LDS reads and the decode of the next sub-chunk's first
 // step, so the matrix core does not idle across sub-chunks.  The loop runs two whole chunks per
 // pass; the 0-7 sub-chunks left after it run once every copy has landed, with no further barrier.
 // Past the last chunk, reads and copies are clamped to it (redundant, never used).
 // Between tiles, the copies of the next tile's first chunk are issued before the stores of the
 // finished tile, so the store traffic and the next tile's first loads are in flight together; the
-// stores stage the accumulators through the second stage, whose copies follow the stores.  Each
-// lane waits for its own copies and a barrier precedes every reuse of a stage, so stages never see
-// two tiles' copies or the staging race.
+// stores stage the accumulators through the second stage, whose first copies follow the stores.
+// Each lane waits for its own copies and a barrier precedes every reuse of a stage, so stages never
+// see two tiles' copies or the staging race.
 template <int WAVES_M, int WAVES_N, int FM, int FN>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, 1)
 gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
@@ -564,8 +577,8 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
     const int tid_t = threadIdx.x;
     RowOffsets<Cfg> ro;
     row_offsets<Cfg, FM, FN>(p, m0, n0, tid_t, ro);
-    issue_chunk<Cfg>(p, ro, 0, s0);
-    issue_chunk<Cfg>(p, ro, min(1, last), s1);
+    issue_part<Cfg, 0, CopyParts<Cfg>::kCopies>(p, ro, 0, s0);
+    issue_part<Cfg, 0, CopyParts<Cfg>::k1>(p, ro, min(1, last), s1);
   }
 
   for (int par = 0;; par ^= 1) {
@@ -596,21 +609,25 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
     decode_scales(f0, sh, sa, sb);
     decode_step<0>(f0, sa, sb, a0, b0);
 
-    constexpr int kCopies = Cfg::kPiecesA + Cfg::kPiecesB + Cfg::kWordsA + Cfg::kWordsB;
-    // One chunk: sub-chunks 0-2 each read the next one from the same stage; sub-chunk 3 reads the
-    // next chunk's first sub-chunk after the barrier and copies chunk kc+2 into this chunk's
-    // stage.  The register sets alternate f0, f1, f0, f1, so a chunk starts and ends with f0.  The
-    // stages are named statically (the loop runs two chunks per pass), so the compiler sees that
-    // reads of one stage do not alias the copies in flight into the other.
+    using CP = CopyParts<Cfg>;
+    // One chunk: sub-chunks 0-2 each read the next one from the same stage, and sub-chunks 0 and
+    // 1 copy parts 1 and 2 of chunk kc+1 into the other stage; sub-chunk 3 reads the next chunk's
+    // first sub-chunk after the barrier and copies part 0 of chunk kc+2 into this chunk's stage.
+    // The register sets alternate f0, f1, f0, f1, so a chunk starts and ends with f0.  The stages
+    // are named statically (the loop runs two chunks per pass), so the compiler sees that reads of
+    // one stage do not alias the copies in flight into the other.
     auto run_chunk = [&](uint8_t* stage, uint8_t* next_stage, int kc) {
-      pipelined_chunk<true, false, 0>(f0, f1, stage, sub_chunk(fo, 1), sa, sb, a0, b0, a1, b1, sh,
-                                      acc, [] {});
-      pipelined_chunk<true, false, 0>(f1, f0, stage, sub_chunk(fo, 2), sa, sb, a0, b0, a1, b1, sh,
-                                      acc, [] {});
+      const int k1 = min(kc + 1, last), k2 = min(kc + 2, last);
+      pipelined_chunk<true, false, CP::k2 - CP::k1>(
+          f0, f1, stage, sub_chunk(fo, 1), sa, sb, a0, b0, a1, b1, sh, acc,
+          [&] { issue_part<Cfg, CP::k1, CP::k2>(p, ro, k1, next_stage); });
+      pipelined_chunk<true, false, CP::kCopies - CP::k2>(
+          f1, f0, stage, sub_chunk(fo, 2), sa, sb, a0, b0, a1, b1, sh, acc,
+          [&] { issue_part<Cfg, CP::k2, CP::kCopies>(p, ro, k1, next_stage); });
       pipelined_chunk<true, false, 0>(f0, f1, stage, sub_chunk(fo, 3), sa, sb, a0, b0, a1, b1, sh,
                                       acc, [] {});
-      pipelined_chunk<true, true, kCopies>(f1, f0, next_stage, fo, sa, sb, a0, b0, a1, b1, sh, acc,
-                                           [&] { issue_chunk<Cfg>(p, ro, min(kc + 2, last), stage); });
+      pipelined_chunk<true, true, CP::k1>(f1, f0, next_stage, fo, sa, sb, a0, b0, a1, b1, sh, acc,
+                                          [&] { issue_part<Cfg, 0, CP::k1>(p, ro, k2, stage); });
     };
     int kc = 0;
     for (; 4 * kc + 7 < nsub; kc += 2) {
@@ -618,10 +635,12 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
       run_chunk(s1, s0, kc + 1);
     }
     // 0 to 7 sub-chunks remain: chunk kc in s0 (its first sub-chunk already in f0), then chunk
-    // kc+1 in s1.  Once every copy of both has landed they run with no further barrier, two
-    // sub-chunks (f0 then f1) per pass; the last read of a pass is clamped to the last sub-chunk.
+    // kc+1 in s1, whose parts 1 and 2 are copied now.  Once every copy of both has landed they run
+    // with no further barrier, two sub-chunks (f0 then f1) per pass; the last read of a pass is
+    // clamped to the last sub-chunk.
     int sc = 4 * kc;
     if (sc < nsub) {
+      issue_part<Cfg, CP::k1, CP::kCopies>(p, ro, min(kc + 1, last), s1);
       __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0)
       __builtin_amdgcn_s_barrier();
       auto stage_of = [&](int c) -> const uint8_t* { return (c >> 2) > kc ? s1 : s0; };
@@ -654,7 +673,7 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
       n0 = (int)tni * Cfg::BN;
       RowOffsets<Cfg> ron;
       row_offsets<Cfg, FM, FN>(p, m0, n0, tid_e, ron);
-      issue_chunk<Cfg>(p, ron, 0, s0);
+      issue_part<Cfg, 0, CopyParts<Cfg>::kCopies>(p, ron, 0, s0);
     }
     const bool interior = vec && tm0 + Cfg::BM <= p.M && tn0 + Cfg::BN <= p.N;
     float* const epi = reinterpret_cast<float*>(s1) + wave_e * kEpiArea;
@@ -670,7 +689,7 @@ gemm_tiled_kernel(GemmArgs p, uint32_t tiles_m, uint32_t tiles_n) {
       const int tid_c = opaque_tid();
       RowOffsets<Cfg> ron;
       row_offsets<Cfg, FM, FN>(p, m0, n0, tid_c, ron);
-      issue_chunk<Cfg>(p, ron, min(1, last), s1);
+      issue_part<Cfg, 0, CopyParts<Cfg>::k1>(p, ron, min(1, last), s1);
     }
     if (!more) break;
   }
