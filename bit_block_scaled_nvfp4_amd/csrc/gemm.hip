@@ -199,8 +199,8 @@ __device__ __forceinline__ void issue_part(const GemmArgs& p, const RowOffsets<C
 }
 
 // The copies of a chunk go out in three parts: part 0 right after the barrier that frees the
-// stage, parts 1 and 2 during the first two sub-chunks of the chunk before it.  Spreading them keeps
-// each hand-over's burst of copies short (a variant issuing all of them at once was 2-3 % slower).
+// stage, parts 1 and 2 during the first two sub-chunks of the chunk before it.  Spreading them
+// keeps each hand-over's burst of copies short (issuing all of them at once was 2-4 % slower).
 template <class Cfg>
 struct CopyParts {
   static constexpr int kCopies = Cfg::kPiecesA + Cfg::kPiecesB + Cfg::kWordsA + Cfg::kWordsB;
@@ -261,13 +261,17 @@ template <int FM, int FN>
 __device__ __forceinline__ void read_frags(const uint8_t* stage, const FragOffsets& o,
                                            Frags<FM, FN>& f) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i) f.qa[i] = *reinterpret_cast<const uint4*>(stage + o.a_frag + i * 4096);
+  for (int i = 0; i < FM; ++i)
+    f.qa[i] = *reinterpret_cast<const uint4*>(stage + o.a_frag + i * 4096);
 #pragma unroll
-  for (int j = 0; j < FN; ++j) f.qb[j] = *reinterpret_cast<const uint4*>(stage + o.b_frag + j * 4096);
+  for (int j = 0; j < FN; ++j)
+    f.qb[j] = *reinterpret_cast<const uint4*>(stage + o.b_frag + j * 4096);
 #pragma unroll
-  for (int i = 0; i < FM; ++i) f.sa[i] = *reinterpret_cast<const uint32_t*>(stage + o.a_scl + i * 512);
+  for (int i = 0; i < FM; ++i)
+    f.sa[i] = *reinterpret_cast<const uint32_t*>(stage + o.a_scl + i * 512);
 #pragma unroll
-  for (int j = 0; j < FN; ++j) f.sb[j] = *reinterpret_cast<const uint32_t*>(stage + o.b_scl + j * 512);
+  for (int j = 0; j < FN; ++j)
+    f.sb[j] = *reinterpret_cast<const uint32_t*>(stage + o.b_scl + j * 512);
 }
 
 template <int STEP>
@@ -363,7 +367,8 @@ __device__ __forceinline__ void interleave_after_barrier() {
     if (k < kDsMfma) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
     if constexpr (NVM > 0) {  // VMEM
       if ((k + 1) * kVmPerMfma <= NVM) __builtin_amdgcn_sched_group_barrier(0x010, kVmPerMfma, 0);
-      else if (k * kVmPerMfma < NVM) __builtin_amdgcn_sched_group_barrier(0x010, NVM % kVmPerMfma, 0);
+      else if (k * kVmPerMfma < NVM)
+        __builtin_amdgcn_sched_group_barrier(0x010, NVM % kVmPerMfma, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);  // VALU
   }
