@@ -164,8 +164,8 @@ def decode(args, torch, nv, W):
     weight copy) replayed back to back from a HIP graph, total / 24.  The algorithmic bytes of the
     product are the NVFP4 weights (codes + scales), the encoded activations and the f32 output.
     ``linear``: the same step through nvfp4_linear (call and graph-replay timings as above): encode
-    and product in one launch up to 6 rows, two launches above (where every workgroup's encode of
-    all the rows costs more than the separate encode launch)."""
+    and product in one launch up to 6 rows at this K (M * K / 1024 <= 32), two launches above
+    (where every workgroup's encode of all the rows costs more than the separate encode launch)."""
     import numpy as np
 
     w = W.WORKLOADS[4]
@@ -218,7 +218,8 @@ def decode(args, torch, nv, W):
         nbytes = w.N * w.K * 9 // 16 + M * w.K * 9 // 16 + M * w.N * 4
         gbs = nbytes / (k_ms * 1e-3) / 1e9
         # the same step through nvfp4_linear: the activation encode and the product in one launch
-        # up to 6 rows (one call per step; bytes: the bf16 activation read instead of its codes)
+        # up to 6 rows at this K (one call per step; bytes: the bf16 activation read instead of its
+        # codes)
         for i in range(2 * R):
             wc, ws = copies[i % R]
             nv.nvfp4_linear(ad, ga, wc, ws, gw, out=C, a_codes=ac, a_scales=as_)
@@ -250,7 +251,8 @@ def decode(args, torch, nv, W):
                         "linear": {"kernel_us": round(lk_ms * 1e3, 3),
                                    "call_us": round(lcall_ms * 1e3, 3),
                                    "GB/s": round(lbytes / (lk_ms * 1e-3) / 1e9, 1),
-                                   "bytes": lbytes, "launches": 1 if M <= 6 else 2}}
+                                   "bytes": lbytes,
+                                   "launches": 1 if M <= 6 and M * w.K <= 32 * 1024 else 2}}
     res["ceilings"] = _decode_ceilings(torch, copies, R)
     return res
 

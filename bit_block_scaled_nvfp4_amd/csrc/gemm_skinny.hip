@@ -33,9 +33,13 @@
 // Activation input.  Either its NVFP4 codes and scales (the product alone), or the raw activation
 // (f32, bf16 or f16) with its static global scale: then every wavefront first encodes exactly the
 // blocks its own fragments need (its chunk of every phase, all M rows) with the encoder's block
-// routine (bit-identical codes and scales) into its own LDS area, the wavefronts of workgroup 0
-// also write theirs out for the caller, and the lanes read their fragments back -- no workgroup
-// barrier.  That makes a decode step's activation encode and product one launch.
+// routine (bit-identical codes and scales) into its own LDS area, and the lanes read their
+// fragments back -- no workgroup barrier; the wavefronts of workgroup 0 write their blocks out for
+// the caller after their MFMAs.  That makes a decode step's activation encode and product one
+// launch.  The raw blocks of a wavefront (M * NPH * 8 of them, at most 256) are loaded in one batch
+// before the weights: a load issued after the weight loads could only be waited for together with
+// all of them (the load counter drains in issue order), which would hold every decode and MFMA
+// back until the wavefront's last weight byte had landed.
 //
 // Reduction: the 8 wavefronts' partial 16x16 tiles of each tile are summed through LDS in a fixed
 // order (deterministic), scaled per column by 1 / (gA * gW[seg(n)]) and stored.  Every output
@@ -101,7 +105,8 @@ __device__ __forceinline__ uint32_t pick_scales(uint2 v, int q, int r, int g) {
   return ((g & 2) ? hi : lo) >> ((g & 1) * 16);
 }
 
-// The encoding form's activation loads: B blocks per thread and batch, 32-bit words per block.
+// The encoding form's activation loads: kEncodeBatch blocks per lane (so at most 256 blocks per
+// wavefront: M * NPH <= 32), 32-bit words per block.
 constexpr int kEncodeBatch = 4;
 template <nvfp4_dtype XDT>
 constexpr int encode_words() {
@@ -117,11 +122,11 @@ __device__ __forceinline__ void wave_block(int b, int wave, int& row, int& col) 
   col = chunk_of<NPH>(rem >> 3, wave) * 128 + (rem & 7) * 16;  // element offset within the row
 }
 
-// Load batch `base` (this wavefront's blocks base + j * 64 + lane, j < B, clamped to its last
-// block) of the raw activation into registers.
+// Load this wavefront's blocks j * 64 + lane, j < kEncodeBatch (clamped to its last block), of the
+// raw activation into registers.
 template <nvfp4_dtype XDT, int NPH>
 __device__ __forceinline__ void encode_load(const GemmArgs& p, const DecodeEncode& e, int wave,
-                                            int lane, int base,
+                                            int lane,
                                             uint32_t (&raw)[kEncodeBatch][encode_words<XDT>()]) {
   constexpr int W = encode_words<XDT>();
   const int nblk = p.M * NPH * 8;
@@ -129,7 +134,7 @@ __device__ __forceinline__ void encode_load(const GemmArgs& p, const DecodeEncod
 #pragma unroll
   for (int j = 0; j < kEncodeBatch; ++j) {
     int row, col;
-    wave_block<NPH>(min(base + j * 64 + lane, nblk - 1), wave, row, col);
+    wave_block<NPH>(min(j * 64 + lane, nblk - 1), wave, row, col);
     const uint8_t* src = xb + ((int64_t)row * e.ldx + col) * codec::elem_bytes<XDT>();
 #pragma unroll
     for (int i = 0; i < W / 4; ++i) {
@@ -142,58 +147,53 @@ __device__ __forceinline__ void encode_load(const GemmArgs& p, const DecodeEncod
   }
 }
 
-// Encode this wavefront's blocks of the activation with the static scale g and the encoder's block
-// routine into its own LDS area (codes [row][phase][64 bytes of its chunk], scales
-// [row][phase][8]), spread over its 64 lanes; the wavefronts of workgroup 0 also write their blocks
-// to `e` (together, the whole encoded activation).  No other wavefront reads the area, so no
-// barrier is needed: the wavefront's LDS accesses complete in order.  `cur` holds the first batch,
-// loaded by the caller before the weight loads so that encoding it waits for nothing else; each
-// later batch is loaded while the one before it is encoded.
+// Encode this wavefront's blocks of the activation (`raw`, all of them) with the static scale g and
+// the encoder's block routine into its own LDS area (codes [row][phase][64 bytes of its chunk],
+// scales [row][phase][8]), spread over its 64 lanes.  No other wavefront reads the area, so no
+// barrier is needed: the wavefront's LDS accesses complete in order.
 template <nvfp4_dtype XDT, int NPH>
-__device__ __forceinline__ void encode_activation(const GemmArgs& p, const DecodeEncode& e, float g,
-                                                  int wave, int lane,
-                                                  uint32_t (&cur)[kEncodeBatch][encode_words<XDT>()],
+__device__ __forceinline__ void encode_activation(const GemmArgs& p, float g, int lane,
+                                                  const uint32_t (&raw)[kEncodeBatch][encode_words<XDT>()],
                                                   uint8_t* lcodes, uint8_t* lscales) {
-  constexpr int B = kEncodeBatch;
-  constexpr int W = encode_words<XDT>();
   const float gs6 = g / 6.0f;
   const int nblk = p.M * NPH * 8;
-  const bool out = blockIdx.x == 0 && e.codes != nullptr;
-  uint32_t nxt[B][W];
-  for (int base = 0; base < nblk; base += B * 64) {
-    if (base + B * 64 < nblk) encode_load<XDT, NPH>(p, e, wave, lane, base + B * 64, nxt);
 #pragma unroll
-    for (int j = 0; j < B; ++j) {
-      const int b = base + j * 64 + lane;
-      if (b >= nblk) continue;
-      float v[16];
+  for (int j = 0; j < kEncodeBatch; ++j) {
+    const int b = j * 64 + lane;
+    if (b >= nblk) continue;
+    float v[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if constexpr (XDT == NVFP4_F32) {
-          v[i] = __uint_as_float(cur[j][i]);
-        } else if constexpr (XDT == NVFP4_BF16) {
-          const uint32_t w2 = cur[j][i / 2];
-          v[i] = __uint_as_float((i & 1) ? (w2 & 0xFFFF0000u) : (w2 << 16));
-        } else {
-          const uint32_t w2 = cur[j][i / 2];
-          v[i] = (float)__builtin_bit_cast(_Float16, (uint16_t)((i & 1) ? (w2 >> 16) : (w2 & 0xFFFFu)));
-        }
-      }
-      uint32_t word[2];
-      const uint32_t sc = codec::encode_codes(v, g, gs6, word);
-      *reinterpret_cast<uint2*>(lcodes + b * 8) = uint2{word[0], word[1]};
-      lscales[b] = (uint8_t)sc;
-      if (out) {
-        int row, col;
-        wave_block<NPH>(b, wave, row, col);
-        *reinterpret_cast<uint2*>(e.codes + (int64_t)row * (p.K / 2) + col / 2) = uint2{word[0], word[1]};
-        e.scales[(int64_t)row * (p.K / 16) + col / 16] = (uint8_t)sc;
+    for (int i = 0; i < 16; ++i) {
+      if constexpr (XDT == NVFP4_F32) {
+        v[i] = __uint_as_float(raw[j][i]);
+      } else if constexpr (XDT == NVFP4_BF16) {
+        const uint32_t w2 = raw[j][i / 2];
+        v[i] = __uint_as_float((i & 1) ? (w2 & 0xFFFF0000u) : (w2 << 16));
+      } else {
+        const uint32_t w2 = raw[j][i / 2];
+        v[i] = (float)__builtin_bit_cast(_Float16, (uint16_t)((i & 1) ? (w2 >> 16) : (w2 & 0xFFFFu)));
       }
     }
-#pragma unroll
-    for (int j = 0; j < B; ++j)
-#pragma unroll
-      for (int i = 0; i < W; ++i) cur[j][i] = nxt[j][i];
+    uint32_t word[2];
+    const uint32_t sc = codec::encode_codes(v, g, gs6, word);
+    *reinterpret_cast<uint2*>(lcodes + b * 8) = uint2{word[0], word[1]};
+    lscales[b] = (uint8_t)sc;
+  }
+}
+
+// The wavefront's encoded blocks (its LDS area), written out to `e`: the wavefronts of workgroup 0
+// together write the whole encoded activation.
+template <int NPH>
+__device__ __forceinline__ void write_encoded(const GemmArgs& p, const DecodeEncode& e, int wave,
+                                              int lane, const uint8_t* lcodes,
+                                              const uint8_t* lscales) {
+  const int nblk = p.M * NPH * 8;
+  for (int b = lane; b < nblk; b += 64) {
+    int row, col;
+    wave_block<NPH>(b, wave, row, col);
+    *reinterpret_cast<uint2*>(e.codes + (int64_t)row * (p.K / 2) + col / 2) =
+        *reinterpret_cast<const uint2*>(lcodes + b * 8);
+    e.scales[(int64_t)row * (p.K / 16) + col / 16] = lscales[b];
   }
 }
 
@@ -244,14 +244,14 @@ gemm_skinny_kernel(GemmArgs p, DecodeEncode e, int ncols) {
         as2[q] = *reinterpret_cast<const uint16_t*>(p.a_scales + arow * ks + chunk_of<NPH>(q, wave) * 8 + g * 2);
     }
   }
-  // encoding form: the activation's global scale and first batch of blocks, loaded before any weight
-  // load so that the encode waits only for them
+  // encoding form: the activation's global scale and raw blocks, loaded before any weight load so
+  // that the encode waits only for them
   constexpr nvfp4_dtype kXdt = kEncode ? (nvfp4_dtype)XDT : NVFP4_BF16;
   float enc_g = 0.0f;
   uint32_t enc_raw[kEncodeBatch][encode_words<kXdt>()];
   if constexpr (kEncode) {
     enc_g = __builtin_nontemporal_load(p.a_g);
-    encode_load<kXdt, NPH>(p, e, wave, lane, 0, enc_raw);
+    encode_load<kXdt, NPH>(p, e, wave, lane, enc_raw);
   }
   __builtin_amdgcn_sched_barrier(0);
   // weight scales of every phase, then the weight codes phase by phase (rows past the workgroup's
@@ -286,7 +286,7 @@ gemm_skinny_kernel(GemmArgs p, DecodeEncode e, int ncols) {
   if constexpr (kEncode) {
     uint8_t* const lcodes = act[wave];
     uint8_t* const lscales = act[wave] + 16 * NPH * 64;
-    encode_activation<kXdt, NPH>(p, e, enc_g, wave, lane, enc_raw, lcodes, lscales);
+    encode_activation<kXdt, NPH>(p, enc_g, lane, enc_raw, lcodes, lscales);
 #pragma unroll
     for (int q = 0; q < NPH; ++q) {
       aq[q] = *reinterpret_cast<const uint4*>(lcodes + (arow * NPH + q) * 64 + g * 16);
@@ -336,6 +336,12 @@ gemm_skinny_kernel(GemmArgs p, DecodeEncode e, int ncols) {
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[q][j], bv, acc[t], 0, 0, 0);
       }
     }
+  }
+
+  // the encoded activation out for the caller, after every weight load has been waited for
+  if constexpr (kEncode) {
+    if (blockIdx.x == 0 && e.codes != nullptr)
+      write_encoded<NPH>(p, e, wave, lane, act[wave], act[wave] + 16 * NPH * 64);
   }
 
   // deterministic reduction of the 8 partial tiles of each tile: wavefront `tile` adds the 8 in
@@ -834,22 +840,29 @@ hipError_t compute_units(int& cus) {
 
 // Rows up to which the encoding form runs: every workgroup encodes all M activation rows itself,
 // so its encode work grows with M while a separate encode launch spreads it over the device.  On
-// the 5120 x 5120 decode product one launch took 8.2 / 9.1 / 9.7 us at M = 1 / 4 / 6 against
-// 9.0 / 9.6 / 9.9 us for encode + product as two launches (graph replays), but 11.1 / 14.4 us at
-// M = 8 / 16 against 9.9 / 10.0 us.
+// the 5120 x 5120 decode product one launch took 7.8 / 8.8 / 9.2 us at M = 1 / 4 / 6 against
+// 9.0 / 9.5 / 9.7 us for encode + product as two launches (graph replays); an earlier form that
+// could take more rows took 11.1 / 14.4 us at M = 8 / 16 against 9.9 / 10.0 us.
 constexpr int64_t kEncodeMaxRows = 6;
+
+// A wavefront's raw activation blocks (M * K / 128 of them) fit the one batch it loads before the
+// weights.
+static bool encode_fits_one_batch(int64_t M, int64_t K) {
+  return M * (K / kPhaseK) * 8 <= kEncodeBatch * 64;
+}
 
 bool skinny_one_pass(int64_t M, int64_t N, int64_t K, int x_dtype) {
   int cus = 0;
   if (compute_units(cus) != hipSuccess) return false;
   if (x_dtype == NVFP4_F32 && K > kEncodeF32MaxPhases * kPhaseK) return false;
   return M >= 1 && M <= kEncodeMaxRows && K % kPhaseK == 0 && K <= kSkinnyMaxK &&
-         (N + cus - 1) / cus <= 32;
+         encode_fits_one_batch(M, K) && (N + cus - 1) / cus <= 32;
 }
 
 hipError_t launch_gemm_skinny_encode(const GemmArgs& a, const void* x, nvfp4_dtype x_dtype,
                                      int64_t ldx, uint8_t* codes, uint8_t* scales,
                                      hipStream_t stream) {
+  if (!encode_fits_one_batch(a.M, a.K)) return hipErrorInvalidValue;
   int cus = 0;
   hipError_t e = compute_units(cus);
   if (e != hipSuccess) return e;

@@ -179,11 +179,11 @@ nvfp4_status fused_nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
  * Source: ai.info summary, "Methodology in Plain English" (activations quantized on the fly with
  * calibrated scales; W4A4 on every linear layer) and "Main Findings" (decode is weight-bandwidth-
  * bound; fused modules keep their own global scales).  For decode shapes with at most 6 rows (K a
- * multiple of 1024 up to 8192, at most 32 output columns per compute unit) both steps run in one
- * launch: every workgroup encodes the few activation rows itself while its weight bytes stream in,
- * and one of them writes the codes out.  Other shapes, decode shapes with 7 to 16 rows included
- * (where that redundant encode costs more than a launch), run the encoder and the product as two
- * launches.
+ * multiple of 1024 up to 8192, M * K / 1024 <= 32, at most 32 output columns per compute unit; K
+ * up to 5120 for an F32 x) both steps run in one launch: every workgroup encodes the few activation
+ * rows itself while its weight bytes stream in, and one of them writes the codes out.  Other
+ * shapes, decode shapes with 7 to 16 rows included (where that redundant encode costs more than a
+ * launch), run the encoder and the product as two launches.
  *
  *   x, x_dtype, ldx      device activation [M, K] (F32, BF16 or F16), as nvfp4_quantize's x.
  *   a_gscale             device, one float: the static activation scale gA (read only).

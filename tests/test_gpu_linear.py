@@ -2,8 +2,8 @@
 scales must equal the oracle's encoding under the same static scale bit for bit, and C must equal
 fused_nvfp4_gemm on those codes bit for bit (same kernels, same accumulation) and the oracle's exact
 product within the stated tolerance.  Decode shapes with at most 6 rows (K a multiple of 1024 up
-to 8192) run encode and product in one launch; the other shapes, decode shapes of 7 to 16 rows
-included, run them as two."""
+to 8192, M * K / 1024 <= 32) run encode and product in one launch; the other shapes, decode shapes
+of 7 to 16 rows and of 5 or 6 rows with longer K included, run them as two."""
 
 import numpy as np
 import pytest
@@ -50,10 +50,11 @@ def _run(x, dtype, wt, segs, what, ga=None, out_dtype="f32"):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 5120, 1024), (4, 3000, 2048), (6, 5120, 5120),
-                                   (2, 8100, 8192), (5, 40, 3072), (6, 4096, 7168), (1, 16, 1024)])
+                                   (2, 8100, 8192), (5, 40, 3072), (4, 4096, 8192), (1, 16, 1024)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
 def test_decode_shapes_one_launch(M, N, K, dtype):
-    # one or two 16-column tiles per workgroup, 1 to 8 phases of K, every input type
+    # one or two 16-column tiles per workgroup, 1 to 8 phases of K, every input type; 4 rows at
+    # K = 8192 fill the encode's one batch of blocks exactly (f32 input above K = 5120: two launches)
     x = random_matrix(M * 31 + K, M, K, outlier_cols=max(1, K // 100), dtype="bf16")
     if dtype == "f16":
         x = np.asarray(np.float16(x / 64), np.float32)  # exactly representable in f16
@@ -63,10 +64,11 @@ def test_decode_shapes_one_launch(M, N, K, dtype):
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 300, 512), (17, 100, 1024), (5, 70, 48), (3, 9000, 1024),
-                                   (2, 40, 17408), (7, 40, 3072), (16, 5120, 5120)])
+                                   (2, 40, 17408), (7, 40, 3072), (16, 5120, 5120), (6, 4096, 7168),
+                                   (5, 300, 7168)])
 def test_two_launch_shapes(M, N, K):
     # more than 16 rows, K not a multiple of 1024, more than 32 columns per compute unit, long K,
-    # 7 to 16 rows
+    # 7 to 16 rows, 5 or 6 rows whose raw blocks exceed the encode's one batch
     x = random_matrix(M * 37 + K, M, K, outlier_cols=3, dtype="bf16")
     wt = random_matrix(N * 3 + K, N, K, std=0.02)
     _run(x, "bf16", wt, [0, N], f"linear two launches M={M} N={N} K={K}")
