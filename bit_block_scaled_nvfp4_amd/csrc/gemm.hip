@@ -11,7 +11,8 @@
 //  * gemm_general_kernel: any K that is a multiple of 16.  One wavefront per 32x32 output tile,
 //    operands read straight from global memory 4 bytes (8 codes) per lane per K step.
 //  * gemm_tiled_kernel: K a multiple of 64.  A workgroup owns a BM x BN output tile (256 x 256 or
-//    256 x 192, chosen per problem); each K chunk of 256 is staged in LDS as raw 4-bit codes plus
+//    256 x 192 chosen per problem, 64 x 64 for the last N % 256 columns when a problem is split
+//    into two launches); each K chunk of 256 is staged in LDS as raw 4-bit codes plus
 //    E4M3 bytes (9/16 byte per element instead of 2 for f16, so staging costs a quarter of the LDS
 //    space and bandwidth of an f16 GEMM), then every wavefront decodes its own fragments in
 //    registers right before the MFMAs, one sub-chunk of 64 at a time.
@@ -349,15 +350,18 @@ __device__ __forceinline__ void mfma_range(const half8_t (&av)[FM], const half8_
 }
 
 // MFMAs of step 2 issued before the mid-sub-chunk hand-over: they keep the matrix core busy while
-// the wavefronts meet.
-constexpr int kPreBarrierMfma = 4;
+// the wavefronts meet (4 of the 12 or 16 of the wide tiles, half of a small tile's).
+template <int FM, int FN>
+constexpr int pre_barrier_mfma() {
+  return FM * FN >= 8 ? 4 : FM * FN / 2;
+}
 
 // Schedule of the MFMAs after the hand-over: the next sub-chunk's LDS reads (two per MFMA) and the
 // copies of the chunk after the next go out between MFMAs, with the decode VALU spread over all
 // of them, rather than as one block in front of the MFMAs.
 template <int FM, int FN, int NDS, int NVM>
 __device__ __forceinline__ void interleave_after_barrier() {
-  constexpr int kM = FM * FN - kPreBarrierMfma;
+  constexpr int kM = FM * FN - pre_barrier_mfma<FM, FN>();
   constexpr int kDsMfma = (NDS + 1) / 2;          // MFMAs carrying two LDS reads
   constexpr int kVmPerMfma = (NVM + kM - 1) / kM;  // copies per MFMA (the last group may be short)
   constexpr int kValu = (8 * (FM + FN) + kM - 1) / kM + 1;
@@ -399,7 +403,7 @@ __device__ __forceinline__ void pipelined_chunk(const Frags<FM, FN>& cur, Frags<
   decode_step<2>(cur, sa, sb, a0, b0);
   interleave_mfma_valu<FM, FN>();
   __builtin_amdgcn_sched_barrier(0);
-  mfma_range<0, kPreBarrierMfma>(a0, b0, acc);
+  mfma_range<0, pre_barrier_mfma<FM, FN>()>(a0, b0, acc);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (HAS_NEXT) {
     if constexpr (SYNC) {
@@ -410,7 +414,7 @@ __device__ __forceinline__ void pipelined_chunk(const Frags<FM, FN>& cur, Frags<
     read_frags(nstage, no, nxt);
     if constexpr (NVM > 0) issue();
   }
-  mfma_range<kPreBarrierMfma, FM * FN>(a0, b0, acc);
+  mfma_range<pre_barrier_mfma<FM, FN>(), FM * FN>(a0, b0, acc);
   decode_step<3>(cur, sa, sb, a1, b1);
   interleave_after_barrier<FM, FN, HAS_NEXT ? 2 * (FM + FN) : 0, HAS_NEXT ? NVM : 0>();
   __builtin_amdgcn_sched_barrier(0);
@@ -714,15 +718,44 @@ hipError_t launch_tiled_cfg(const GemmArgs& a, int cus, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Tile shapes of the persistent kernel: 256 x 256 (4 x 4 fragments per wavefront) and 256 x 192
-// (4 x 3).  The narrower tile decodes more per MFMA (7 fragment words per 12 MFMAs instead of 8 per
-// 16) and measured about 0.89 of the wider one's rate per tile FLOP, but it can save a whole round
-// of tiles: the GDN in_proj (4096 x 8288) is 528 tiles of 256 x 256 on 256 compute units, three
-// rounds of which the last is 1/16 full, and 704 of 256 x 192, three rounds of 3/4 the work.
-// The shape is chosen by the estimated time, rounds x tile FLOPs / relative rate.  Every output
-// element is accumulated the same way in either shape (same K chunks, steps and MFMA), so the
-// choice never changes a result.
+// Tile shapes of the persistent kernel: 256 x 256 (4 x 4 fragments per wavefront), 256 x 192
+// (4 x 3) and, for the last columns only, 64 x 64 (1 x 1).  The narrower wide tile decodes more per
+// MFMA (7 fragment words per 12 MFMAs instead of 8 per 16) and measured about 0.89 of the wider
+// one's rate per tile FLOP, but it can save a whole round of tiles: the GDN in_proj (4096 x 8288)
+// is 528 tiles of 256 x 256 on 256 compute units, three rounds of which the last is 1/16 full, and
+// 704 of 256 x 192, three rounds of 3/4 the work.  The third way runs the whole 256-column tile
+// columns (8192 there, two full rounds) as one launch and the remaining N % 256 columns as a second
+// launch of 64 x 64 tiles, 128 of them at the GDN in_proj.  A small tile contracts so little per K
+// chunk that the copy latency of the next chunk sets its pace: one round of them took about 0.4 of a
+// 256 x 256 round at the same K (GDN in_proj: 0.267 ms split against 0.281 ms in 256 x 192 tiles and
+// 0.333 ms in 256 x 256, on one machine).  The way is chosen by the estimated time, in rounds of
+// 256 x 256 tiles.  Every output element is accumulated the same way in every shape (same K
+// chunks, steps and MFMA), so the choice never changes a result.
 constexpr float kNarrowTileRate = 0.89f;
+constexpr float kStripRoundCost = 0.4f;
+
+// The tile columns of 256 as one launch, the last a.N % 256 columns as a launch of 64 x 64 tiles
+// on the same stream: the second sees the columns [nfull, N) of W and C as its whole problem, with
+// the segment table cut and rebased to them (the same alpha values, so the same bits).
+hipError_t launch_tiled_split(const GemmArgs& a, int nfull, int cus, hipStream_t stream) {
+  GemmArgs body = a;
+  body.N = nfull;
+  const hipError_t e = launch_tiled_cfg<2, 2, 4, 4>(body, cus, stream);
+  if (e != hipSuccess) return e;
+  GemmArgs strip = a;
+  strip.w_codes = a.w_codes + (int64_t)nfull * (a.K / 2);
+  strip.w_scales = a.w_scales + (int64_t)nfull * (a.K / 16);
+  strip.c = a.c_bf16 ? (void*)(reinterpret_cast<uint16_t*>(a.c) + nfull)
+                     : (void*)(reinterpret_cast<float*>(a.c) + nfull);
+  strip.N = a.N - nfull;
+  int first = 0;  // the segment that holds column nfull
+  while (first + 1 < a.seg.nseg && a.seg.off[first + 1] <= nfull) ++first;
+  strip.seg_g = a.seg_g + first;
+  strip.seg.nseg = a.seg.nseg - first;
+  for (int t = 0; t <= NVFP4_MAX_SEGMENTS; ++t)
+    strip.seg.off[t] = t <= strip.seg.nseg ? max(a.seg.off[first + t] - nfull, 0) : strip.N;
+  return launch_tiled_cfg<2, 2, 1, 1>(strip, cus, stream);
+}
 
 }  // namespace
 
@@ -732,12 +765,18 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   cus = max(cus, 1);
-  auto rounds = [&](int bm, int bn) {
-    const int64_t t = (int64_t)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
-    return (t + cus - 1) / cus;
+  auto rounds = [&](int64_t m, int64_t n, int bm, int bn) {
+    const int64_t t = ((m + bm - 1) / bm) * ((n + bn - 1) / bn);
+    return (float)((t + cus - 1) / cus);
   };
-  const float wide = (float)rounds(256, 256) * 256.0f * 256.0f;
-  const float narrow = (float)rounds(256, 192) * 256.0f * 192.0f / kNarrowTileRate;
+  const float wide = rounds(a.M, a.N, 256, 256);
+  const float narrow = rounds(a.M, a.N, 256, 192) * (192.0f / 256.0f) / kNarrowTileRate;
+  const int nfull = a.N / 256 * 256;
+  const float split = nfull > 0 && nfull < a.N
+                          ? rounds(a.M, nfull, 256, 256) +
+                                rounds(a.M, a.N - nfull, 64, 64) * kStripRoundCost
+                          : wide + 1.0f;
+  if (split < wide && split < narrow) return launch_tiled_split(a, nfull, cus, stream);
   if (narrow < wide) return launch_tiled_cfg<2, 2, 4, 3>(a, cus, stream);
   return launch_tiled_cfg<2, 2, 4, 4>(a, cus, stream);
 }

@@ -419,10 +419,12 @@ def test_mlp_decode_shapes_full_size(wid, M):
 
 def test_fused_equals_per_segment_calls_across_tile_shapes():
     """The GDN in_proj's shape (M = 4096, modules of 2048, 2048, 4096, 48 and 48 columns): the fused
-    product runs 256 x 192 tiles (three rounds of 704 tiles instead of 528 tiles of 256 x 256 whose
-    third round is 1/16 full), the 4096-column module alone runs 256 x 256 tiles and the others
-    256 x 192.  Every element is accumulated the same way in either shape, so the fused result
-    equals the per-module results bit for bit; sampled rows are checked against the oracle."""
+    product runs as two launches, 256 x 256 tiles over the first 8192 columns (two full rounds)
+    and 64 x 64 tiles over the last 96 (instead of 528 tiles of 256 x 256 whose third round is 1/16
+    full, or three rounds of 704 tiles of 256 x 192); the 4096-column module alone runs 256 x 256
+    tiles and the others 256 x 192.  Every element is accumulated the same way in every shape, so
+    the fused result equals the per-module results bit for bit; sampled rows are checked against
+    the oracle."""
     from workloads import random_nvfp4_bytes
 
     from .gpu_util import oracle_product

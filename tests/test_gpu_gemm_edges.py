@@ -67,6 +67,7 @@ RAW_SHAPES = [
     (65, 130, 192, "tiled 256 x 192, 3 K sub-chunks: no loop pass"),
     (17, 1000, 2048, "tiled 256 x 192, 17 rows"),
     (4096, 4096, 128, "tiled 256 x 256, one full round, one K chunk"),
+    (2048, 8232, 64, "tiled, split: 256 x 256 tiles over 8192 columns, 64 x 64 over the last 40"),
     (1, 3000, 2048, "one-pass decode, one tile per workgroup"),
     (16, 6000, 2048, "one-pass decode, two tiles per workgroup"),
     (3, 8100, 8192, "one-pass decode, K = 8192"),
@@ -152,6 +153,28 @@ def test_mid_size_full_output(M, N, K, what):
     _run(ac, as_, ga, wc, ws, gw, segs, f"full output, {what}")
 
 
+def test_split_launch_full_output_and_segment_calls():
+    """A problem split into two launches: 256 tiles of 256 x 256 over the first 8192 columns (one
+    round) and 32 tiles of 64 x 64 over the last 40, with a module boundary inside those 40 columns
+    (the second launch sees its columns' part of the segment table, rebased).  Every element is
+    compared with the oracle, and the fused result equals the per-module calls (which run single
+    launches of other tile shapes) bit for bit."""
+    M, N, K = 2048, 8232, 320
+    segs = [0, 3000, 8212, N]
+    a = random_matrix(97, M, K, outlier_cols=3)
+    wt = random_matrix(98, N, K, std=0.02)
+    ac, as_, ga = oracle.quantize(a)
+    wc, ws, gw = oracle.quantize_segments(wt, segs)
+    fused, _ = _run(ac, as_, ga, wc, ws, gw, segs, "split launch, 5 K sub-chunks")
+    parts = []
+    for j in range(len(segs) - 1):
+        lo, hi = segs[j], segs[j + 1]
+        C, _ = _run(ac, as_, ga, wc[lo:hi], ws[lo:hi], gw[j:j + 1], [0, hi - lo],
+                    f"split launch, module {j} alone")
+        parts.append(C)
+    assert np.array_equal(fused, np.concatenate(parts, axis=1))
+
+
 def test_mid_size_raw_bytes_full_output():
     M, N, K = 2304, 7936, 192
     ac, as_ = random_nvfp4_bytes(5, M, K)
@@ -165,6 +188,8 @@ def test_mid_size_raw_bytes_full_output():
                       "sub-chunk"),
     (1100, 19653, 704, "385 tiles of 256 x 256; per tile one loop pass, a chunk and a lone "
                        "sub-chunk"),
+    (2048, 8232, 704, "split: 256 tiles of 256 x 256, then 32 of 64 x 64; per tile one loop pass, "
+                      "a chunk and a lone sub-chunk"),
 ])
 def test_mid_size_loop_sampled_rows(M, N, K, what):
     """Several tiles per persistent workgroup with K long enough for the K loop itself: the GPU
