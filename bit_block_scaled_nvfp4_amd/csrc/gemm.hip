@@ -725,10 +725,11 @@ hipError_t launch_tiled_cfg(const GemmArgs& a, int cus, hipStream_t stream) {
 // is 528 tiles of 256 x 256 on 256 compute units, three rounds of which the last is 1/16 full, and
 // 704 of 256 x 192, three rounds of 3/4 the work.  The third way runs the whole 256-column tile
 // columns (8192 there, two full rounds) as one launch and the remaining N % 256 columns as a second
-// launch of 64 x 64 tiles, 128 of them at the GDN in_proj.  A small tile contracts so little per K
-// chunk that the copy latency of the next chunk sets its pace: one round of them took about 0.4 of a
-// 256 x 256 round at the same K (GDN in_proj: 0.267 ms split against 0.281 ms in 256 x 192 tiles and
-// 0.333 ms in 256 x 256, on one machine).  The way is chosen by the estimated time, in rounds of
+// launch of 64 x 64 tiles, 128 of them at the GDN in_proj.  A small tile gives each wavefront a
+// single 32 x 32 accumulator, one dependent chain of MFMAs with little work per K chunk to cover the
+// copies of the next: one round of them took 0.2-0.4 of a 256 x 256 round at the same K, and the
+// estimate takes 0.4 (GDN in_proj: 0.267 ms split against 0.281 ms in 256 x 192 tiles and 0.333 ms
+// in 256 x 256, on one machine).  The way is chosen by the estimated time, in rounds of
 // 256 x 256 tiles.  Every output element is accumulated the same way in every shape (same K
 // chunks, steps and MFMA), so the choice never changes a result.
 constexpr float kNarrowTileRate = 0.89f;
