@@ -175,6 +175,39 @@ def test_split_launch_full_output_and_segment_calls():
     assert np.array_equal(fused, np.concatenate(parts, axis=1))
 
 
+@pytest.mark.parametrize("odt", ["f32", "bf16"])
+def test_split_launch_into_output_view(odt):
+    """The split launch writing into a column window of a wider buffer (row pitch N + 11 elements,
+    so rows are not 16-byte aligned; window starting 8 elements in): the second launch's columns
+    start at the window's column 8192.  Elements outside the window keep their sentinel; the f32
+    result is within the product tolerance, the bf16 one within one more rounding."""
+    import torch
+
+    import bit_block_scaled_nvfp4_amd as nv
+
+    M, N, K = 2048, 8232, 64
+    segs = [0, 4100, 8200, N]
+    a = random_matrix(99, M, K, outlier_cols=3)
+    wt = random_matrix(100, N, K, std=0.02)
+    ac, as_, ga = oracle.quantize(a)
+    wc, ws, gw = oracle.quantize_segments(wt, segs)
+    dt = torch.float32 if odt == "f32" else torch.bfloat16
+    buf = torch.full((M, N + 11), -7.0, dtype=dt, device=DEV)
+    out = buf[:, 8:8 + N]
+    log(f"split launch into a view ({odt}): M={M} N={N} K={K}")
+    nv.fused_nvfp4_gemm(_up(ac), _up(as_), scalar(ga), _up(wc), _up(ws),
+                        _up(np.asarray(gw, np.float32)), segs, out=out)
+    torch.cuda.synchronize()
+    hb = buf.float().cpu().numpy()
+    assert np.all(hb[:, :8] == -7.0) and np.all(hb[:, 8 + N:] == -7.0)
+    C = hb[:, 8:8 + N].astype(np.float64)
+    R, B = oracle_product(ac, as_, ga, wc, ws, gw, segs)
+    if odt == "f32":
+        check_gemm(C, R, B, "split launch into a view")
+    else:  # one extra rounding of the FP32 result to bf16
+        assert np.all(np.abs(C - R) <= 2.0 ** -8 * np.abs(R) + 1e-4 * B)
+
+
 def test_mid_size_raw_bytes_full_output():
     M, N, K = 2304, 7936, 192
     ac, as_ = random_nvfp4_bytes(5, M, K)
