@@ -68,6 +68,7 @@ RAW_SHAPES = [
     (17, 1000, 2048, "tiled 256 x 192, 17 rows"),
     (4096, 4096, 128, "tiled 256 x 256, one full round, one K chunk"),
     (2048, 8232, 64, "tiled, split: 256 x 256 tiles over 8192 columns, 64 x 64 over the last 40"),
+    (1990, 8200, 192, "tiled, split, partial last tile row in both launches, 3 K sub-chunks"),
     (1, 3000, 2048, "one-pass decode, one tile per workgroup"),
     (16, 6000, 2048, "one-pass decode, two tiles per workgroup"),
     (3, 8100, 8192, "one-pass decode, K = 8192"),
