@@ -209,6 +209,22 @@ def test_split_launch_into_output_view(odt):
         assert np.all(np.abs(C - R) <= 2.0 ** -8 * np.abs(R) + 1e-4 * B)
 
 
+@pytest.mark.parametrize("M,N,K,what", [
+    (48, 320, 65600, "tiled, K = 65600: 128 passes of the two-chunk loop and a lone sub-chunk"),
+    (40, 8232, 16448, "tiled 256 x 192, K = 16448: 32 passes of the two-chunk loop and a lone sub-chunk"),
+])
+def test_tiled_long_k_full_output(M, N, K, what):
+    """The tiled product far along K (the longest K of the parity tests above is 17408 at full
+    size): FP32 accumulation over thousands of MFMA steps stays within the tolerance, and the
+    K loop's bookkeeping holds over hundreds of chunks.  Every element against the oracle."""
+    a = random_matrix(101, M, K, outlier_cols=5)
+    wt = random_matrix(102, N, K, std=0.02)
+    segs = [0, N // 2 + 1, N]
+    ac, as_, ga = oracle.quantize(a)
+    wc, ws, gw = oracle.quantize_segments(wt, segs)
+    _run(ac, as_, ga, wc, ws, gw, segs, what)
+
+
 def test_mid_size_raw_bytes_full_output():
     M, N, K = 2304, 7936, 192
     ac, as_ = random_nvfp4_bytes(5, M, K)
